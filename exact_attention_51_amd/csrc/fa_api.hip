@@ -1,0 +1,135 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument validation,
+// kernel-instance dispatch and launch on the caller's stream.  No call here
+// allocates, copies or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+int check_common(int B, int H, int N, int D, float scale, int causal) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  const int64_t elems = (int64_t)B * H * N * D;
+  if (elems > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int map_launch(int rc) {
+  if (rc == 0) return FA_OK;
+  if (rc == -2) return FA_ERR_UNSUPPORTED;
+  return FA_ERR_LAUNCH;
+}
+
+fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
+                     float scale, int causal) {
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return (1 << 16) | 0; }
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK:
+      return "success";
+    case FA_ERR_INVALID_ARG:
+      return "invalid argument (null pointer, non-positive size, bad scale or causal flag, or size overflow)";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported shape (head dimension must be 64, 128 or 256)";
+    case FA_ERR_LAUNCH:
+      return "kernel launch failed";
+    default:
+      return "unknown error code";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D, float scale,
+           int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  const fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, D, scale, causal);
+  if (D == 256) return map_launch(fa::launch_fwd_bf16_d256(a, (hipStream_t)stream));
+  return map_launch(fa::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int D,
+               float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  return map_launch(fa::launch_fwd_f32(fwd_args(q, k, v, o, lse, B, H, N, D, scale, causal), (hipStream_t)stream));
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+              float* delta, void* dq, int B, int H, int N, int D, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !delta || !dq) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  fa::BwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dO = dO;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal;
+  return map_launch(fa::launch_bwd_dq(a, (hipStream_t)stream));
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                void* dk, void* dv, int B, int H, int N, int D, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !delta || !dk || !dv) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  fa::BwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lse = lse;
+  a.delta = const_cast<float*>(delta);
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal;
+  return map_launch(fa::launch_bwd_dkdv(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

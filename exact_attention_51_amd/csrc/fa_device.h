@@ -1,0 +1,143 @@
+// fa_device.h -- device primitives shared by the gfx950 attention kernels.
+//
+// Everything here is written for CDNA4 (gfx950) and wave64 only: bf16 MFMA
+// 32x32x16 with float32 accumulators, the LDS transpose read
+// ds_read_b64_tr_b16, direct global->LDS loads of 16 bytes per lane and the
+// cross-half lane swap v_permlane32_swap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef s16x4 __attribute__((address_space(3))) * lds_s16x4_ptr;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// ---------------------------------------------------------------- MFMA
+//
+// v_mfma_f32_32x32x16_bf16, C[32x32] += A[32x16] * B[16x32].  Lane l holds
+//   A: row m = l % 32, k = (l / 32) * 8 + i    (i = 0..7)
+//   B: col n = l % 32, k = (l / 32) * 8 + i
+//   C: acc[r] = C[(r / 4) * 8 + (l / 32) * 4 + r % 4][l % 32]
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ bf16x2 pack_bf16(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_u32(float lo, float hi) {
+  bf16x2 p = pack_bf16(lo, hi);
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// Four packed pairs -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 join8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3), __builtin_shufflevector(c, d, 0, 1, 2, 3),
+                                 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Eight float32 accumulator values -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                        float a7) {
+  u32x4 u = {pack_bf16_u32(a0, a1), pack_bf16_u32(a2, a3), pack_bf16_u32(a4, a5), pack_bf16_u32(a6, a7)};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }    // v_rcp_f32
+__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+
+// Value of x from lanes l % 32 and 32 + l % 32, in every lane: (lower, upper).
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return __builtin_fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
+}
+
+// ---------------------------------------------------------------- LDS
+//
+// K and V tiles live in LDS as rows of D bf16 split into 16-byte chunks.
+// The chunk c of row r is stored at physical chunk c ^ swz(r).  swz is a bit
+// permutation of the low row bits chosen so that both access patterns are
+// free of bank conflicts:
+//   * ds_read_b128 of one logical chunk from 16 consecutive rows (K operand),
+//   * ds_read_b64_tr_b16 of 4 consecutive rows x 2 adjacent chunks (V operand).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D >= 128) {
+    // row bits (b3 b2 b1 b0) -> chunk bits (b3 b1 b0 b2); D = 256 uses 4 of its 5 chunk bits
+    int x = r & 15;
+    return ((x & 3) << 1) | ((x >> 2) & 1) | (x & 8);
+  } else {
+    // D = 64: two rows per 256-byte bank window; x = (r / 2) % 8 -> chunk bits (x0 x1 x2) -> (x1 x0 x2)
+    int x = (r >> 1) & 7;
+    return ((x & 1) << 1) | ((x >> 1) & 1) << 2 | ((x >> 2) & 1);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ int lds_off_bytes(int row, int chunk) {
+  return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
+}
+
+__device__ __forceinline__ s16x4 ds_read_tr(const char __attribute__((address_space(3))) * p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's 16 bytes land at
+// LDS byte address lds_base + 16 * l.  lds_base must be the same in every
+// lane of the wave (it is passed in M0).  Issued from inline assembly so
+// that the compiler does not guard every later LDS read with a wait on it.
+// The caller orders these copies itself: wait_vmcnt + a workgroup barrier
+// before the copied data is read, and a barrier between the last read of a
+// buffer and the next copy into it (the barrier also keeps the compiler
+// from moving LDS reads across the copy).  The s_nop is the wait state a
+// write of M0 needs before an LDS DMA reads it.
+__device__ __forceinline__ void load_lds16(const void* gptr, const void __attribute__((address_space(3))) * lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "{m0}"(base));
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+}  // namespace fa

@@ -1,0 +1,115 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
+ *
+ * The operation.  For every (batch b, head h), with Q, K, V the N x D
+ * slices q[b][h], k[b][h], v[b][h]:
+ *
+ *     S = scale * Q K^T                       (N x N, never stored)
+ *     P = row-wise softmax of S               (causal: S[i][j] = -inf for j > i)
+ *     O = P V                                 (N x D)
+ *     L[i] = m_i + ln(l_i)                    (natural-log log-sum-exp of row i)
+ *
+ * where m_i is the row max of S and l_i = sum_j exp(S[i][j] - m_i).  This is
+ * the exact-attention definition of the "Flash Attention" page (opening
+ * definition) and of "Learning Metal with FlashAttention" (section
+ * FlashAttention); L is the statistic the forward kernel of the
+ * metal-flash-attention README saves for the backward ("Quantifying
+ * performance", forward pseudocode).  Causal masking is top-left aligned:
+ * query i sees keys 0..i.
+ *
+ * The backward entry points compute the gradients of O with respect to Q, K
+ * and V given dO, split the way the metal-flash-attention README's backward
+ * pseudocode splits them ("Quantifying performance": a backward-query kernel
+ * and a backward-key-value kernel, no floating-point atomics):
+ *
+ *     delta[i] = sum_d dO[i][d] * O[i][d]
+ *     P = exp(S - L)            (S the scaled scores, L from the forward)
+ *     dP = dO V^T,  dS = P * (dP - delta)    (elementwise)
+ *     dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * Layout.   Q, K, V, O, dO, dQ, dK, dV are contiguous [B][H][N][D] (BHND,
+ *           D fastest).  L and delta are contiguous float32 [B][H][N].
+ * Pointers. All tensor pointers are DEVICE pointers.  The caller allocates
+ *           and owns every buffer; the library never allocates, frees,
+ *           copies between host and device or synchronises.  Outputs must
+ *           not alias inputs.
+ * Stream.   `stream` is a hipStream_t passed as void*; NULL is the default
+ *           stream.  Each call enqueues its kernels and returns; results are
+ *           ready when the stream reaches that point.
+ * Errors.   0 on success, else a negative FA_ERR_* code; nothing is thrown
+ *           or aborted across the ABI.  Argument checks happen before any
+ *           HIP call, so a rejected call touches no device state.
+ * Threads.  No global mutable state: calls from several host threads on
+ *           different streams are safe.
+ * Sizes.    B, H, N >= 1; B*H*N*D must fit in 2^31 - 1 elements per tensor.
+ *           Head dims: D in {64, 128} for fa_fwd (also 256), see below.
+ *           scale must be finite and > 0 (the scores use scale = 1/sqrt(D)
+ *           in every workload here; any positive scale is accepted).
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_ERR_INVALID_ARG (-1) /* null pointer, B/H/N/D <= 0, bad scale, size overflow */
+#define FA_ERR_UNSUPPORTED (-2) /* valid but not supported: head dim or sequence length */
+#define FA_ERR_LAUNCH (-3)      /* the kernel launch failed (hipGetLastError) */
+
+/*
+ * Forward, bfloat16 in and out, float32 accumulation.
+ *   q, k, v : bf16 [B][H][N][D]        (read)
+ *   o       : bf16 [B][H][N][D]        (written; O rounded to nearest-even)
+ *   lse     : f32  [B][H][N]           (written; L = m + ln l, natural log)
+ * D in {64, 128, 256}.  Any N >= 1.  causal: 0 or 1.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
+           float scale, int causal, void* stream);
+
+/*
+ * Forward, float32 in and out, float32 arithmetic throughout.  Same
+ * arguments and semantics as fa_fwd.  D in {64, 128, 256}; any N >= 1.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int D,
+               float scale, int causal, void* stream);
+
+/*
+ * Backward, query side (metal-flash-attention README, "Quantifying
+ * performance", backward-query pseudocode).  Computes
+ *   delta : f32  [B][H][N]   delta[i] = sum_d dO[i][d] O[i][d]   (written)
+ *   dq    : bf16 [B][H][N][D]                                     (written)
+ * from q, k, v, o (the forward output), dO (bf16) and lse (the forward's
+ * L).  Each workgroup owns a block of query rows and loops over key blocks,
+ * so no two workgroups write the same element: no atomics, no workspace.
+ * D in {64, 128, 256}; any N >= 1.
+ */
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+              float* delta, void* dq, int B, int H, int N, int D, float scale, int causal, void* stream);
+
+/*
+ * Backward, key/value side (metal-flash-attention README, "Quantifying
+ * performance", backward-key-value pseudocode).  Computes
+ *   dk, dv : bf16 [B][H][N][D]   (written)
+ * from q, k, v, dO, lse and delta.  delta must be the one fa_bwd_dq wrote:
+ * enqueue this call after fa_bwd_dq on the same stream (or otherwise order
+ * it after).  Each workgroup owns a block of key rows and loops over query
+ * blocks: no atomics, no workspace.  D in {64, 128, 256}; any N >= 1.
+ */
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                void* dk, void* dv, int B, int H, int N, int D, float scale, int causal, void* stream);
+
+/* A static, human-readable string for an FA_* code (never NULL). */
+const char* fa_strerror(int code);
+
+/* Library ABI version: (major << 16) | minor. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,112 @@
+"""The C-ABI library: it loads, exports every symbol include/fa.h declares,
+and rejects bad arguments before touching the GPU.  No compute call is made,
+so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_51_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    assert names == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_dq", "fa_bwd_dkdv", "fa_strerror", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_header_signatures_match_binding():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, (_, args) in _lib.SIGNATURES.items():
+        m = re.search(rf"\b{name}\s*\(([^)]*)\)", text)
+        assert m, name
+        params = [p.strip() for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), (name, params)
+        for p, a in zip(params, args):
+            if "*" in p:
+                assert a is ctypes.c_void_p, (name, p)
+            elif p.startswith("float"):
+                assert a is ctypes.c_float, (name, p)
+            else:
+                assert p.startswith("int") and a is ctypes.c_int, (name, p)
+
+
+def test_version_and_strerror():
+    lib = _lib.load()
+    assert lib.fa_version() >> 16 == 1
+    for code in (0, -1, -2, -3, 12345):
+        s = lib.fa_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case below fails validation first
+
+
+def _fwd(lib, fn="fa_fwd", ptrs=None, B=1, H=1, N=128, D=64, scale=0.125, causal=0):
+    ptrs = ptrs or [FAKE] * 5
+    return getattr(lib, fn)(*ptrs, B, H, N, D, scale, causal, None)
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+def test_forward_argument_validation(fn):
+    lib = _lib.load()
+    inv, uns = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert _fwd(lib, fn, ptrs=ptrs) == inv
+    assert _fwd(lib, fn, B=0) == inv
+    assert _fwd(lib, fn, H=-1) == inv
+    assert _fwd(lib, fn, N=0) == inv
+    assert _fwd(lib, fn, D=0) == inv
+    assert _fwd(lib, fn, scale=0.0) == inv
+    assert _fwd(lib, fn, scale=-1.0) == inv
+    assert _fwd(lib, fn, scale=float("nan")) == inv
+    assert _fwd(lib, fn, scale=float("inf")) == inv
+    assert _fwd(lib, fn, causal=2) == inv
+    assert _fwd(lib, fn, B=1024, H=1024, N=4096, D=64) == inv  # 2^38 elements
+    for d in (1, 32, 96, 100, 160, 512):
+        assert _fwd(lib, fn, D=d) == uns
+
+
+@pytest.mark.parametrize("fn,nptr", [("fa_bwd_dq", 8), ("fa_bwd_dkdv", 8)])
+def test_backward_argument_validation(fn, nptr):
+    lib = _lib.load()
+    f = getattr(lib, fn)
+    inv, uns = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    for i in range(nptr):
+        ptrs = [FAKE] * nptr
+        ptrs[i] = None
+        assert f(*ptrs, 1, 1, 128, 64, 0.125, 0, None) == inv
+    ptrs = [FAKE] * nptr
+    assert f(*ptrs, 1, 1, 0, 64, 0.125, 0, None) == inv
+    assert f(*ptrs, 1, 1, 128, 64, float("nan"), 0, None) == inv
+    assert f(*ptrs, 1, 1, 128, 64, 0.125, 7, None) == inv
+    assert f(*ptrs, 1, 1, 128, 80, 0.125, 0, None) == uns
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    import exact_attention_51_amd as fa
+
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)

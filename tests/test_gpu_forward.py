@@ -1,0 +1,208 @@
+"""GPU parity of the forward kernels against the float64 oracle, through the C ABI.
+
+Full-size workloads are checked element by element where the oracle finishes
+in seconds (c1, c2, c5) and on sampled rows otherwise (c3, c4: every head,
+the ends, tile boundaries and random rows; attention rows are independent,
+so the oracle computes just those rows).  Small shapes cover ragged lengths,
+several tiles and both masking modes.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from fa_inputs import WORKLOADS, make_inputs
+from tests._gpu import (
+    TOL_BF16_L,
+    TOL_BF16_O,
+    TOL_F32,
+    dev_bf16,
+    host,
+    inputs_on_device,
+    log,
+    sample_rows,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+def _fa():
+    import exact_attention_51_amd as fa
+
+    return fa
+
+
+def _run(w, x):
+    import torch
+
+    q, k, v = inputs_on_device(w, x)
+    o, lse = _fa().fwd(q, k, v, w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _tols(w):
+    return (TOL_F32, TOL_F32) if w.dtype == "fp32" else (TOL_BF16_O, TOL_BF16_L)
+
+
+def _check_full(w, x, o, lse):
+    o_ref, l_ref = oracle.forward(x.q, x.k, x.v, w.scale, w.causal)
+    eo = float(np.abs(host(o) - o_ref).max())
+    el = float(np.abs(host(lse) - l_ref).max())
+    to, tl = _tols(w)
+    log(f"  {w.name} B={w.B} H={w.H} N={w.N} D={w.D} causal={w.causal}: max|dO|={eo:.3e} max|dL|={el:.3e}")
+    assert eo <= to and el <= tl, (eo, el)
+    assert np.isfinite(host(o)).all() and np.isfinite(host(lse)).all()
+
+
+def _check_rows(w, x, o, lse, count=24):
+    oh, lh = host(o), host(lse)
+    assert np.isfinite(lh).all()
+    eo = el = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = sample_rows(w.N, count, seed=1000 * b + h)
+            o_ref, l_ref = oracle.forward_rows(x.q[b, h], x.k[b, h], x.v[b, h], rows, w.scale, w.causal)
+            eo = max(eo, float(np.abs(oh[b, h, rows] - o_ref).max()))
+            el = max(el, float(np.abs(lh[b, h, rows] - l_ref).max()))
+    to, tl = _tols(w)
+    log(f"  {w.name} sampled rows: max|dO|={eo:.3e} max|dL|={el:.3e}")
+    assert eo <= to and el <= tl, (eo, el)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workload_forward(name):
+    w = WORKLOADS[name]
+    log(f"test_workload_forward[{name}] start")
+    x = make_inputs(w, with_do=False)
+    o, lse = _run(w, x)
+    if name in ("c3", "c4"):
+        _check_rows(w, x, o, lse)
+    else:
+        _check_full(w, x, o, lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("N", [1, 5, 64, 65, 130, 256, 300, 520])
+def test_forward_bf16_shapes(N, D, causal):
+    w = WORKLOADS["c2"].with_(name="edge", B=1, H=2, N=N, D=D, causal=causal, seed=N * 7 + D)
+    log(f"test_forward_bf16_shapes N={N} D={D} causal={causal}")
+    x = make_inputs(w, with_do=False)
+    _check_full(w, x, *_run(w, x))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("N", [1, 33, 256, 300])
+def test_forward_f32_shapes(N, D, causal):
+    w = WORKLOADS["c1"].with_(name="edge32", B=2, H=1, N=N, D=D, causal=causal, seed=N + D)
+    log(f"test_forward_f32_shapes N={N} D={D} causal={causal}")
+    x = make_inputs(w, with_do=False)
+    _check_full(w, x, *_run(w, x))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_forward_peaked_rows(D):
+    """Q scaled by 3 (and by 8): nearly one-hot rows stress the rescale path."""
+    for mult in (3.0, 8.0):
+        w = WORKLOADS["c4"].with_(name="peaked", B=1, H=2, N=1024, D=D, q_mult=mult, seed=int(mult) + D)
+        log(f"test_forward_peaked_rows D={D} q_mult={mult}")
+        x = make_inputs(w, with_do=False)
+        _check_full(w, x, *_run(w, x))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_forward_invariants(D):
+    import torch
+
+    fa = _fa()
+    n = 384
+    w = WORKLOADS["c2"].with_(B=1, H=1, N=n, D=D, seed=D)
+    x = make_inputs(w, with_do=False)
+    q, k, v = inputs_on_device(w, x)
+    log(f"test_forward_invariants D={D}")
+    for causal in (False, True):
+        # constant V: every output row equals that row
+        vc = v[:, :, :1, :].expand(-1, -1, n, -1).contiguous()
+        o, _ = fa.fwd(q, k, vc, w.scale, causal)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(host(o), host(vc), rtol=0, atol=1e-2)
+        # identical keys: plain mean (prefix mean under causal) of V, and L = scale q.k + ln(count)
+        kc = k[:, :, :1, :].expand(-1, -1, n, -1).contiguous()
+        o, lse = fa.fwd(q, kc, v, w.scale, causal)
+        torch.cuda.synchronize()
+        vh = x.v[0, 0].astype(np.float64)
+        counts = np.arange(1, n + 1) if causal else np.full(n, n)
+        mean = np.cumsum(vh, axis=0) / counts[:, None] if causal else np.tile(vh.mean(axis=0), (n, 1))
+        np.testing.assert_allclose(host(o)[0, 0], mean, rtol=0, atol=2e-2)
+        l_ref = w.scale * (x.q[0, 0].astype(np.float64) @ x.k[0, 0, 0].astype(np.float64)) + np.log(counts)
+        np.testing.assert_allclose(host(lse)[0, 0], l_ref, rtol=0, atol=1e-2)
+    # causal row 0 sees key 0 only: O_0 = V_0 exactly
+    o, lse = fa.fwd(q, k, v, w.scale, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o)[0, 0, 0], host(v)[0, 0, 0])
+
+
+def test_forward_deterministic():
+    import torch
+
+    w = WORKLOADS["c3"].with_(B=1, H=4, N=2048)
+    x = make_inputs(w, with_do=False)
+    q, k, v = inputs_on_device(w, x)
+    fa = _fa()
+    o1, l1 = fa.fwd(q, k, v, w.scale, True)
+    o2, l2 = fa.fwd(q, k, v, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forward_causal_prefix():
+    """Causal rows < n do not depend on keys >= n: a length-n run agrees."""
+    import torch
+
+    fa = _fa()
+    w = WORKLOADS["c3"].with_(B=1, H=2, N=1024)
+    x = make_inputs(w, with_do=False)
+    q, k, v = inputs_on_device(w, x)
+    o, lse = fa.fwd(q, k, v, w.scale, True)
+    for n in (1, 100, 256, 700):
+        op, lp = fa.fwd(q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous(), w.scale, True)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(host(op), host(o)[:, :, :n], rtol=0, atol=2e-2)
+        np.testing.assert_allclose(host(lp), host(lse)[:, :, :n], rtol=0, atol=1e-3)
+
+
+def test_forward_batch_slices_independent():
+    """A [B, H] batch equals separate single-head calls, bit for bit."""
+    import torch
+
+    fa = _fa()
+    w = WORKLOADS["c2"].with_(B=2, H=3, N=320)
+    x = make_inputs(w, with_do=False)
+    q, k, v = inputs_on_device(w, x)
+    o, lse = fa.fwd(q, k, v, w.scale, False)
+    for b in range(2):
+        for h in range(3):
+            sl = lambda t: t[b : b + 1, h : h + 1].contiguous()  # noqa: E731
+            o1, l1 = fa.fwd(sl(q), sl(k), sl(v), w.scale, False)
+            torch.cuda.synchronize()
+            assert torch.equal(o1[0, 0], o[b, h]) and torch.equal(l1[0, 0], lse[b, h])
+
+
+def test_forward_writes_only_its_outputs():
+    """Outputs of a ragged call stay inside [B, H, N, D]: guard words around them are untouched."""
+    import torch
+
+    fa = _fa()
+    w = WORKLOADS["c3"].with_(B=1, H=1, N=77, D=128)
+    x = make_inputs(w, with_do=False)
+    q, k, v = (dev_bf16(b) for b in (x.q_bits, x.k_bits, x.v_bits))
+    n_o = w.N * w.D
+    o_buf = torch.full((n_o + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    l_buf = torch.full((w.N + 1024,), 7.0, dtype=torch.float32, device="cuda")
+    o = o_buf[:n_o].view(1, 1, w.N, w.D)
+    lse = l_buf[: w.N].view(1, 1, w.N)
+    fa.fwd(q, k, v, w.scale, True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((o_buf[n_o:] == 7.0).all()) and bool((l_buf[w.N :] == 7.0).all())

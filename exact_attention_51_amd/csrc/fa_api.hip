@@ -72,7 +72,6 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   const int rc = check_common(B, H, N, D, scale, causal);
   if (rc != FA_OK) return rc;
   const fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, D, scale, causal);
-  if (D == 256) return map_launch(fa::launch_fwd_bf16_d256(a, (hipStream_t)stream));
   return map_launch(fa::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 

@@ -133,6 +133,63 @@ __device__ __forceinline__ void load_lds16(const void* gptr, const void __attrib
       : "v"(gptr), "{m0}"(base));
 }
 
+// Same, 4 bytes per lane: lane l's dword lands at lds_base + 4 * l.
+__device__ __forceinline__ void load_lds4(const void* gptr, const void __attribute__((address_space(3))) * lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gptr), "{m0}"(base));
+}
+
+typedef char __attribute__((address_space(3))) lds_char;
+
+// Copy rows row0 .. row0+ROWS-1 (clamped to N-1) of a [N][D] bf16 matrix into
+// an LDS buffer of ROWS x D, in the swizzled layout above.  All WAVES waves of
+// the workgroup take part; each issues ROWS*D/8/WAVES/64 direct loads.
+template <int D, int ROWS, int WAVES>
+__device__ __forceinline__ void copy_rows_lds(const __bf16* __restrict__ src, int N, int row0, lds_char* buf, int wave,
+                                              int lane) {
+  constexpr int kRowChunks = D / 8;
+  constexpr int kChunksPerWave = ROWS * kRowChunks / WAVES;
+  static_assert(kChunksPerWave % 64 == 0, "tile must split into whole wave loads");
+#pragma unroll
+  for (int i = 0; i < kChunksPerWave / 64; ++i) {
+    const int slot0 = wave * kChunksPerWave + i * 64;  // wave-uniform
+    const int slot = slot0 + lane;
+    const int r = slot / kRowChunks;
+    const int c = (slot % kRowChunks) ^ swz<D>(r);
+    int grow = row0 + r;
+    grow = grow < N ? grow : N - 1;
+    load_lds16(src + (size_t)grow * D + c * 8, buf + slot0 * 16);
+  }
+}
+
+// MFMA operand of 8 bf16 along k, read transposed out of a swizzled [rows][D]
+// LDS tile (rows are the k index, D the m/n index).  The 32 m/n values are
+// d0 .. d0+31; the k slots are rows r0 + {half*4 + 0..3, 8 + half*4 + 0..3},
+// which is the order in which a 32x32 accumulator holds its rows, so an
+// accumulator packed to bf16 is the matching other operand.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr_operand(const lds_char* tile, int r0, int d0, int lane) {
+  const int g = lane >> 4, j16 = lane & 15, half = lane >> 5;
+  const int dcol = d0 + (g & 1) * 16 + (j16 & 3) * 4;
+  const int chunk = dcol >> 3;
+  const int boff = (dcol & 7) * 2;
+  const int r1 = r0 + half * 4 + (j16 >> 2);
+  const s16x4 va = ds_read_tr(tile + lds_off_bytes<D>(r1, chunk) + boff);
+  const s16x4 vb = ds_read_tr(tile + lds_off_bytes<D>(r1 + 8, chunk) + boff);
+  const s16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+  return __builtin_bit_cast(bf16x8, v8);
+}
+
+// MFMA operand of 8 bf16 along k = d, read row-wise: row `row`, d = ds*16 + half*8 + 0..7.
+template <int D>
+__device__ __forceinline__ bf16x8 read_row_operand(const lds_char* tile, int row, int ds, int half) {
+  return *(const bf16x8 __attribute__((address_space(3)))*)(tile + lds_off_bytes<D>(row, ds * 2 + half));
+}
+
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at max).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

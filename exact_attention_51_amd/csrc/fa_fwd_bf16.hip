@@ -38,42 +38,21 @@ namespace fa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 64;
-constexpr int kBlockM = kWaves * kRowsPerWave;  // 256 query rows per workgroup
-constexpr int kBlockN = 64;                     // keys per K/V tile
-constexpr float kRescaleThreshold = 8.0f;       // exp2-domain growth allowed before O is rescaled
+constexpr int kBlockN = 64;                // keys per K/V tile
+constexpr float kRescaleThreshold = 8.0f;  // exp2-domain growth allowed before O is rescaled
 
 template <int D>
 struct FwdCfg {
+  // Query blocks of 32 rows per wave: two for D <= 128 (64 rows, O in 2*D/32*16
+  // registers), one for D = 256 so that O and Q^T still fit the register file.
+  static constexpr int kQB = D <= 128 ? 2 : 1;
+  static constexpr int kRowsPerWave = 32 * kQB;
+  static constexpr int kBlockM = kWaves * kRowsPerWave;        // query rows per workgroup
   static constexpr int kDSteps = D / 16;                       // k-steps of the S product
   static constexpr int kDBlocks = D / 32;                      // 32-wide d blocks of O
   static constexpr int kTileBytes = kBlockN * D * 2;           // one K or V tile
-  static constexpr int kChunksPerWave = kTileBytes / 16 / kWaves;  // 16-byte chunks one wave copies
-  static constexpr int kLoadsPerWave = kChunksPerWave / 64;    // direct-load instructions per tensor
-  static constexpr int kRowChunks = D / 8;                     // 16-byte chunks per row
   static constexpr int kLdsBytes = 4 * kTileBytes;             // K and V, two buffers each
 };
-
-typedef char __attribute__((address_space(3))) lds_char;
-
-// Copy key/value tile `tile` (rows tile*64 .. +63, clamped to N-1) of one
-// tensor into an LDS buffer, in the swizzled layout.
-template <int D>
-__device__ __forceinline__ void load_tile(const __bf16* __restrict__ src, int N, int tile, lds_char* buf, int wave,
-                                          int lane) {
-  using C = FwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::kLoadsPerWave; ++i) {
-    const int slot0 = wave * C::kChunksPerWave + i * 64;  // wave-uniform
-    const int slot = slot0 + lane;
-    const int r = slot / C::kRowChunks;
-    const int pc = slot % C::kRowChunks;
-    const int c = pc ^ swz<D>(r);
-    int grow = tile * kBlockN + r;
-    grow = grow < N ? grow : N - 1;
-    load_lds16(src + (size_t)grow * D + c * 8, buf + slot0 * 16);
-  }
-}
 
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(
@@ -96,29 +75,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const __bf16* __restrict__ K = (const __bf16*)a.k + head_off;
   const __bf16* __restrict__ V = (const __bf16*)a.v + head_off;
 
-  const int q0 = qtile * kBlockM;
-  const int wq0 = q0 + wave * kRowsPerWave;
+  constexpr int QB = C::kQB;
+  const int q0 = qtile * C::kBlockM;
+  const int wq0 = q0 + wave * C::kRowsPerWave;
   const bool wave_active = wq0 < N;
   const int n_ktiles_all = (N + kBlockN - 1) / kBlockN;
   int nt = n_ktiles_all;
   int wave_last = n_ktiles_all - 1;
   if constexpr (CAUSAL) {
-    const int blk_last_row = min(q0 + kBlockM - 1, N - 1);
+    const int blk_last_row = min(q0 + C::kBlockM - 1, N - 1);
     nt = blk_last_row / kBlockN + 1;
-    wave_last = min(wq0 + kRowsPerWave - 1, N - 1) / kBlockN;
+    wave_last = min(wq0 + C::kRowsPerWave - 1, N - 1) / kBlockN;
   }
 
   lds_char* kbuf[2] = {smem, smem + C::kTileBytes};
   lds_char* vbuf[2] = {smem + 2 * C::kTileBytes, smem + 3 * C::kTileBytes};
 
   // Tile 0 in flight while Q is fetched.
-  load_tile<D>(K, N, 0, kbuf[0], wave, lane);
-  load_tile<D>(V, N, 0, vbuf[0], wave, lane);
+  copy_rows_lds<D, kBlockN, kWaves>(K, N, 0, kbuf[0], wave, lane);
+  copy_rows_lds<D, kBlockN, kWaves>(V, N, 0, vbuf[0], wave, lane);
 
   // Q^T as MFMA B operands: lane holds query column l32, d = ds*16 + half*8 + 0..7.
-  bf16x8 qf[2][C::kDSteps];
+  bf16x8 qf[QB][C::kDSteps];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     int row = wq0 + qb * 32 + l32;
     row = row < N ? row : N - 1;
 #pragma unroll
@@ -126,15 +106,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       qf[qb][ds] = *(const bf16x8*)(Q + (size_t)row * D + ds * 16 + half * 8);
   }
 
-  f32x16 o[2][C::kDBlocks];
+  f32x16 o[QB][C::kDBlocks];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-  float m[2] = {-__builtin_inff(), -__builtin_inff()};  // running max, raw (unscaled) score units
-  float l[2] = {0.f, 0.f};                               // this lane's partial row sum
+  float m[QB], l[QB];  // running max (raw, unscaled score units); this lane's partial row sum
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -__builtin_inff();
+    l[qb] = 0.f;
+  }
   const float c = a.scale_log2;                           // scale * log2(e)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -142,28 +126,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     wait_vmcnt<0>();
     __syncthreads();
     if (j + 1 < nt) {
-      load_tile<D>(K, N, j + 1, kbuf[(j + 1) & 1], wave, lane);
-      load_tile<D>(V, N, j + 1, vbuf[(j + 1) & 1], wave, lane);
+      copy_rows_lds<D, kBlockN, kWaves>(K, N, (j + 1) * kBlockN, kbuf[(j + 1) & 1], wave, lane);
+      copy_rows_lds<D, kBlockN, kWaves>(V, N, (j + 1) * kBlockN, vbuf[(j + 1) & 1], wave, lane);
     }
     if (!wave_active || j > wave_last) continue;
     const lds_char* kb_ = kbuf[j & 1];
     const lds_char* vb_ = vbuf[j & 1];
 
     // ---- S^T = K_j Q^T : s[kb][qb], keys kb*32.., queries qb*32..
-    f32x16 s[2][2];
+    f32x16 s[2][QB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < C::kDSteps; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3)))*)(kb_ + lds_off_bytes<D>(kb * 32 + l32, ds * 2 + half));
+        const bf16x8 kf = read_row_operand<D>(kb_, kb * 32 + l32, ds, half);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(kf, qf[qb][ds], s[kb][qb]);
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(kf, qf[qb][ds], s[kb][qb]);
       }
     }
 
@@ -174,7 +158,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           const int query = wq0 + qb * 32 + l32;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -187,9 +171,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     }
 
     // ---- online softmax per query block; P packed to bf16 B operands
-    bf16x8 pk[2][2][2];  // [qb][kb][16-key chunk]
+    bf16x8 pk[QB][2][2];  // [qb][kb][16-key chunk]
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float mx = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -227,25 +211,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     }
 
     // ---- O^T += V_j^T P^T
-    const int g = lane >> 4, j16 = lane & 15;
 #pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db) {
-      const int dcol = db * 32 + (g & 1) * 16 + (j16 & 3) * 4;
-      const int chunk = dcol >> 3;
-      const int boff = (dcol & 7) * 2;
+    for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const int r1 = kb * 32 + cc * 16 + half * 4 + (j16 >> 2);
-          const s16x4 va = ds_read_tr(vb_ + lds_off_bytes<D>(r1, chunk) + boff);
-          const s16x4 vb = ds_read_tr(vb_ + lds_off_bytes<D>(r1 + 8, chunk) + boff);
-          const s16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+          const bf16x8 vf = read_tr_operand<D>(vb_, kb * 32 + cc * 16, db * 32, lane);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma32(vf, pk[qb][kb][cc], o[qb][db]);
+          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf, pk[qb][kb][cc], o[qb][db]);
         }
-    }
   }
 
   // ---- epilogue: O = acc / l, L = m*scale + ln l
@@ -253,7 +228,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   __bf16* __restrict__ O = (__bf16*)a.o + head_off;
   float* __restrict__ Lse = a.lse + (size_t)bh * N;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = sum_halves(l[qb]);
     const float inv = 1.0f / lt;
     const int row = wq0 + qb * 32 + l32;
@@ -273,7 +248,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
 template <int D, bool CAUSAL>
 int launch(const FwdArgs& a, hipStream_t stream) {
-  const int n_qtiles = (a.N + kBlockM - 1) / kBlockM;
+  const int n_qtiles = (a.N + FwdCfg<D>::kBlockM - 1) / FwdCfg<D>::kBlockM;
   const TileSched sched = make_sched(n_qtiles, a.B * a.H, CAUSAL);
   const long grid = (long)n_qtiles * a.B * a.H;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, a, sched);
@@ -285,6 +260,7 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.D == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
   if (a.D == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+  if (a.D == 256) return a.causal ? launch<256, true>(a, stream) : launch<256, false>(a, stream);
   return -2;
 }
 

@@ -39,7 +39,6 @@ struct BwdArgs {
 // Each returns 0 on a successful launch, -1 when the launch failed and -2
 // when no kernel instance exists for the shape.
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
-int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 int launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);

@@ -47,16 +47,31 @@ COMMON_FLAGS = [
 ]
 
 
-# Kernel sources never produce or test NaN on purpose: without this the
-# compiler wraps every float max in a canonicalising v_max(x, x).  The API
-# file (argument checks on the host) keeps full IEEE semantics.
+# Kernel sources never produce or test NaN on purpose: without
+# -fno-honor-nans the compiler wraps every float max in a canonicalising
+# v_max(x, x).  The API file (argument checks on the host) keeps full IEEE
+# semantics.  MFMA results are kept in architectural VGPRs: with the default
+# accumulator-register form the compiler moved the O accumulators between
+# AGPRs and VGPRs on every key tile (hundreds of v_accvgpr moves per tile).
+# The D = 256 forward keeps its 128-register O accumulators in AGPRs (and
+# this compiler crashes on it in VGPR form), so it is built without it.
 KERNEL_FLAGS = ["-fno-honor-nans"]
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 HOST_ONLY_SOURCES = {"fa_api.hip"}
+AGPR_FORM_SOURCES = {"fa_fwd_bf16_d256.hip"}
+
+
+def source_flags(name: str) -> list[str]:
+    if name in HOST_ONLY_SOURCES:
+        return []
+    if name in AGPR_FORM_SOURCES:
+        return list(KERNEL_FLAGS)
+    return KERNEL_FLAGS + VGPR_FORM
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    extra = [] if os.path.basename(src) in HOST_ONLY_SOURCES else KERNEL_FLAGS
+    extra = source_flags(os.path.basename(src))
     cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -49,7 +49,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   lds_char* kbuf[2] = {smem, smem + kTileBytes};
   lds_char* vbuf[2] = {smem + 2 * kTileBytes, smem + 3 * kTileBytes};
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+            half = lane >> 5;
   int qtile, bh;
   sched_item(sched, blockIdx.x, qtile, bh);
   const int N = a.N;
@@ -207,7 +208,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 
   lds_char* lbuf[2] = {stat0, stat0 + C::kStatBytes};
   lds_char* dbuf[2] = {stat0 + 2 * C::kStatBytes, stat0 + 3 * C::kStatBytes};
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+            half = lane >> 5;
   int ktile, bh;
   sched_item(sched, blockIdx.x, ktile, bh);
   const int N = a.N;

@@ -88,21 +88,26 @@ __device__ __forceinline__ float sum_halves(float x) {
 // ---------------------------------------------------------------- LDS
 //
 // K and V tiles live in LDS as rows of D bf16 split into 16-byte chunks.
-// The chunk c of row r is stored at physical chunk c ^ swz(r).  swz is a bit
-// permutation of the low row bits chosen so that both access patterns are
-// free of bank conflicts:
-//   * ds_read_b128 of one logical chunk from 16 consecutive rows (K operand),
-//   * ds_read_b64_tr_b16 of 4 consecutive rows x 2 adjacent chunks (V operand).
+// The chunk c of row r is stored at physical chunk c ^ swz(r).  The LDS
+// serves 256 bytes (16 chunk slots) per cycle; swz is chosen so that both
+// access patterns of the kernels hit 16 distinct slots:
+//   * ds_read_b128: 16 lanes read one logical chunk from 16 consecutive rows
+//     (swz must be a bijection on those rows);
+//   * ds_read_b64_tr_b16: 32 lanes read 4 consecutive chunks (4-aligned)
+//     from 4 consecutive rows (4-aligned), so each of the 4 rows must land
+//     its 4 chunks in a different 4-slot group.
+// For rows of 256 bytes (D = 128; D = 256 rows span two windows) this is
+// the swap of the two 2-bit halves of r % 16.  For D = 64 two rows share a
+// window: x = (r / 2) % 8 must be a bijection, with bit 2 of the result
+// separating rows r and r + 2.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (D >= 128) {
-    // row bits (b3 b2 b1 b0) -> chunk bits (b3 b1 b0 b2); D = 256 uses 4 of its 5 chunk bits
-    int x = r & 15;
-    return ((x & 3) << 1) | ((x >> 2) & 1) | (x & 8);
+    const int x = r & 15;
+    return ((x & 3) << 2) | (x >> 2);
   } else {
-    // D = 64: two rows per 256-byte bank window; x = (r / 2) % 8 -> chunk bits (x0 x1 x2) -> (x1 x0 x2)
-    int x = (r >> 1) & 7;
-    return ((x & 1) << 1) | ((x >> 1) & 1) << 2 | ((x >> 2) & 1);
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
   }
 }
 
@@ -131,6 +136,29 @@ __device__ __forceinline__ void load_lds16(const void* gptr, const void __attrib
       "global_load_lds_dwordx4 %0, off"
       :
       : "v"(gptr), "{m0}"(base));
+}
+
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset: the address arithmetic per copy is scalar only.  The compiler
+// may rebuild the SGPR base with v_readfirstlane right before this
+// instruction, and a VMEM instruction may read an SGPR written by a VALU
+// instruction only after 5 wait states; the compiler cannot see the read
+// inside the assembly, so the s_nop 4 here provides them (and covers the
+// M0 write too).
+__device__ __forceinline__ void load_lds16_sbase(const void* sbase, uint32_t voff,
+                                                 const void __attribute__((address_space(3))) * lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  // readfirstlane returns a signed int: widen each half through uint32_t so
+  // the low half is zero-extended (a sign-extended low half with bit 31 set
+  // would corrupt the upper address bits).
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)sbase);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)sbase >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile(
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sb), "{m0}"(base));
 }
 
 // Same, 4 bytes per lane: lane l's dword lands at lds_base + 4 * l.
@@ -165,6 +193,53 @@ __device__ __forceinline__ void copy_rows_lds(const __bf16* __restrict__ src, in
     load_lds16(src + (size_t)grow * D + c * 8, buf + slot0 * 16);
   }
 }
+
+// Row-tile copier with loop-invariant per-lane offsets: ROWS x D bf16 rows
+// starting at a uniform row go to a swizzled LDS tile with a scalar base per
+// copy.  Callers keep every tile inside the tensor (a ragged last tile is
+// taken shifted back so that it ends at row N-1); only tensors shorter than
+// a tile need per-lane clamping.
+template <int D, int ROWS, int WAVES>
+struct RowTileCopier {
+  static constexpr int kRowChunks = D / 8;
+  static constexpr int kChunksPerWave = ROWS * kRowChunks / WAVES;
+  static constexpr int kLoads = kChunksPerWave / 64;
+  static_assert(kChunksPerWave % 64 == 0, "tile must split into whole wave loads");
+  uint32_t off[kLoads];  // byte offset of this lane's chunk relative to the tile's first row
+  int rowi[kLoads];      // its row within the tile
+  int wave_slot0;
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    wave_slot0 = wave * kChunksPerWave;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int slot = wave_slot0 + i * 64 + lane;
+      const int r = slot / kRowChunks;
+      const int c = (slot % kRowChunks) ^ swz<D>(r);
+      rowi[i] = r;
+      off[i] = (uint32_t)((r * D + c * 8) * 2);
+    }
+  }
+
+  // Rows row0 .. row0+ROWS-1 must all exist: a scalar base per copy.
+  __device__ __forceinline__ void copy(const __bf16* __restrict__ src, int row0, lds_char* buf) const {
+    const __bf16* base = src + (size_t)row0 * D;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_lds16_sbase(base, off[i], buf + (wave_slot0 + i * 64) * 16);
+  }
+
+  // A tile reaching past row N-1 (row0 <= N-1): rows past it are clamped
+  // onto it per lane.
+  __device__ __forceinline__ void copy_clamped(const __bf16* __restrict__ src, int N, int row0, lds_char* buf) const {
+    const __bf16* base = src + (size_t)row0 * D;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int over = row0 + rowi[i] - (N - 1);
+      const uint32_t o = over > 0 ? off[i] - (uint32_t)(over * D * 2) : off[i];
+      load_lds16_sbase(base, o, buf + (wave_slot0 + i * 64) * 16);
+    }
+  }
+};
 
 // MFMA operand of 8 bf16 along k, read transposed out of a swizzled [rows][D]
 // LDS tile (rows are the k index, D the m/n index).  The 32 m/n values are

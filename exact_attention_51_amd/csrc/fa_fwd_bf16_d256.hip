@@ -1,0 +1,29 @@
+// fa_fwd_bf16_d256.hip -- forward instance for D = 256 (one 32-row query
+// block per wave, two-deep K/V ring).  Built without forcing MFMA results
+// into architectural VGPRs: at D = 256 the O accumulators (128 registers)
+// belong in the accumulator registers.
+#include "fa_fwd_bf16.h"
+
+namespace fa {
+namespace fwd {
+
+template <int D, bool CAUSAL, int QB, int W>
+int launch(const FwdArgs& a, hipStream_t stream) {
+  using C = FwdCfg<D, QB, W>;
+  const int n_qtiles = (a.N + C::kBlockM - 1) / C::kBlockM;
+  const TileSched sched = make_sched(n_qtiles, a.B * a.H, CAUSAL);
+  const long grid = (long)n_qtiles * a.B * a.H;
+  if (a.N < 64)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QB, W, true>), dim3((unsigned)grid), dim3(64 * W), 0, stream, a, sched);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QB, W, false>), dim3((unsigned)grid), dim3(64 * W), 0, stream, a, sched);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace fwd
+
+int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream) {
+  return a.causal ? fwd::launch<256, true, 1, 4>(a, stream) : fwd::launch<256, false, 1, 4>(a, stream);
+}
+
+}  // namespace fa

@@ -66,10 +66,14 @@ struct FwdCfg {
 #define FA_FWD_NB 3
 #endif
   static constexpr int kNB = D <= 128 ? FA_FWD_NB : 2;   // ring depth (D = 256: 2 x 2 x 32 KB)
+  static_assert(kNB == 2 || kNB == 3, "the main loop is unrolled for a ring of 2 or 3 slots");
   // With two waves per SIMD at D >= 128 the Q^T operands move from
   // registers to LDS (same swizzled row layout as K) to stay within 256
   // registers; the LDS then holds the K/V ring plus every wave's Q rows.
-  static constexpr bool kQInLds = W == 8 && D >= 128;
+#ifndef FA_FWD_QLDS
+#define FA_FWD_QLDS 0
+#endif
+  static constexpr bool kQInLds = FA_FWD_QLDS && W == 8 && D >= 128;
   static constexpr int kQBytes = kQInLds ? W * kRowsPerWave * D * 2 : 0;
   static constexpr int kLdsBytes = 2 * kNB * kTileBytes + kQBytes;
   // one group = the K tile and the V tile a loop step issues
@@ -131,19 +135,22 @@ struct FwdKernel {
   // covered by the previous tile.  key0 is the tile's first row, kmin the
   // first key the tile contributes.
   __device__ __forceinline__ void mask(f32x16 (&acc)[2][QB], int key0, int kmin, int wq0, int N) {
+    // Element (kb, r) of this lane holds key base + off with a compile-time
+    // offset off; the visible keys are the offsets in [lo, hi).
+    const int base = key0 + half * 4;
+    const int lo = kmin - base;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      int hi = N - base;
+      if constexpr (CAUSAL) hi = min(hi, wq0 + qb * 32 + l32 + 1 - base);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int query = wq0 + qb * 32 + l32;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          bool keep = key < N && key >= kmin;
-          if constexpr (CAUSAL) keep = keep && key <= query;
-          acc[kb][qb][r] = keep ? acc[kb][qb][r] : -__builtin_inff();
+          const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+          acc[kb][qb][r] = (off >= lo && off < hi) ? acc[kb][qb][r] : -__builtin_inff();
         }
-      }
+    }
   }
 
   // Row max of a score tile (both halves agree afterwards).
@@ -206,31 +213,103 @@ struct FwdKernel {
     }
   }
 
-  // Instruction order of an unmasked step, as scheduling-group pipelines:
-  // the score MFMAs of the next tile are each paired with one K fragment
-  // read and a share of the exponentials of this tile; the P V MFMAs with
-  // their two transposed V reads and a share of the next tile's row max.
-  // Bounding the reads in flight this way also bounds register pressure.
-  __device__ __forceinline__ void schedule() {
-#ifndef FA_FWD_NO_SCHED
-    constexpr int kS = 2 * QB * C::kDSteps;     // score MFMAs
-    constexpr int kP = 4 * QB * C::kDBlocks;    // P V MFMAs
-    constexpr int kExp = 32 * QB;               // exponentials
-    constexpr int kValuA = 56 * QB;             // fma, pack, dot2 and friends of the exp stage
+  // ---- pipelined step, written in issue order -------------------------
+  // The S MFMAs of the next tile each carry their share of this tile's
+  // exponentials; the P V MFMAs of this tile each carry a share of the
+  // next tile's row max; every LDS fragment is read kPf fragments ahead of
+  // the MFMA that consumes it.  sched_barrier fences keep the compiler from
+  // regrouping the sequence (it would otherwise cluster reads next to their
+  // use and the MFMAs of one product together).
+  static constexpr int kKFrags = 2 * C::kDSteps;   // K fragments per tile, QB MFMAs each
+  static constexpr int kVFrags = 4 * C::kDBlocks;  // V fragments per tile, QB MFMAs each
+  static constexpr int kPf = 3;                    // read-ahead in fragments
+  static constexpr int kPairs = 16 * QB;           // exp pairs per tile and lane
+  static constexpr int kMaxUnits = 9 * QB;         // row-max work units per tile
+  static constexpr int kMaxStart = 2;              // first P V MFMA that carries row-max work
+
+  // K fragment i = (ds, kb) = (i / 2, i % 2)
+  __device__ __forceinline__ bf16x8 kfrag(const lds_char* kt, int i) const {
+    return *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[i >> 1] + (i & 1) * 32 * D * 2);
+  }
+  // V fragment j = (kb, cc, db): (kb, cc) = j / kDBlocks, db = j % kDBlocks
+  __device__ __forceinline__ bf16x8 vfrag(const lds_char* vt, int j) const {
+    const int kc = j / C::kDBlocks, db = j % C::kDBlocks;
+    const int rows = ((kc >> 1) * 32 + (kc & 1) * 16) * D * 2;
+    const s16x4 va = ds_read_tr(vt + voff[db][0] + rows);
+    const s16x4 vb = ds_read_tr(vt + voff[db][1] + rows);
+    const s16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+    return __builtin_bit_cast(bf16x8, v8);
+  }
+
+  __device__ __forceinline__ void pipelined(const lds_char* kt, const lds_char* vt, const f32x16 (&sc)[2][QB],
+                                            f32x16 (&sn)[2][QB], float c) {
+    constexpr int nS = kKFrags * QB;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float mc[QB];
 #pragma unroll
-    for (int i = 0; i < kS; ++i) {
-      if (i % QB == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // K fragment read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x400, kExp / kS, 0);           // exp
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuA / kS, 0);         // VALU
-    }
+    for (int qb = 0; qb < QB; ++qb) mc[qb] = m[qb] * c;
+    bf16x8 kf[kKFrags];
+    bf16x8 vf[kVFrags];
+    bf16x2 pr[QB][2][2][4];
+    bf16x8 pk[QB][2][2];
+    float t[QB][8];
+
 #pragma unroll
-    for (int i = 0; i < kP; ++i) {
-      if (i % QB == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V fragment reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                   // VALU (row max)
+    for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kt, i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // phase A: S of the next tile + exp of this tile
+#pragma unroll
+    for (int i = 0; i < kKFrags; ++i) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int ds = i >> 1, kb = i & 1;
+        sn[kb][qb] = mfma32(kf[i], qfrag(qb, ds), ds == 0 ? f32x16{} : sn[kb][qb]);
+        const int mi = i * QB + qb;
+#pragma unroll
+        for (int e = mi * kPairs / nS; e < (mi + 1) * kPairs / nS; ++e) {
+          const int eq = e / 16, kb2 = (e / 8) & 1, cc = (e / 4) & 1, w = e & 3;
+          const float e0 = fast_exp2(__builtin_fmaf(sc[kb2][eq][cc * 8 + 2 * w], c, -mc[eq]));
+          const float e1 = fast_exp2(__builtin_fmaf(sc[kb2][eq][cc * 8 + 2 * w + 1], c, -mc[eq]));
+          pr[eq][kb2][cc][w] = pack_bf16(e0, e1);
+          l[eq] = __builtin_amdgcn_fdot2_f32_bf16(pr[eq][kb2][cc][w], ones, l[eq], false);
+          if (w == 3)
+            pk[eq][kb2][cc] = join8(pr[eq][kb2][cc][0], pr[eq][kb2][cc][1], pr[eq][kb2][cc][2], pr[eq][kb2][cc][3]);
+        }
+      }
+      if (i + kPf < kKFrags)
+        kf[i + kPf] = kfrag(kt, i + kPf);
+      else
+        vf[i + kPf - kKFrags] = vfrag(vt, i + kPf - kKFrags);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#endif
+
+    // phase B: P V of this tile + row max of the next tile
+#pragma unroll
+    for (int j = 0; j < kVFrags; ++j) {
+      const int kc = j / C::kDBlocks, db = j % C::kDBlocks;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[j], pk[qb][kc >> 1][kc & 1], o[qb][db]);
+      if (j + kPf < kVFrags) vf[j + kPf] = vfrag(vt, j + kPf);
+      if (j >= kMaxStart) {
+        constexpr int nPos = kVFrags - kMaxStart;
+        const int p = j - kMaxStart;
+#pragma unroll
+        for (int u = p * kMaxUnits / nPos; u < (p + 1) * kMaxUnits / nPos; ++u) {
+          if (u < 8 * QB) {  // max of four scores
+            const int qb = u / 8, i = u % 8, kb = i >> 2, r = (i & 3) * 4;
+            t[qb][i] = __builtin_fmaxf(__builtin_fmaxf(sn[kb][qb][r], sn[kb][qb][r + 1]),
+                                       __builtin_fmaxf(sn[kb][qb][r + 2], sn[kb][qb][r + 3]));
+          } else {  // combine, then across the two halves of the wave
+            const int qb = u - 8 * QB;
+            const float a = __builtin_fmaxf(__builtin_fmaxf(t[qb][0], t[qb][1]), __builtin_fmaxf(t[qb][2], t[qb][3]));
+            const float b = __builtin_fmaxf(__builtin_fmaxf(t[qb][4], t[qb][5]), __builtin_fmaxf(t[qb][6], t[qb][7]));
+            mx[qb] = max_halves(__builtin_fmaxf(a, b));
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // O^T += V^T P^T from V ring slot vt (see vslot)
@@ -418,12 +497,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     issue_k(p + NB, b);
     issue_v(p + NB - 1, (b + NB - 1) % NB);
     k.update_max(c);
-    bf16x8 pk[QB][2][2];
-    k.scores(k.kbuf((b + 1) % NB), k.s[cur ^ 1]);
-    k.exponentiate(k.s[cur], c, pk);
-    k.accumulate(k.vslot(b), pk);
-    k.rowmax(k.s[cur ^ 1]);
-    k.schedule();
+    k.pipelined(k.kbuf((b + 1) % NB), k.vslot(b), k.s[cur], k.s[cur ^ 1], c);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;

@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd attention TFLOPS (4N²D·B·H, causal halved) + % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
-KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h", "fa_sched.h"]
+KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_bf16.h", "fa_device.h", "fa_sched.h"]
 
 
 def kernel_source_hash() -> str:

@@ -43,6 +43,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -53,6 +54,7 @@ namespace fwd {
 
 constexpr int kBlockN = 64;                // keys per K/V tile
 constexpr float kRescaleThreshold = 8.0f;  // exp2-domain growth allowed before O is rescaled
+constexpr float kMaxFloor = 1.0e30f;       // the running max starts at -kMaxFloor
 
 template <int D, int QB, int W>
 struct FwdCfg {
@@ -62,22 +64,20 @@ struct FwdCfg {
   static constexpr int kDSteps = D / 16;                 // k-steps of the S product
   static constexpr int kDBlocks = D / 32;                // 32-wide d blocks of O
   static constexpr int kTileBytes = kBlockN * D * 2;     // one K or V tile
-#ifndef FA_FWD_NB
-#define FA_FWD_NB 3
-#endif
-  static constexpr int kNB = D <= 128 ? FA_FWD_NB : 2;   // ring depth (D = 256: 2 x 2 x 32 KB)
-  static_assert(kNB == 2 || kNB == 3, "the main loop is unrolled for a ring of 2 or 3 slots");
-  // With two waves per SIMD at D >= 128 the Q^T operands move from
-  // registers to LDS (same swizzled row layout as K) to stay within 256
-  // registers; the LDS then holds the K/V ring plus every wave's Q rows.
-#ifndef FA_FWD_QLDS
-#define FA_FWD_QLDS 0
-#endif
-  static constexpr bool kQInLds = FA_FWD_QLDS && W == 8 && D >= 128;
-  static constexpr int kQBytes = kQInLds ? W * kRowsPerWave * D * 2 : 0;
-  static constexpr int kLdsBytes = 2 * kNB * kTileBytes + kQBytes;
-  // one group = the K tile and the V tile a loop step issues
-  static constexpr int kLoadsPerGroup = 2 * (kTileBytes / 16 / kWaves / 64);
+  // K/V ring: kNB slots each; K of position p is issued kLeadK steps
+  // before the step that first reads it, V kLeadV steps before.  Step p
+  // reads K(p+1) and V(p) and refills the slots of K(p) and V(p-1).
+  static constexpr int kNB = D <= 128 ? 4 : 2;
+  static constexpr int kLeadK = kNB;
+  static constexpr int kLeadV = kNB - 1;
+  static constexpr int kLdsBytes = 2 * kNB * kTileBytes;
+  // direct-to-LDS loads per wave for one K or V tile
+  static constexpr int kLoadsPerTile = kTileBytes / 16 / kWaves / 64;
+  // Loads a step may leave in flight when it starts (those of the
+  // kStepsInFlight previous steps): its barrier must publish K(p+1) and V(p).
+  static constexpr int kStepsInFlight = kNB - 2;
+  static_assert(kNB % 2 == 0, "the loop is unrolled over the ring and the two score sets");
+  static constexpr int kUnroll = kNB;
   // 8-wave workgroups put two waves on each SIMD (registers must stay <= 256)
   static constexpr int kWavesPerEU = W / 4;
 };
@@ -91,6 +91,7 @@ struct FwdKernel {
   bf16x8 qf[QB][C::kDSteps];  // Q^T as B operands: query column l32, d = ds*16 + half*8 + 0..7
   f32x16 o[QB][C::kDBlocks];  // O^T accumulators
   f32x16 s[2][2][QB];         // two score tiles in ping-pong: [set][kb][qb]
+  bf16x8 pk[QB][2][2];        // P of the tile in flight, as B operands
   float m[QB], l[QB], mx[QB];
   int koff[C::kDSteps];      // per-lane K operand offsets within a K tile
   int voff[C::kDBlocks][2];  // per-lane V operand offsets, V region base included
@@ -103,30 +104,16 @@ struct FwdKernel {
   __device__ __forceinline__ lds_char* kbuf(int b) const { return smem + b * C::kTileBytes; }
   __device__ __forceinline__ lds_char* vbuf(int b) const { return smem + (NB + b) * C::kTileBytes; }
   __device__ __forceinline__ const lds_char* vslot(int b) const { return smem + b * C::kTileBytes; }
-  __device__ __forceinline__ lds_char* qtile() const { return smem + 2 * NB * C::kTileBytes + wave * C::kRowsPerWave * D * 2; }
-  // Q^T operand for query block qb, d-step ds (LDS copy shares K's row layout)
-  __device__ __forceinline__ bf16x8 qfrag(int qb, int ds) const {
-    if constexpr (C::kQInLds)
-      return *(const bf16x8 __attribute__((address_space(3)))*)(qtile() + koff[ds] + qb * 32 * D * 2);
-    else
-      return qf[qb][ds];
-  }
 
   // S^T tile from the K buffer kt: acc[kb][qb]
   __device__ __forceinline__ void scores(const lds_char* kt, f32x16 (&acc)[2][QB]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[kb][qb][r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < C::kDSteps; ++ds)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[ds] + kb * 32 * D * 2);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[kb][qb] = mfma32(kf, qfrag(qb, ds), acc[kb][qb]);
+        for (int qb = 0; qb < QB; ++qb) acc[kb][qb] = mfma32(kf, qf[qb][ds], ds == 0 ? f32x16{} : acc[kb][qb]);
       }
   }
 
@@ -159,26 +146,30 @@ struct FwdKernel {
     for (int qb = 0; qb < QB; ++qb) {
       float t[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kb = i >> 2, r = (i & 3) * 4;
-        t[i] = __builtin_fmaxf(__builtin_fmaxf(acc[kb][qb][r], acc[kb][qb][r + 1]),
-                               __builtin_fmaxf(acc[kb][qb][r + 2], acc[kb][qb][r + 3]));
-      }
-      const float a = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), __builtin_fmaxf(t[2], t[3]));
-      const float b = __builtin_fmaxf(__builtin_fmaxf(t[4], t[5]), __builtin_fmaxf(t[6], t[7]));
-      mx[qb] = max_halves(__builtin_fmaxf(a, b));
+      for (int i = 0; i < 8; ++i) t[i] = max4(acc[i >> 2][qb], (i & 3) * 4);
+      mx[qb] = max_halves(max8(t));
     }
+  }
+  __device__ __forceinline__ static float max4(const f32x16& a, int r) {
+    return __builtin_fmaxf(__builtin_fmaxf(a[r], a[r + 1]), __builtin_fmaxf(a[r + 2], a[r + 3]));
+  }
+  __device__ __forceinline__ static float max8(const float (&t)[8]) {
+    const float a = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), __builtin_fmaxf(t[2], t[3]));
+    const float b = __builtin_fmaxf(__builtin_fmaxf(t[4], t[5]), __builtin_fmaxf(t[6], t[7]));
+    return __builtin_fmaxf(a, b);
   }
 
   // Raise the running max to include mx; rescale O and l when it grew by
   // more than the threshold in any lane of the wave (a wave-uniform branch).
+  // The running max starts at a finite floor, not -inf: a row may see only
+  // masked keys in its first tiles, and exp2(-inf - floor) is then 0.
   __device__ __forceinline__ void update_max(float c) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float m_new = __builtin_fmaxf(m[qb], mx[qb]);
       const bool grow = (m_new - m[qb]) * c > kRescaleThreshold;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float alpha = fast_exp2((m[qb] - m_new) * c);  // 0 on the first tile (m = -inf)
+        const float alpha = fast_exp2((m[qb] - m_new) * c);  // 0 on the first tile (m at the floor)
 #pragma unroll
         for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
@@ -189,43 +180,22 @@ struct FwdKernel {
     }
   }
 
-  // P = exp2(S c - m c) packed to bf16 B operands; the row sum is taken over
-  // the rounded P that enters the product.
-  __device__ __forceinline__ void exponentiate(const f32x16 (&sc)[2][QB], float c, bf16x8 (&pk)[QB][2][2]) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mc = m[qb] * c;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          bf16x2 pr[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e0 = fast_exp2(__builtin_fmaf(sc[kb][qb][cc * 8 + 2 * i], c, -mc));
-            const float e1 = fast_exp2(__builtin_fmaf(sc[kb][qb][cc * 8 + 2 * i + 1], c, -mc));
-            pr[i] = pack_bf16(e0, e1);
-            l[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr[i], ones, l[qb], false);
-          }
-          pk[qb][kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
-        }
-    }
-  }
-
-  // ---- pipelined step, written in issue order -------------------------
-  // The S MFMAs of the next tile each carry their share of this tile's
-  // exponentials; the P V MFMAs of this tile each carry a share of the
-  // next tile's row max; every LDS fragment is read kPf fragments ahead of
-  // the MFMA that consumes it.  sched_barrier fences keep the compiler from
-  // regrouping the sequence (it would otherwise cluster reads next to their
-  // use and the MFMAs of one product together).
+  // ---- the two halves of a pipelined step, written in issue order -----
+  // Phase A issues the score MFMAs of the next tile, each carrying its
+  // share of this tile's exponentials (P rounded to bf16, row sum over the
+  // rounded P).  Phase B issues the P V MFMAs of this tile, each carrying a
+  // share of the next tile's row max.  LDS fragments are read kPf fragments
+  // ahead of the MFMA that consumes them.  sched_barrier fences keep the
+  // compiler from regrouping the sequence (it would otherwise cluster reads
+  // next to their use and the MFMAs of one product together).
   static constexpr int kKFrags = 2 * C::kDSteps;   // K fragments per tile, QB MFMAs each
   static constexpr int kVFrags = 4 * C::kDBlocks;  // V fragments per tile, QB MFMAs each
   static constexpr int kPf = 3;                    // read-ahead in fragments
+  static constexpr int nS = kKFrags * QB;          // score MFMAs per step
+  static constexpr int nP = kVFrags * QB;          // P V MFMAs per step
   static constexpr int kPairs = 16 * QB;           // exp pairs per tile and lane
   static constexpr int kMaxUnits = 9 * QB;         // row-max work units per tile
-  static constexpr int kMaxStart = 2;              // first P V MFMA that carries row-max work
+  static constexpr int kMaxStart = 2;              // first P V MFMA carrying row-max work
 
   // K fragment i = (ds, kb) = (i / 2, i % 2)
   __device__ __forceinline__ bf16x8 kfrag(const lds_char* kt, int i) const {
@@ -241,30 +211,25 @@ struct FwdKernel {
     return __builtin_bit_cast(bf16x8, v8);
   }
 
-  __device__ __forceinline__ void pipelined(const lds_char* kt, const lds_char* vt, const f32x16 (&sc)[2][QB],
-                                            f32x16 (&sn)[2][QB], float c) {
-    constexpr int nS = kKFrags * QB;
+  // S of the next tile (K buffer kt, into sn) + exp of this tile (sc).
+  __device__ __forceinline__ void phase_a(const lds_char* kt, const f32x16 (&sc)[2][QB], f32x16 (&sn)[2][QB],
+                                          float c) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mc[qb] = m[qb] * c;
     bf16x8 kf[kKFrags];
-    bf16x8 vf[kVFrags];
     bf16x2 pr[QB][2][2][4];
-    bf16x8 pk[QB][2][2];
-    float t[QB][8];
-
 #pragma unroll
     for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kt, i);
     __builtin_amdgcn_sched_barrier(0);
-
-    // phase A: S of the next tile + exp of this tile
 #pragma unroll
     for (int i = 0; i < kKFrags; ++i) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int ds = i >> 1, kb = i & 1;
-        sn[kb][qb] = mfma32(kf[i], qfrag(qb, ds), ds == 0 ? f32x16{} : sn[kb][qb]);
+        sn[kb][qb] = mfma32(kf[i], qf[qb][ds], ds == 0 ? f32x16{} : sn[kb][qb]);
+        // exp pairs e = (qb, kb, cc, w) carried by this MFMA
         const int mi = i * QB + qb;
 #pragma unroll
         for (int e = mi * kPairs / nS; e < (mi + 1) * kPairs / nS; ++e) {
@@ -277,59 +242,50 @@ struct FwdKernel {
             pk[eq][kb2][cc] = join8(pr[eq][kb2][cc][0], pr[eq][kb2][cc][1], pr[eq][kb2][cc][2], pr[eq][kb2][cc][3]);
         }
       }
-      if (i + kPf < kKFrags)
-        kf[i + kPf] = kfrag(kt, i + kPf);
-      else
-        vf[i + kPf - kKFrags] = vfrag(vt, i + kPf - kKFrags);
+      if (i + kPf < kKFrags) kf[i + kPf] = kfrag(kt, i + kPf);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
 
-    // phase B: P V of this tile + row max of the next tile
+  // P V of the tile whose P is in pk (V buffer vt) + row max of sn into mx.
+  __device__ __forceinline__ void phase_b(const lds_char* vt, const f32x16 (&sn)[2][QB]) {
+    bf16x8 vf[kVFrags];
+    float t[QB][8];
+#pragma unroll
+    for (int j = 0; j < kPf; ++j) vf[j] = vfrag(vt, j);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kVFrags; ++j) {
       const int kc = j / C::kDBlocks, db = j % C::kDBlocks;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[j], pk[qb][kc >> 1][kc & 1], o[qb][db]);
-      if (j + kPf < kVFrags) vf[j + kPf] = vfrag(vt, j + kPf);
-      if (j >= kMaxStart) {
-        constexpr int nPos = kVFrags - kMaxStart;
-        const int p = j - kMaxStart;
+      for (int qb = 0; qb < QB; ++qb) {
+        o[qb][db] = mfma32(vf[j], pk[qb][kc >> 1][kc & 1], o[qb][db]);
+        const int mi = j * QB + qb;
+        if (mi >= kMaxStart) {
+          constexpr int nPos = nP - kMaxStart;
+          const int p = mi - kMaxStart;
 #pragma unroll
-        for (int u = p * kMaxUnits / nPos; u < (p + 1) * kMaxUnits / nPos; ++u) {
-          if (u < 8 * QB) {  // max of four scores
-            const int qb = u / 8, i = u % 8, kb = i >> 2, r = (i & 3) * 4;
-            t[qb][i] = __builtin_fmaxf(__builtin_fmaxf(sn[kb][qb][r], sn[kb][qb][r + 1]),
-                                       __builtin_fmaxf(sn[kb][qb][r + 2], sn[kb][qb][r + 3]));
-          } else {  // combine, then across the two halves of the wave
-            const int qb = u - 8 * QB;
-            const float a = __builtin_fmaxf(__builtin_fmaxf(t[qb][0], t[qb][1]), __builtin_fmaxf(t[qb][2], t[qb][3]));
-            const float b = __builtin_fmaxf(__builtin_fmaxf(t[qb][4], t[qb][5]), __builtin_fmaxf(t[qb][6], t[qb][7]));
-            mx[qb] = max_halves(__builtin_fmaxf(a, b));
+          for (int u = p * kMaxUnits / nPos; u < (p + 1) * kMaxUnits / nPos; ++u) {
+            if (u < 8 * QB) {
+              t[u / 8][u % 8] = max4(sn[(u % 8) >> 2][u / 8], (u % 4) * 4);
+            } else {
+              const int q2 = u - 8 * QB;
+              mx[q2] = max_halves(max8(t[q2]));
+            }
           }
         }
       }
+      if (j + kPf < kVFrags) vf[j + kPf] = vfrag(vt, j + kPf);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-
-  // O^T += V^T P^T from V ring slot vt (see vslot)
-  __device__ __forceinline__ void accumulate(const lds_char* vt, const bf16x8 (&pk)[QB][2][2]) {
-#pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int rows = (kb * 32 + cc * 16) * D * 2;
-          const s16x4 va = ds_read_tr(vt + voff[db][0] + rows);
-          const s16x4 vb = ds_read_tr(vt + voff[db][1] + rows);
-          const s16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf, pk[qb][kb][cc], o[qb][db]);
-        }
-  }
 };
+
+// f(i + j, integral_constant<j>) for j = 0, 1, ... while i + j < n
+template <typename F, int... J>
+__device__ __forceinline__ void unrolled(int i, int n, F& f, std::integer_sequence<int, J...>) {
+  (void)((i + J < n && (f(i + J, std::integral_constant<int, J>()), true)) && ...);
+}
 
 // SMALL: N < 64, a single tile whose missing rows are clamped per lane.
 template <int D, bool CAUSAL, int QB, int W, bool SMALL>
@@ -338,6 +294,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W),
 fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   using C = FwdCfg<D, QB, W>;
   constexpr int NB = C::kNB;
+  constexpr int LK = C::kLeadK, LV = C::kLeadV;
   constexpr int kWaves = C::kWaves;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLdsBytes];
   FwdKernel<D, CAUSAL, QB, W> k;
@@ -363,37 +320,32 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   const bool wave_active = wq0 < N;
   const int n_ktiles_all = (N + kBlockN - 1) / kBlockN;
   int nt = n_ktiles_all;
-  int wave_last = n_ktiles_all - 1;
-  if constexpr (CAUSAL) {
-    nt = min(q0 + C::kBlockM - 1, N - 1) / kBlockN + 1;
-    wave_last = min(wq0 + C::kRowsPerWave - 1, N - 1) / kBlockN;
-  }
+  if constexpr (CAUSAL) nt = min(q0 + C::kBlockM - 1, N - 1) / kBlockN + 1;
   const bool ragged = (N % kBlockN) != 0;
 
   // Processing order.  Online softmax does not depend on the order of the
-  // key tiles, so the tiles that need a mask go first: the block's diagonal
-  // region under causal masking (tiles q0/64 .. nt-1), else a ragged last
-  // tile (or the single tile of a short tensor), else none.  These R tiles
-  // run through a plain serial step; the remaining main tiles 0 .. nt-R-1
-  // are below every wave's diagonal and run through the pipelined step,
-  // which then needs no mask code and no per-wave skip.
+  // key tiles, so the R tiles that need a mask go first: the block's
+  // diagonal region under causal masking (tiles q0/64 .. nt-1), else a
+  // ragged last tile (or the single tile of a short tensor), else none.
+  // Every wave processes every tile of its block; keys a wave may not see
+  // are masked.
   int first_masked = nt;
   if (SMALL) first_masked = 0;
   else if (CAUSAL) first_masked = q0 / kBlockN;
   else if (ragged) first_masked = n_ktiles_all - 1;
   const int R = nt - first_masked;
-  // tile at sequence position p (positions past the end repeat the last tile)
+  // tile at sequence position p (positions past the end load a valid tile
+  // that is never read)
   auto seq_tile = [&](int p) { return p < R ? first_masked + p : p - R; };
   // First row of key tile t: tiles lie inside the tensor, a ragged last
   // tile is shifted back to end at row N-1 (its keys below t*64 are masked).
   auto tile_row0 = [&](int t) { return SMALL ? 0 : min(min(t, n_ktiles_all - 1) * kBlockN, N - kBlockN); };
-  // Ring slots are counted from the first main position, so that the
-  // unrolled main loop sees compile-time slots.
-  auto ring = [&](int p) { return ((p - R) % NB + NB) % NB; };
+  auto mask_tile = [&](f32x16 (&acc)[2][QB], int p) {
+    const int t = seq_tile(p);
+    k.mask(acc, tile_row0(t), t * kBlockN, wq0, N);
+  };
 
-  // Load group g = (K at position g+1, V at position g).  Groups past the
-  // end repeat the last tile: they keep the per-step vmcnt count fixed and
-  // are never read.
+  // K and V of sequence position p go to ring slot p % NB.
   RowTileCopier<D, kBlockN, kWaves> cp;
   cp.init(wave, lane);
   auto issue_k = [&](int p, int b) {
@@ -404,21 +356,15 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     if constexpr (SMALL) cp.copy_clamped(V, N, 0, k.vbuf(b));
     else cp.copy(V, tile_row0(seq_tile(p)), k.vbuf(b));
   };
-
-  issue_k(0, ring(0));
-  if constexpr (C::kQInLds) {  // this wave's Q rows, behind K at position 0 in the load order
-    RowTileCopier<D, C::kRowsPerWave, 1> cq;
-    cq.init(0, lane);
-    if (wq0 + C::kRowsPerWave <= N)
-      cq.copy(Q, wq0, k.qtile());
-    else
-      cq.copy_clamped(Q, N, min(wq0, N - 1), k.qtile());
-  }
+  // Prologue loads, oldest first: K0, then K(i+1), V(i) for i = 0, 1, ...
+  // (the order in which the first steps need them).
+  issue_k(0, 0);
 #pragma unroll
-  for (int g = 0; g < NB - 1; ++g) {
-    issue_k(g + 1, ring(g + 1));
-    issue_v(g, ring(g));
+  for (int i = 0; i < LK - 1; ++i) {
+    issue_k(i + 1, i + 1);
+    if (i < LV) issue_v(i, i);
   }
+  constexpr int kPrologueAfterK0 = LK + LV - 1;  // tiles issued after K0
 
   // per-lane loop-invariant LDS offsets (row offsets of kb/cc blocks keep the swizzle)
 #pragma unroll
@@ -439,93 +385,44 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   for (int qb = 0; qb < QB; ++qb) {
     int row = wq0 + qb * 32 + k.l32;
     row = row < N ? row : N - 1;
-    if constexpr (!C::kQInLds) {
 #pragma unroll
-      for (int ds = 0; ds < C::kDSteps; ++ds) k.qf[qb][ds] = *(const bf16x8*)(Q + (size_t)row * D + ds * 16 + k.half * 8);
-    }
+    for (int ds = 0; ds < C::kDSteps; ++ds) k.qf[qb][ds] = *(const bf16x8*)(Q + (size_t)row * D + ds * 16 + k.half * 8);
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) k.o[qb][db][r] = 0.f;
-    k.m[qb] = -__builtin_inff();
+    k.m[qb] = -kMaxFloor;
     k.l[qb] = 0.f;
   }
   const float c = a.scale_log2;
 
-  // ---- masked region: serial steps, position p = tile first_masked + p
-  for (int p = 0; p < R; ++p) {
-    // group p holds V at p; K at p came with group p-1 (K at 0 and Q first)
-    wait_vmcnt<(NB - 2) * C::kLoadsPerGroup>();
-    __syncthreads();
-    const int t = first_masked + p;
-    if (wave_active && t <= wave_last) {
-      bf16x8 pk[QB][2][2];
-      k.scores(k.kbuf(ring(p)), k.s[0]);
-      if (SMALL || (CAUSAL && t == wave_last) || (ragged && t == n_ktiles_all - 1))
-        k.mask(k.s[0], tile_row0(t), t * kBlockN, wq0, N);
-      k.rowmax(k.s[0]);
-      k.update_max(c);
-      k.exponentiate(k.s[0], c, pk);
-      k.accumulate(k.vslot(ring(p)), pk);
-    }
-    __syncthreads();  // K at p is read in this step: refill its slot only now
-    issue_k(p + NB, ring(p + NB));
-    issue_v(p + NB - 1, ring(p + NB - 1));
-  }
+  // S of position 0
+  wait_vmcnt<kPrologueAfterK0 * C::kLoadsPerTile>();
+  __syncthreads();
+  k.scores(k.kbuf(0), k.s[0]);
+  if (R > 0) mask_tile(k.s[0], 0);
+  k.rowmax(k.s[0]);
 
-  // ---- main region: pipelined steps at positions p = R .. nt-1
-  const int n_main = nt - R;
-  if (n_main > 0) {
-    // K at position R: K at 0 (and Q) when there is no masked region, else
-    // it came with group R-1, which the last masked step waited for.
-    if (R == 0) {
-      wait_vmcnt<(NB - 1) * C::kLoadsPerGroup>();
-      __syncthreads();
-    }
-    k.scores(k.kbuf(0), k.s[0]);
-    k.rowmax(k.s[0]);
-  }
-  // One step at position p (main index i = p - R): wait for group p
-  // (K at p+1, V at p), refill, then S at p+1 alongside exp(S at p), then
-  // P V at p alongside rowmax(S at p+1).  Ring slot and score set are the
-  // compile-time constants i % NB and i % 2.
-  auto step = [&](int p, auto bconst, auto curconst) {
-    constexpr int b = decltype(bconst)::value;
-    constexpr int cur = decltype(curconst)::value;
-    wait_vmcnt<(NB - 2) * C::kLoadsPerGroup>();
+  // Step p: exp and P V of position p, S and row max of position p+1, as
+  // phase A (score MFMAs + exponentials) then phase B (P V MFMAs + row
+  // max).  The step's barrier publishes K(p+1) and V(p) and frees the slots
+  // of K(p) and V(p-1), which the step refills with positions p+LK, p+LV.
+  // Ring slot and score set are compile-time: the loop is unrolled NB times.
+  auto step = [&](int p, auto jconst) {
+    constexpr int j = decltype(jconst)::value;  // p % kUnroll
+    constexpr int b = j % NB;                   // p % NB
+    constexpr int cur = j & 1;                  // p % 2
+    wait_vmcnt<C::kStepsInFlight * 2 * C::kLoadsPerTile>();
     __syncthreads();
-    issue_k(p + NB, b);
-    issue_v(p + NB - 1, (b + NB - 1) % NB);
+    issue_k(p + LK, (b + LK) % NB);
+    issue_v(p + LV, (b + LV) % NB);
     k.update_max(c);
-    k.pipelined(k.kbuf((b + 1) % NB), k.vslot(b), k.s[cur], k.s[cur ^ 1], c);
+    k.phase_a(k.kbuf((b + 1) % NB), k.s[cur], k.s[cur ^ 1], c);
+    if (p + 1 < R) mask_tile(k.s[cur ^ 1], p + 1);
+    k.phase_b(k.vslot(b), k.s[cur ^ 1]);
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2 % NB>;
-  using I3 = std::integral_constant<int, 3 % NB>;
-  using I4 = std::integral_constant<int, 4 % NB>;
-  using I5 = std::integral_constant<int, 5 % NB>;
-  // unrolled over lcm(2, NB) steps so that ring slot and score set are static
-  for (int i = 0; i < n_main; i += 2 * NB) {
-    const int p = R + i;
-    step(p, I0(), I0());
-    if (i + 1 >= n_main) break;
-    step(p + 1, I1(), I1());
-    if (i + 2 >= n_main) break;
-    if constexpr (NB == 3) {
-      step(p + 2, I2(), I0());
-      if (i + 3 >= n_main) break;
-      step(p + 3, I3(), I1());
-      if (i + 4 >= n_main) break;
-      step(p + 4, I4(), I0());
-      if (i + 5 >= n_main) break;
-      step(p + 5, I5(), I1());
-    } else {
-      step(p + 2, I0(), I0());
-      if (i + 3 >= n_main) break;
-      step(p + 3, I1(), I1());
-    }
-  }
+  for (int i = 0; i < nt; i += C::kUnroll)
+    unrolled(i, nt, step, std::make_integer_sequence<int, C::kUnroll>());
   wait_vmcnt<0>();  // no direct-to-LDS copy may outlive the workgroup
 
   // ---- epilogue: O = acc / l, L = m*scale + ln l

@@ -1,0 +1,174 @@
+"""rocprofv3 evidence for the forward kernel at the bench workload.
+
+Run on a GPU machine from the repository root:
+
+    python3 profile_fwd.py            # kernel trace + FETCH_SIZE / WRITE_SIZE passes
+
+Writes its summaries under gpurun_out/profile_fwd/profiles/ (the GPU machine
+keeps only gpurun_out/); `python3 profile_fwd.py --summarize` rebuilds them
+from the returned CSVs, under profiles/:
+  fwd_bf16_c3_kernel_trace.md  per-kernel durations of `bench.py --no-cpu --no-others`
+  fwd_bf16_c3_traffic.md       HBM bytes per launch of the forward kernel
+  fwd_bf16_c3_traffic.json     the same figure, keyed by a hash of the kernel
+                               sources (bench.py reports it only while the
+                               hash still matches)
+
+The TCC FETCH_SIZE / WRITE_SIZE counters are calibrated against a plain
+device copy of known size: the factor (bytes moved / counter bytes) for each
+counter is applied to the forward kernel's counter value.  Each counter is
+collected in its own rocprofv3 pass (counter-block limits).
+
+`python3 profile_fwd.py --copy BYTES` is the calibration workload: it copies a
+BYTES-long device buffer three times (run under rocprofv3 by the main mode).
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(ROOT, "gpurun_out", "profile_fwd")
+PROFILES = os.path.join(ROOT, "profiles")
+FWD_KERNEL = "fwd_bf16_kernel"
+COPY_BYTES = 1 << 30
+BENCH = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "30", "--warmup", "5", "--no-cpu", "--no-others"]
+
+
+def copy_workload(nbytes: int) -> None:
+    import torch
+
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(f"copied {nbytes} bytes 3 times", flush=True)
+
+
+def run(cmd: list[str], timeout: int) -> None:
+    """Run a rocprofv3 pass.  rocprofv3 may end with SIGSEGV after the
+    profiled program has finished and its results are written; the caller
+    checks that the result files exist."""
+    print("+ " + " ".join(cmd), flush=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    rc = subprocess.run(cmd, timeout=timeout, env=env, cwd="/tmp").returncode
+    if rc not in (0, 139, -11):
+        raise SystemExit(f"rocprofv3 failed with exit code {rc}")
+
+
+def counter_rows(outdir: str) -> list[dict]:
+    (path,) = glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True)
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def per_dispatch(rows: list[dict], name_filter) -> list[float]:
+    vals: dict[int, float] = {}
+    for r in rows:
+        if name_filter(r["Kernel_Name"]):
+            d = int(r["Dispatch_Id"])
+            vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+    return [vals[d] for d in sorted(vals)]
+
+
+def kernel_source_hash() -> str:
+    sys.path.insert(0, ROOT)
+    import bench
+
+    return bench.kernel_source_hash()
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--copy", type=int, default=0, help="calibration workload: copy this many bytes")
+    ap.add_argument("--summarize", action="store_true",
+                    help="only rebuild profiles/ from the CSVs already under gpurun_out/profile_fwd")
+    args = ap.parse_args()
+    if args.copy:
+        copy_workload(args.copy)
+        return 0
+
+    if not args.summarize:
+        os.makedirs(OUT, exist_ok=True)
+        me = [sys.executable, os.path.abspath(__file__)]
+        run(cmd_kernel_trace(), 600)  # 1. kernel trace with per-kernel statistics
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):  # 2. one counter per pass: forward, then copy
+            run(["rocprofv3", "--pmc", ctr, "--kernel-include-regex", FWD_KERNEL, "--output-format", "csv", "-d",
+                 os.path.join(OUT, f"fwd_{ctr}"), "-o", "run", "--", *BENCH], 300)
+            run(["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", os.path.join(OUT, f"copy_{ctr}"), "-o",
+                 "run", "--", *me, "--copy", str(COPY_BYTES)], 300)
+    summarize(OUT, PROFILES if args.summarize else os.path.join(OUT, "profiles"))
+    return 0
+
+
+def cmd_kernel_trace() -> list[str]:
+    return ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", os.path.join(OUT, "ktrace"),
+            "-o", "run", "--", *BENCH]
+
+
+def summarize(out: str, dest: str) -> None:
+    """Turn the rocprofv3 CSVs under `out` into the summaries under `dest`."""
+    os.makedirs(dest, exist_ok=True)
+    (stats,) = glob.glob(os.path.join(out, "ktrace", "**", "*kernel_stats.csv"), recursive=True)
+    with open(stats) as f:
+        krows = list(csv.DictReader(f))
+    counters = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        fwd = per_dispatch(counter_rows(os.path.join(out, f"fwd_{ctr}")), lambda n: FWD_KERNEL in n)
+        cp = per_dispatch(counter_rows(os.path.join(out, f"copy_{ctr}")), lambda n: True)
+        cp = sorted(cp)[-3:]  # the three copies are the largest dispatches
+        counters[ctr] = {"fwd_kib": fwd, "copy_kib": cp}
+    fetch_f = (COPY_BYTES / 1024) / statistics.median(counters["FETCH_SIZE"]["copy_kib"])
+    write_f = (COPY_BYTES / 1024) / statistics.median(counters["WRITE_SIZE"]["copy_kib"])
+    fetch_b = statistics.median(counters["FETCH_SIZE"]["fwd_kib"][1:]) * 1024 * fetch_f
+    write_b = statistics.median(counters["WRITE_SIZE"]["fwd_kib"][1:]) * 1024 * write_f
+    total = fetch_b + write_b
+    rec = {
+        "kernel": FWD_KERNEL,
+        "workload": "causal forward B=2 H=16 N=8192 D=128 bf16",
+        "kernel_source_hash": kernel_source_hash(),
+        "bytes_per_launch": round(total),
+        "fetch_bytes": round(fetch_b),
+        "write_bytes": round(write_b),
+        "copy_scale_fetch": fetch_f,
+        "copy_scale_write": write_f,
+        "raw": counters,
+        "command": "python3 profile_fwd.py",
+    }
+    with open(os.path.join(dest, "fwd_bf16_c3_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+
+    lines = ["# Forward kernel, causal B=2 H=16 N=8192 D=128 bf16: kernel trace", "",
+             "Command (repository root, GPU box): `python3 profile_fwd.py`, which runs", "",
+             "    " + " ".join(cmd_kernel_trace()).replace(ROOT + "/", "").replace(sys.executable, "python3"), "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in krows:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    with open(os.path.join(dest, "fwd_bf16_c3_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    algo = 2 * 16 * 8192 * 128 * 2 * 4 + 2 * 16 * 8192 * 4  # Q, K, V read + O written, L written
+    lines = ["# Forward kernel, causal B=2 H=16 N=8192 D=128 bf16: HBM traffic per launch", "",
+             "Command (repository root, GPU box): `python3 profile_fwd.py` (one rocprofv3 `--pmc` pass per counter,",
+             "forward kernel filtered by name; calibration = 1 GiB device copy, `python3 profile_fwd.py --copy 1073741824`).", "",
+             f"- FETCH_SIZE scale (copy bytes / counter bytes): {fetch_f:.4f}",
+             f"- WRITE_SIZE scale: {write_f:.4f}",
+             f"- forward fetch: {fetch_b / 2**20:.1f} MiB, write: {write_b / 2**20:.1f} MiB, total {total / 2**20:.1f} MiB per launch",
+             f"- algorithmic bytes (Q, K, V read once; O, L written once): {algo / 2**20:.1f} MiB",
+             f"- ratio measured / algorithmic: {total / algo:.2f}",
+             f"- kernel source hash: {rec['kernel_source_hash']}"]
+    with open(os.path.join(dest, "fwd_bf16_c3_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

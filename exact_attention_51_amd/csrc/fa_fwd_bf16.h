@@ -1,17 +1,15 @@
 // fa_fwd_bf16.h -- exact-attention forward kernel template, bf16 in/out, gfx950.
 // Instantiated in fa_fwd_bf16.hip (D = 64, 128) and fa_fwd_bf16_d256.hip.
 //
-// One workgroup = 8 waves (two per SIMD; 4 at D = 256); each wave owns
-// 32*QB query rows of one (batch, head) and the whole loop over keys for
-// them.  The streaming
-// structure is the one every page describes ("Learning Metal with
-// FlashAttention", section FlashAttention; "Flash Attention" page, kernel
-// anatomy; metal-flash-attention README, "Quantifying performance", forward
-// pseudocode): the Q rows are loaded once and stay resident (in registers,
-// or in LDS when two waves share a SIMD at D >= 128), K and V
-// stream through LDS in tiles of 64 keys, the running row max m and row sum
-// l rescale the unnormalised accumulator, and the score matrix only ever
-// exists as MFMA accumulator registers.
+// One workgroup = 8 waves at D <= 128 (two per SIMD), 4 waves at D = 256;
+// each wave owns 32*QB query rows of one (batch, head) and the whole loop
+// over keys for them.  The streaming structure is the one every page
+// describes ("Learning Metal with FlashAttention", section FlashAttention;
+// "Flash Attention" page, kernel anatomy; metal-flash-attention README,
+// "Quantifying performance", forward pseudocode): the Q rows are loaded once
+// and stay in registers, K and V stream through LDS in tiles of 64 keys, the
+// running row max m and row sum l rescale the unnormalised accumulator, and
+// the score matrix only ever exists as MFMA accumulator registers.
 //
 // MI355X-specific choices:
 // * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA.
@@ -22,24 +20,26 @@
 //   O^T += V^T P^T; keys are a summation index, so the V operand is read
 //   from LDS in the matching key order with ds_read_b64_tr_b16, which also
 //   does the transpose V needs.  P never touches LDS.
-// * Software pipeline inside each wave: while the MFMA pipe computes the
-//   scores of tile j+1, the VALU exponentiates, packs and sums tile j; while
-//   it accumulates P_j V_j, the VALU takes the row max of tile j+1.  The
-//   rescale decision for a tile sits between the two.
+// * Software pipeline inside each wave, written in issue order: phase A
+//   issues the score MFMAs of tile j+1, each carrying a share of the
+//   exponentials of tile j; phase B issues the P V MFMAs of tile j, each
+//   carrying a share of the row max of tile j+1.  The rescale decision for
+//   a tile sits before phase A.
 // * K/V tiles go global -> LDS with 16-byte direct loads (no VGPR staging)
-//   into a ring of NB buffers per tensor, issued NB-1 tiles ahead.  The
-//   loop is unrolled over the ring so every LDS address is a per-lane
-//   offset computed once plus an instruction immediate.  Rows are
-//   XOR-swizzled in 16-byte chunks (see swz) so that both LDS read patterns
-//   are free of bank conflicts.
+//   into a ring of NB slots per tensor, issued 3-4 steps ahead.  The loop is
+//   unrolled over the ring so every LDS address is a per-lane offset
+//   computed once plus an instruction immediate.  Rows are XOR-swizzled in
+//   16-byte chunks (see swz) so that both LDS read patterns are free of bank
+//   conflicts.
 // * exp is exp2 with scale*log2(e) folded into one FMA per score.  The
 //   rescale of O is skipped while the running max has grown by less than
 //   2^8 in the exp2 domain (the stale max is still an exact reference
 //   point: P and l are just both scaled by the same bounded factor).
-// * Causal masking skips every key tile above a wave's diagonal; only the
-//   diagonal tile is masked element by element.  The tiles that need a mask
-//   (a block's diagonal region, or a ragged last tile) are processed first
-//   by a plain serial step, so the pipelined main loop carries no mask code.
+// * Causal masking skips every key tile above the workgroup's last row.
+//   The tiles that need a mask (the block's diagonal region, or a ragged
+//   last tile) come first in the processing order and run through the same
+//   pipelined step, with the mask applied to their scores between the two
+//   phases.
 #pragma once
 
 #include <type_traits>
@@ -67,7 +67,10 @@ struct FwdCfg {
   // K/V ring: kNB slots each; K of position p is issued kLeadK steps
   // before the step that first reads it, V kLeadV steps before.  Step p
   // reads K(p+1) and V(p) and refills the slots of K(p) and V(p-1).
-  static constexpr int kNB = D <= 128 ? 4 : 2;
+#ifndef FA_FWD_NB
+#define FA_FWD_NB 4
+#endif
+  static constexpr int kNB = D <= 128 ? FA_FWD_NB : 2;
   static constexpr int kLeadK = kNB;
   static constexpr int kLeadV = kNB - 1;
   static constexpr int kLdsBytes = 2 * kNB * kTileBytes;
@@ -79,7 +82,10 @@ struct FwdCfg {
   static_assert(kNB % 2 == 0, "the loop is unrolled over the ring and the two score sets");
   static constexpr int kUnroll = kNB;
   // 8-wave workgroups put two waves on each SIMD (registers must stay <= 256)
-  static constexpr int kWavesPerEU = W / 4;
+#ifndef FA_FWD_WPE
+#define FA_FWD_WPE (W / 4)
+#endif
+  static constexpr int kWavesPerEU = FA_FWD_WPE;
 };
 
 template <int D, bool CAUSAL, int QB, int W>

@@ -60,7 +60,15 @@ template <int D, int QB, int W>
 struct FwdCfg {
   static constexpr int kWaves = W;                       // waves per workgroup (4 or 8)
   static constexpr int kRowsPerWave = 32 * QB;
-  static constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
+  // Key split: with kSplit = 2 the two 32-key halves of every tile go to two
+  // waves that own the same query rows; their partial results are merged
+  // at the end.  D = 256 uses it: its work is B*H*N/32 waves of 32 rows,
+  // which without the split fills only half of the SIMDs at the sizes of
+  // interest (and it halves the score registers of a wave).
+  static constexpr int kSplit = D == 256 ? 2 : 1;
+  static constexpr int kKB = 2 / kSplit;                 // 32-key blocks a wave takes per tile
+  static constexpr int kQBlocks = kWaves / kSplit;       // waves with distinct query rows
+  static constexpr int kBlockM = kQBlocks * kRowsPerWave;  // query rows per workgroup
   static constexpr int kDSteps = D / 16;                 // k-steps of the S product
   static constexpr int kDBlocks = D / 32;                // 32-wide d blocks of O
   static constexpr int kTileBytes = kBlockN * D * 2;     // one K or V tile
@@ -74,6 +82,10 @@ struct FwdCfg {
   static constexpr int kLeadK = kNB;
   static constexpr int kLeadV = kNB - 1;
   static constexpr int kLdsBytes = 2 * kNB * kTileBytes;
+  // merge of a key split: per query block, 64 lanes x (O accumulators + m + l) floats
+  static constexpr int kMergeFloats = QB * kDBlocks * 16 + 2 * QB;
+  static_assert(kSplit == 1 || kLdsBytes >= kQBlocks * 64 * 4 * kMergeFloats,
+                "the merge of a key split reuses the ring");
   // direct-to-LDS loads per wave for one K or V tile
   static constexpr int kLoadsPerTile = kTileBytes / 16 / kWaves / 64;
   // Loads a step may leave in flight when it starts (those of the
@@ -92,12 +104,13 @@ template <int D, bool CAUSAL, int QB, int W>
 struct FwdKernel {
   using C = FwdCfg<D, QB, W>;
   static constexpr int NB = C::kNB;
+  static constexpr int KB = C::kKB;
 
   // per-wave state
   bf16x8 qf[QB][C::kDSteps];  // Q^T as B operands: query column l32, d = ds*16 + half*8 + 0..7
   f32x16 o[QB][C::kDBlocks];  // O^T accumulators
-  f32x16 s[2][2][QB];         // two score tiles in ping-pong: [set][kb][qb]
-  bf16x8 pk[QB][2][2];        // P of the tile in flight, as B operands
+  f32x16 s[2][KB][QB];        // two score tiles in ping-pong: [set][kb][qb]
+  bf16x8 pk[QB][KB][2];       // P of the tile in flight, as B operands
   float m[QB], l[QB], mx[QB];
   int koff[C::kDSteps];      // per-lane K operand offsets within a K tile
   int voff[C::kDBlocks][2];  // per-lane V operand offsets, V region base included
@@ -112,11 +125,11 @@ struct FwdKernel {
   __device__ __forceinline__ const lds_char* vslot(int b) const { return smem + b * C::kTileBytes; }
 
   // S^T tile from the K buffer kt: acc[kb][qb]
-  __device__ __forceinline__ void scores(const lds_char* kt, f32x16 (&acc)[2][QB]) {
+  __device__ __forceinline__ void scores(const lds_char* kt, f32x16 (&acc)[KB][QB]) {
 #pragma unroll
     for (int ds = 0; ds < C::kDSteps; ++ds)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[ds] + kb * 32 * D * 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[kb][qb] = mfma32(kf, qf[qb][ds], ds == 0 ? f32x16{} : acc[kb][qb]);
@@ -127,7 +140,7 @@ struct FwdKernel {
   // (in a ragged last tile, loaded shifted to end at row N-1) already
   // covered by the previous tile.  key0 is the tile's first row, kmin the
   // first key the tile contributes.
-  __device__ __forceinline__ void mask(f32x16 (&acc)[2][QB], int key0, int kmin, int wq0, int N) {
+  __device__ __forceinline__ void mask(f32x16 (&acc)[KB][QB], int key0, int kmin, int wq0, int N) {
     // Element (kb, r) of this lane holds key base + off with a compile-time
     // offset off; the visible keys are the offsets in [lo, hi).
     const int base = key0 + half * 4;
@@ -137,7 +150,7 @@ struct FwdKernel {
       int hi = N - base;
       if constexpr (CAUSAL) hi = min(hi, wq0 + qb * 32 + l32 + 1 - base);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
@@ -147,22 +160,24 @@ struct FwdKernel {
   }
 
   // Row max of a score tile (both halves agree afterwards).
-  __device__ __forceinline__ void rowmax(const f32x16 (&acc)[2][QB]) {
+  __device__ __forceinline__ void rowmax(const f32x16 (&acc)[KB][QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float t[8];
+      float t[4 * KB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = max4(acc[i >> 2][qb], (i & 3) * 4);
-      mx[qb] = max_halves(max8(t));
+      for (int i = 0; i < 4 * KB; ++i) t[i] = max4(acc[i >> 2][qb], (i & 3) * 4);
+      mx[qb] = max_halves(maxn(t));
     }
   }
   __device__ __forceinline__ static float max4(const f32x16& a, int r) {
     return __builtin_fmaxf(__builtin_fmaxf(a[r], a[r + 1]), __builtin_fmaxf(a[r + 2], a[r + 3]));
   }
-  __device__ __forceinline__ static float max8(const float (&t)[8]) {
-    const float a = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), __builtin_fmaxf(t[2], t[3]));
-    const float b = __builtin_fmaxf(__builtin_fmaxf(t[4], t[5]), __builtin_fmaxf(t[6], t[7]));
-    return __builtin_fmaxf(a, b);
+  __device__ __forceinline__ static float maxn(const float (&t)[4 * KB]) {
+    float a = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), __builtin_fmaxf(t[2], t[3]));
+#pragma unroll
+    for (int i = 4; i < 4 * KB; i += 4)
+      a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fmaxf(t[i], t[i + 1]), __builtin_fmaxf(t[i + 2], t[i + 3])));
+    return a;
   }
 
   // Raise the running max to include mx; rescale O and l when it grew by
@@ -194,18 +209,18 @@ struct FwdKernel {
   // ahead of the MFMA that consumes them.  sched_barrier fences keep the
   // compiler from regrouping the sequence (it would otherwise cluster reads
   // next to their use and the MFMAs of one product together).
-  static constexpr int kKFrags = 2 * C::kDSteps;   // K fragments per tile, QB MFMAs each
-  static constexpr int kVFrags = 4 * C::kDBlocks;  // V fragments per tile, QB MFMAs each
+  static constexpr int kKFrags = KB * C::kDSteps;      // K fragments per tile, QB MFMAs each
+  static constexpr int kVFrags = 2 * KB * C::kDBlocks;  // V fragments per tile, QB MFMAs each
   static constexpr int kPf = 3;                    // read-ahead in fragments
   static constexpr int nS = kKFrags * QB;          // score MFMAs per step
   static constexpr int nP = kVFrags * QB;          // P V MFMAs per step
-  static constexpr int kPairs = 16 * QB;           // exp pairs per tile and lane
-  static constexpr int kMaxUnits = 9 * QB;         // row-max work units per tile
+  static constexpr int kPairs = 8 * KB * QB;       // exp pairs per tile and lane
+  static constexpr int kMaxUnits = (4 * KB + 1) * QB;  // row-max work units per tile
   static constexpr int kMaxStart = 2;              // first P V MFMA carrying row-max work
 
-  // K fragment i = (ds, kb) = (i / 2, i % 2)
+  // K fragment i = (ds, kb) = (i / KB, i % KB)
   __device__ __forceinline__ bf16x8 kfrag(const lds_char* kt, int i) const {
-    return *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[i >> 1] + (i & 1) * 32 * D * 2);
+    return *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[i / KB] + (i % KB) * 32 * D * 2);
   }
   // V fragment j = (kb, cc, db): (kb, cc) = j / kDBlocks, db = j % kDBlocks
   __device__ __forceinline__ bf16x8 vfrag(const lds_char* vt, int j) const {
@@ -218,14 +233,14 @@ struct FwdKernel {
   }
 
   // S of the next tile (K buffer kt, into sn) + exp of this tile (sc).
-  __device__ __forceinline__ void phase_a(const lds_char* kt, const f32x16 (&sc)[2][QB], f32x16 (&sn)[2][QB],
+  __device__ __forceinline__ void phase_a(const lds_char* kt, const f32x16 (&sc)[KB][QB], f32x16 (&sn)[KB][QB],
                                           float c) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mc[qb] = m[qb] * c;
     bf16x8 kf[kKFrags];
-    bf16x2 pr[QB][2][2][4];
+    bf16x2 pr[QB][KB][2][4];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kt, i);
     __builtin_amdgcn_sched_barrier(0);
@@ -233,13 +248,13 @@ struct FwdKernel {
     for (int i = 0; i < kKFrags; ++i) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int ds = i >> 1, kb = i & 1;
+        const int ds = i / KB, kb = i % KB;
         sn[kb][qb] = mfma32(kf[i], qf[qb][ds], ds == 0 ? f32x16{} : sn[kb][qb]);
         // exp pairs e = (qb, kb, cc, w) carried by this MFMA
         const int mi = i * QB + qb;
 #pragma unroll
         for (int e = mi * kPairs / nS; e < (mi + 1) * kPairs / nS; ++e) {
-          const int eq = e / 16, kb2 = (e / 8) & 1, cc = (e / 4) & 1, w = e & 3;
+          const int eq = e / (8 * KB), kb2 = (e / 8) % KB, cc = (e / 4) & 1, w = e & 3;
           const float e0 = fast_exp2(__builtin_fmaf(sc[kb2][eq][cc * 8 + 2 * w], c, -mc[eq]));
           const float e1 = fast_exp2(__builtin_fmaf(sc[kb2][eq][cc * 8 + 2 * w + 1], c, -mc[eq]));
           pr[eq][kb2][cc][w] = pack_bf16(e0, e1);
@@ -254,9 +269,9 @@ struct FwdKernel {
   }
 
   // P V of the tile whose P is in pk (V buffer vt) + row max of sn into mx.
-  __device__ __forceinline__ void phase_b(const lds_char* vt, const f32x16 (&sn)[2][QB]) {
+  __device__ __forceinline__ void phase_b(const lds_char* vt, const f32x16 (&sn)[KB][QB]) {
     bf16x8 vf[kVFrags];
-    float t[QB][8];
+    float t[QB][4 * KB];
 #pragma unroll
     for (int j = 0; j < kPf; ++j) vf[j] = vfrag(vt, j);
     __builtin_amdgcn_sched_barrier(0);
@@ -272,11 +287,11 @@ struct FwdKernel {
           const int p = mi - kMaxStart;
 #pragma unroll
           for (int u = p * kMaxUnits / nPos; u < (p + 1) * kMaxUnits / nPos; ++u) {
-            if (u < 8 * QB) {
-              t[u / 8][u % 8] = max4(sn[(u % 8) >> 2][u / 8], (u % 4) * 4);
+            if (u < 4 * KB * QB) {
+              t[u / (4 * KB)][u % (4 * KB)] = max4(sn[(u % (4 * KB)) >> 2][u / (4 * KB)], (u % 4) * 4);
             } else {
-              const int q2 = u - 8 * QB;
-              mx[q2] = max_halves(max8(t[q2]));
+              const int q2 = u - 4 * KB * QB;
+              mx[q2] = max_halves(maxn(t[q2]));
             }
           }
         }
@@ -312,6 +327,8 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   k.l32 = k.lane & 31;
   k.half = k.lane >> 5;
   const int wave = k.wave, lane = k.lane;
+  // query block and key half of this wave (kpart = 0 without a key split)
+  const int qblk = wave % C::kQBlocks, kpart = wave / C::kQBlocks;
 
   int qtile, bh;
   sched_item(sched, blockIdx.x, qtile, bh);
@@ -322,7 +339,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   const __bf16* __restrict__ V = (const __bf16*)a.v + head_off;
 
   const int q0 = qtile * C::kBlockM;
-  const int wq0 = q0 + wave * C::kRowsPerWave;
+  const int wq0 = q0 + qblk * C::kRowsPerWave;
   const bool wave_active = wq0 < N;
   const int n_ktiles_all = (N + kBlockN - 1) / kBlockN;
   int nt = n_ktiles_all;
@@ -346,9 +363,9 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   // First row of key tile t: tiles lie inside the tensor, a ragged last
   // tile is shifted back to end at row N-1 (its keys below t*64 are masked).
   auto tile_row0 = [&](int t) { return SMALL ? 0 : min(min(t, n_ktiles_all - 1) * kBlockN, N - kBlockN); };
-  auto mask_tile = [&](f32x16 (&acc)[2][QB], int p) {
+  auto mask_tile = [&](f32x16 (&acc)[C::kKB][QB], int p) {
     const int t = seq_tile(p);
-    k.mask(acc, tile_row0(t), t * kBlockN, wq0, N);
+    k.mask(acc, tile_row0(t) + kpart * 32, t * kBlockN, wq0, N);
   };
 
   // K and V of sequence position p go to ring slot p % NB.
@@ -374,13 +391,13 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
 
   // per-lane loop-invariant LDS offsets (row offsets of kb/cc blocks keep the swizzle)
 #pragma unroll
-  for (int ds = 0; ds < C::kDSteps; ++ds) k.koff[ds] = lds_off_bytes<D>(k.l32, ds * 2 + k.half);
+  for (int ds = 0; ds < C::kDSteps; ++ds) k.koff[ds] = lds_off_bytes<D>(kpart * 32 + k.l32, ds * 2 + k.half);
   {
     const int g = lane >> 4, j16 = lane & 15;
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db) {
       const int dcol = db * 32 + (g & 1) * 16 + (j16 & 3) * 4;
-      const int r1 = k.half * 4 + (j16 >> 2);
+      const int r1 = kpart * 32 + k.half * 4 + (j16 >> 2);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         k.voff[db][t] = NB * C::kTileBytes + lds_off_bytes<D>(r1 + 8 * t, dcol >> 3) + (dcol & 7) * 2;
@@ -430,6 +447,44 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   for (int i = 0; i < nt; i += C::kUnroll)
     unrolled(i, nt, step, std::make_integer_sequence<int, C::kUnroll>());
   wait_vmcnt<0>();  // no direct-to-LDS copy may outlive the workgroup
+
+  if constexpr (C::kSplit == 2) {
+    // Merge the two key halves.  The second-half waves hand their running
+    // max, row sums and O accumulators to the first-half wave of the same
+    // query rows through LDS (lane-major, conflict-free); each pair of
+    // partial results is rescaled to the larger max and added.
+    constexpr int F = C::kMergeFloats;
+    float __attribute__((address_space(3)))* xo =
+        (float __attribute__((address_space(3)))*)k.smem + qblk * 64 * F + lane;
+    __syncthreads();  // every wave is done with the ring
+    if (kpart == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xo[((qb * C::kDBlocks + db) * 16 + r) * 64] = k.o[qb][db][r];
+        xo[(QB * C::kDBlocks * 16 + qb) * 64] = k.m[qb];
+        xo[(QB * C::kDBlocks * 16 + QB + qb) * 64] = k.l[qb];
+      }
+    }
+    __syncthreads();
+    if (kpart == 1) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m2 = xo[(QB * C::kDBlocks * 16 + qb) * 64];
+      const float l2 = xo[(QB * C::kDBlocks * 16 + QB + qb) * 64];
+      const float mn = __builtin_fmaxf(k.m[qb], m2);
+      const float a1 = fast_exp2((k.m[qb] - mn) * c), a2 = fast_exp2((m2 - mn) * c);
+      k.l[qb] = k.l[qb] * a1 + l2 * a2;
+      k.m[qb] = mn;
+#pragma unroll
+      for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          k.o[qb][db][r] = k.o[qb][db][r] * a1 + xo[((qb * C::kDBlocks + db) * 16 + r) * 64] * a2;
+    }
+  }
 
   // ---- epilogue: O = acc / l, L = m*scale + ln l
   if (!wave_active) return;

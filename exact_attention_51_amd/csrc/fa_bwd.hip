@@ -29,9 +29,19 @@ namespace fa {
 
 namespace {
 
-constexpr int kWavesQ = 4;    // dQ kernel: 4 waves x 32 query rows
-constexpr int kRowsQ = 32 * kWavesQ;
+constexpr int kWavesQ = 4;    // dQ kernel: 4 waves per workgroup
 constexpr int kKeyTile = 64;  // dQ kernel: keys per streamed K/V tile
+
+// dQ kernel key split: at D = 256 the two 32-key halves of every K/V tile
+// go to two waves that own the same 32 query rows (their dQ partial sums
+// are added at the end), so a workgroup covers 64 rows and the B*H*N/32
+// query blocks of a workload fill twice as many SIMDs.
+template <int D>
+struct DqCfg {
+  static constexpr int kSplit = D == 256 ? 2 : 1;
+  static constexpr int kKB = 2 / kSplit;               // 32-key blocks a wave takes per tile
+  static constexpr int kRows = 32 * kWavesQ / kSplit;  // query rows per workgroup
+};
 
 // ============================================================== dQ kernel
 //
@@ -43,6 +53,7 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
     BwdArgs a, TileSched sched) {
   constexpr int kDSteps = D / 16, kDBlocks = D / 32;
+  constexpr int KB = DqCfg<D>::kKB, kRowsQ = DqCfg<D>::kRows, kQBlocks = kWavesQ / DqCfg<D>::kSplit;
   constexpr int kTileBytes = kKeyTile * D * 2;
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * kTileBytes];
   lds_char* smem = (lds_char*)smem_raw;
@@ -61,8 +72,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const __bf16* __restrict__ O = (const __bf16*)a.o + head_off;
   const __bf16* __restrict__ dO = (const __bf16*)a.dO + head_off;
 
+  // query block and key half of this wave (kpart = 0 without a key split)
+  const int qblk = wave % kQBlocks, kpart = wave / kQBlocks;
   const int q0 = qtile * kRowsQ;
-  const int wq0 = q0 + wave * 32;
+  const int wq0 = q0 + qblk * 32;
   const bool wave_active = wq0 < N;
   const int n_ktiles_all = (N + kKeyTile - 1) / kKeyTile;
   int nt = n_ktiles_all, wave_last = n_ktiles_all - 1;
@@ -90,7 +103,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   }
   const float delta = sum_halves(dpart);
   const float lse2 = a.lse[(size_t)bh * N + crow] * kLog2e;  // L in the exp2 domain
-  if (wave_active && half == 0 && row < N) a.delta[(size_t)bh * N + row] = delta;
+  if (wave_active && kpart == 0 && half == 0 && row < N) a.delta[(size_t)bh * N + row] = delta;
   const float c = a.scale_log2;
 
   f32x16 dq[kDBlocks];
@@ -110,24 +123,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const lds_char* kt = kbuf[j & 1];
     const lds_char* vt = vbuf[j & 1];
 
-    // S^T = K_j Q^T and dP^T = V_j dO^T, keys kb*32.. (rows), this wave's queries (columns)
-    f32x16 s[2], dp[2];
+    // S^T = K_j Q^T and dP^T = V_j dO^T, keys kr0 + kb*32.. (rows), this wave's queries (columns)
+    const int kr0 = kpart * 32;
+    f32x16 s[KB], dp[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < kDSteps; ++ds)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32(read_row_operand<D>(kt, kb * 32 + l32, ds, half), qf[ds], s[kb]);
-        dp[kb] = mfma32(read_row_operand<D>(vt, kb * 32 + l32, ds, half), dof[ds], dp[kb]);
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = mfma32(read_row_operand<D>(kt, kr0 + kb * 32 + l32, ds, half), qf[ds], s[kb]);
+        dp[kb] = mfma32(read_row_operand<D>(vt, kr0 + kb * 32 + l32, ds, half), dof[ds], dp[kb]);
       }
 
     const bool masked = (CAUSAL && j == wave_last) || (j == n_ktiles_all - 1 && (N % kKeyTile) != 0);
-    bf16x8 dsk[2][2];  // dS^T packed: [key block][16-key chunk]
+    bf16x8 dsk[KB][2];  // dS^T packed: [key block][16-key chunk]
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         bf16x2 pr[4];
@@ -139,7 +153,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
             const int r = cc * 8 + 2 * i + t;
             float x = __builtin_fmaf(s[kb][r], c, -lse2);
             if (masked) {
-              const int key = j * kKeyTile + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+              const int key = j * kKeyTile + kr0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
               bool keep = key < N;
               if constexpr (CAUSAL) keep = keep && key <= row;
               x = keep ? x : -__builtin_inff();
@@ -156,9 +170,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) dq[db] = mfma32(read_tr_operand<D>(kt, kb * 32 + cc * 16, db * 32, lane), dsk[kb][cc], dq[db]);
+        for (int cc = 0; cc < 2; ++cc)
+          dq[db] = mfma32(read_tr_operand<D>(kt, kr0 + kb * 32 + cc * 16, db * 32, lane), dsk[kb][cc], dq[db]);
+  }
+
+  if constexpr (DqCfg<D>::kSplit == 2) {
+    // add the second key half's dQ partial sums (lane-major through LDS)
+    float __attribute__((address_space(3)))* x =
+        (float __attribute__((address_space(3)))*)smem + qblk * 64 * kDBlocks * 16 + lane;
+    static_assert(kQBlocks * 64 * kDBlocks * 16 * 4 <= 4 * kTileBytes, "merge buffer exceeds the ring");
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the K/V tiles
+    if (kpart == 1) {
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(db * 16 + r) * 64] = dq[db][r];
+    }
+    __syncthreads();
+    if (kpart == 1) return;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[db][r] += x[(db * 16 + r) * 64];
   }
 
   if (!wave_active || row >= N) return;
@@ -353,6 +389,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 
 
 template <int D, bool CAUSAL>
 int launch_dq(const BwdArgs& a, hipStream_t stream) {
+  constexpr int kRowsQ = DqCfg<D>::kRows;
   const int n_tiles = (a.N + kRowsQ - 1) / kRowsQ;
   const TileSched sched = make_sched(n_tiles, a.B * a.H, CAUSAL);
   const long grid = (long)n_tiles * a.B * a.H;

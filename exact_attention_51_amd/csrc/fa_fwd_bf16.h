@@ -93,11 +93,10 @@ struct FwdCfg {
   static constexpr int kStepsInFlight = kNB - 2;
   static_assert(kNB % 2 == 0, "the loop is unrolled over the ring and the two score sets");
   static constexpr int kUnroll = kNB;
-  // 8-wave workgroups put two waves on each SIMD (registers must stay <= 256)
-#ifndef FA_FWD_WPE
-#define FA_FWD_WPE (W / 4)
-#endif
-  static constexpr int kWavesPerEU = FA_FWD_WPE;
+  // Waves per SIMD the register budget is cut for: two (<= 256 VGPRs) for
+  // 8-wave workgroups and for 4-wave workgroups at D = 64 (two workgroups per
+  // CU, each with a 64 KB ring); one for D = 256 (4 waves, 128 KB ring).
+  static constexpr int kWavesPerEU = (W == 8 || D == 64) ? 2 : 1;
 };
 
 template <int D, bool CAUSAL, int QB, int W>

@@ -3,12 +3,19 @@
 // translation unit, fa_fwd_bf16_d256.hip, built with different flags).
 #include "fa_fwd_bf16.h"
 
-// query blocks of 32 rows per wave, waves per workgroup
+// Query blocks of 32 rows per wave, and waves per workgroup by head
+// dimension.  Every instance puts two waves on each SIMD: at D = 128 as one
+// 8-wave workgroup per CU (the K/V ring takes 128 KB of LDS), at D = 64 as
+// two 4-wave workgroups per CU, which do not share barriers and so drift
+// into complementary phases (the D = 64 step is bound by its VALU work).
 #ifndef FA_FWD_QB
 #define FA_FWD_QB 1
 #endif
-#ifndef FA_FWD_W
-#define FA_FWD_W 8
+#ifndef FA_FWD_W64
+#define FA_FWD_W64 4
+#endif
+#ifndef FA_FWD_W128
+#define FA_FWD_W128 8
 #endif
 
 namespace fa {
@@ -32,9 +39,10 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
 
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  constexpr int QB = FA_FWD_QB, W = FA_FWD_W;
-  if (a.D == 64) return a.causal ? fwd::launch<64, true, QB, W>(a, stream) : fwd::launch<64, false, QB, W>(a, stream);
-  if (a.D == 128) return a.causal ? fwd::launch<128, true, QB, W>(a, stream) : fwd::launch<128, false, QB, W>(a, stream);
+  constexpr int QB = FA_FWD_QB, W64 = FA_FWD_W64, W128 = FA_FWD_W128;
+  if (a.D == 64) return a.causal ? fwd::launch<64, true, QB, W64>(a, stream) : fwd::launch<64, false, QB, W64>(a, stream);
+  if (a.D == 128)
+    return a.causal ? fwd::launch<128, true, QB, W128>(a, stream) : fwd::launch<128, false, QB, W128>(a, stream);
   if (a.D == 256) return launch_fwd_bf16_d256(a, stream);
   return -2;
 }

@@ -217,11 +217,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 // and 16 queries in its registers; P and dS packed to bf16 are then the
 // k-operands of dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read
 // transposed from the query tile.
+// (D = 256 has its own kernel, fa_bwd_dkdv_d256.hip.)
 template <int D>
 struct KvCfg {
-  static constexpr int kWaves = D <= 128 ? 4 : 2;  // D = 256: resident K/V + tiles must fit in LDS
-  static constexpr int kKeys = 32 * kWaves;        // key rows per workgroup
-  static constexpr int kQTile = D <= 128 ? 64 : 32;
+  static_assert(D <= 128, "");
+  static constexpr int kWaves = 4;
+  static constexpr int kKeys = 32 * kWaves;  // key rows per workgroup
+  static constexpr int kQTile = 64;
   static constexpr int kQB = kQTile / 32;
   static constexpr int kKvBytes = kKeys * D * 2;
   static constexpr int kTileBytes = kQTile * D * 2;
@@ -302,9 +304,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
-    // D = 256 keeps two 128-register accumulators live: contract in short
-    // unrolled runs so operand fragments are consumed as soon as they are read.
-#pragma unroll(D <= 128 ? kDSteps : 2)
+#pragma unroll
     for (int ds = 0; ds < kDSteps; ++ds) {
       const bf16x8 kf = read_row_operand<D>(kres, wave * 32 + l32, ds, half);
       const bf16x8 vf = read_row_operand<D>(vres, wave * 32 + l32, ds, half);
@@ -429,7 +429,7 @@ int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
     case 128:
       return a.causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
     case 256:
-      return a.causal ? launch_dkdv<256, true>(a, stream) : launch_dkdv<256, false>(a, stream);
+      return launch_bwd_dkdv_d256(a, stream);
   }
   return -2;
 }

@@ -42,5 +42,6 @@ int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 int launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+int launch_bwd_dkdv_d256(const BwdArgs& a, hipStream_t stream);  // fa_bwd_dkdv_d256.hip
 
 }  // namespace fa

@@ -378,15 +378,22 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     if constexpr (SMALL) cp.copy_clamped(V, N, 0, k.vbuf(b));
     else cp.copy(V, tile_row0(seq_tile(p)), k.vbuf(b));
   };
-  // Prologue loads, oldest first: K0, then K(i+1), V(i) for i = 0, 1, ...
-  // (the order in which the first steps need them).
+  // Prologue loads, oldest first, in the order the first steps need them:
+  // K0, then K(i+1), V(i) for i = 0, 1, ...  Only K0 K1 V0 go before the Q
+  // rows are loaded: the compiler cannot see these copies and waits for
+  // every load in flight before it first uses Q, so the rest is issued
+  // after the first score tile.
   issue_k(0, 0);
+  issue_k(1, 1);
+  issue_v(0, 0);
+  auto issue_rest_of_prologue = [&]() {
 #pragma unroll
-  for (int i = 0; i < LK - 1; ++i) {
-    issue_k(i + 1, i + 1);
-    if (i < LV) issue_v(i, i);
-  }
-  constexpr int kPrologueAfterK0 = LK + LV - 1;  // tiles issued after K0
+    for (int i = 1; i < LK - 1; ++i) {
+      issue_k(i + 1, i + 1);
+      if (i < LV) issue_v(i, i);
+    }
+  };
+  constexpr int kPrologueAfterK0 = 2;  // tiles issued after K0 before the first score tile
 
   // per-lane loop-invariant LDS offsets (row offsets of kb/cc blocks keep the swizzle)
 #pragma unroll
@@ -424,6 +431,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   k.scores(k.kbuf(0), k.s[0]);
   if (R > 0) mask_tile(k.s[0], 0);
   k.rowmax(k.s[0]);
+  issue_rest_of_prologue();
 
   // Step p: exp and P V of position p, S and row max of position p+1, as
   // phase A (score MFMAs + exponentials) then phase B (P V MFMAs + row

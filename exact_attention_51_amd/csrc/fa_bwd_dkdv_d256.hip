@@ -11,10 +11,17 @@
 // fill the LDS can only run one wave per SIMD pair.  Here the head
 // dimension of the outputs is split instead: a key group of 32 keys has
 // two waves; for every query tile one forms S = Q K^T, the other
-// dP = dO V^T, they swap P and dP through LDS, and each accumulates dK and
-// dV for its half of the 256 output columns.  The work per key group is
-// unchanged, a wave holds 128 accumulator registers, and a 4-wave
-// workgroup (two key groups, 64 keys) keeps every SIMD busy.
+// dP = dO V^T, they swap P (bf16, as it enters the products) and dP (fp32)
+// through LDS, and each accumulates dK and dV for its half of the 256
+// output columns.  The work per key group is unchanged and a wave holds 128
+// accumulator registers.  The K (or V) rows of a wave's keys stay in
+// registers as MFMA operands.
+//
+// The loop is skewed by one query tile so that a step has one barrier and
+// two independent halves of MFMA work: step i forms S (or dP) of tile i and
+// publishes P (or dP) to the exchange, then finishes tile i-1 from the
+// exchange the previous step published (dS, dV, dK).  Query tiles live two
+// steps (a 3-slot ring) and the exchange is double-buffered.
 //
 // Layouts are those of the general kernel (fa_bwd.hip): S = Q K^T and
 // dP = dO V^T put a key in every lane column and 16 queries in its
@@ -33,11 +40,13 @@ struct KvDsplitCfg {
   static constexpr int kWaves = 4;   // 2 key groups x 2 output halves
   static constexpr int kKeys = 64;   // key rows per workgroup
   static constexpr int kQTile = 32;  // query rows per streamed tile
-  static constexpr int kKvBytes = kKeys * D * 2;
   static constexpr int kTileBytes = kQTile * D * 2;
-  static constexpr int kStatBytes = 256;        // 64 floats of L or delta (rows past the tile are spare)
-  static constexpr int kXBytes = 16 * 64 * 4;   // one wave's 32x32 fp32 accumulator, lane-major
-  static constexpr int kLdsBytes = 2 * kKvBytes + 4 * kTileBytes + 4 * kStatBytes + 2 * 2 * kXBytes;
+  static constexpr int kStatBytes = 256;       // 64 floats of L or delta (rows past the tile are spare)
+  static constexpr int kXpBytes = 2 * 64 * 16;  // P: two bf16x8 operands per lane
+  static constexpr int kXdBytes = 16 * 64 * 4;  // dP: a 32x32 fp32 accumulator, lane-major
+  static constexpr int kSlotBytes = 2 * kTileBytes + 2 * kStatBytes;  // Q, dO, L, delta of one tile
+  static constexpr int kXBytes = 2 * (kXpBytes + kXdBytes);            // both key groups
+  static constexpr int kLdsBytes = 3 * kSlotBytes + 2 * kXBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 };
 
@@ -48,14 +57,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   constexpr int D = C::D, kDSteps = D / 16, kHalfBlocks = D / 64, W = C::kWaves;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLdsBytes];
   lds_char* smem = (lds_char*)smem_raw;
-  lds_char* kres = smem;
-  lds_char* vres = smem + C::kKvBytes;
-  lds_char* qbuf[2] = {smem + 2 * C::kKvBytes, smem + 2 * C::kKvBytes + C::kTileBytes};
-  lds_char* obuf[2] = {smem + 2 * C::kKvBytes + 2 * C::kTileBytes, smem + 2 * C::kKvBytes + 3 * C::kTileBytes};
-  lds_char* stat0 = smem + 2 * C::kKvBytes + 4 * C::kTileBytes;
-  lds_char* lbuf[2] = {stat0, stat0 + C::kStatBytes};
-  lds_char* dbuf[2] = {stat0 + 2 * C::kStatBytes, stat0 + 3 * C::kStatBytes};
-  lds_char* xbase = stat0 + 4 * C::kStatBytes;  // [key group][P, dP] exchange
+  // query-tile ring: tile t in slot t % 3 (Q, dO, L, delta)
+  auto qbuf = [&](int sl) { return smem + sl * C::kSlotBytes; };
+  auto obuf = [&](int sl) { return qbuf(sl) + C::kTileBytes; };
+  auto lbuf = [&](int sl) { return qbuf(sl) + 2 * C::kTileBytes; };
+  auto dbuf = [&](int sl) { return qbuf(sl) + 2 * C::kTileBytes + C::kStatBytes; };
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
             half = lane >> 5;
@@ -77,22 +83,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const bool group_active = wk0 < N;
   const int n_qtiles = (N + C::kQTile - 1) / C::kQTile;
   const int t_begin = CAUSAL ? k0 / C::kQTile : 0;  // earlier query tiles see none of these keys
-  float __attribute__((address_space(3)))* xp = (float __attribute__((address_space(3)))*)(xbase + kgrp * 2 * C::kXBytes) + lane;
-  float __attribute__((address_space(3)))* xdp = xp + C::kXBytes / 4;
+  // exchange of tile t in buffer t % 2: [key group][P (bf16x8 [cc][lane]), dP (fp32 [r][lane])]
+  auto xp = [&](int xb) {
+    return (bf16x8 __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
+                                                         kgrp * (C::kXpBytes + C::kXdBytes)) + lane;
+  };
+  auto xdp = [&](int xb) {
+    return (float __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
+                                                      kgrp * (C::kXpBytes + C::kXdBytes) + C::kXpBytes) + lane;
+  };
 
-  auto load_qtile = [&](int t, int b) {
-    copy_rows_lds<D, C::kQTile, W>(Q, N, t * C::kQTile, qbuf[b], wave, lane);
-    copy_rows_lds<D, C::kQTile, W>(dO, N, t * C::kQTile, obuf[b], wave, lane);
+  auto load_qtile = [&](int t) {
+    const int sl = t % 3;
+    copy_rows_lds<D, C::kQTile, W>(Q, N, t * C::kQTile, qbuf(sl), wave, lane);
+    copy_rows_lds<D, C::kQTile, W>(dO, N, t * C::kQTile, obuf(sl), wave, lane);
     if (wave == 0) {
       int r = t * C::kQTile + lane;
       r = r < N ? r : N - 1;
-      load_lds4(Lg + r, lbuf[b]);
-      load_lds4(Dg + r, dbuf[b]);
+      load_lds4(Lg + r, lbuf(sl));
+      load_lds4(Dg + r, dbuf(sl));
     }
   };
-  copy_rows_lds<D, C::kKeys, W>(K, N, k0, kres, wave, lane);
-  copy_rows_lds<D, C::kKeys, W>(V, N, k0, vres, wave, lane);
-  load_qtile(t_begin, 0);
+  load_qtile(t_begin);
 
   // this wave's half of dK^T and dV^T: d blocks dh*4 .. dh*4+3
   f32x16 dk[kHalfBlocks], dv[kHalfBlocks];
@@ -101,34 +113,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
   const float c = a.scale_log2;
-  // the S-forming wave reads K, the dP-forming wave V, and their query-side tile
-  const lds_char* kv = dh == 0 ? kres : vres;
+  // K (S-forming wave) or V (dP-forming wave) of this wave's keys as B
+  // operands: key column l32, d = ds*16 + half*8 + 0..7
+  bf16x8 kvf[kDSteps];
+  {
+    const __bf16* __restrict__ src = dh == 0 ? K : V;
+    const int crow = key < N ? key : N - 1;
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds) kvf[ds] = *(const bf16x8*)(src + (size_t)crow * D + ds * 16 + half * 8);
+  }
 
-  for (int t = t_begin; t < n_qtiles; ++t) {
-    const int b = (t - t_begin) & 1;
+  // does key group kgrp see any query of tile t?
+  auto tile_work = [&](int t) { return group_active && !(CAUSAL && t * C::kQTile + C::kQTile - 1 < wk0); };
+
+  for (int t = t_begin; t <= n_qtiles; ++t) {
+    // publishes tile t (loaded last step) and the exchange of tile t-1
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < n_qtiles) load_qtile(t + 1, b ^ 1);
-    const int tq0 = t * C::kQTile;
-    // every wave passes both barriers of the step; only the work is skipped
-    const bool work = group_active && !(CAUSAL && tq0 + C::kQTile - 1 < wk0);
-    const lds_char* qt = qbuf[b];
-    const lds_char* ot = obuf[b];
+    if (t + 1 < n_qtiles) load_qtile(t + 1);  // into the slot of tile t-2, finished last step
 
-    // 1. S = Q_t K^T (dh = 0) or dP = dO_t V^T (dh = 1), published to the partner
-    f32x16 mine;
-    if (work) {
-      const lds_char* at = dh == 0 ? qt : ot;
+    // 1. tile t: S = Q_t K^T (dh = 0) or dP = dO_t V^T (dh = 1), to the exchange
+    if (t < n_qtiles && tile_work(t)) {
+      const int sl = t % 3, xb = t & 1, tq0 = t * C::kQTile;
+      const lds_char* at = dh == 0 ? qbuf(sl) : obuf(sl);
+      f32x16 mine;
 #pragma unroll
       for (int ds = 0; ds < kDSteps; ++ds)
-        mine = mfma32(read_row_operand<D>(at, l32, ds, half), read_row_operand<D>(kv, kgrp * 32 + l32, ds, half),
-                      ds == 0 ? f32x16{} : mine);
+        mine = mfma32(read_row_operand<D>(at, l32, ds, half), kvf[ds], ds == 0 ? f32x16{} : mine);
       if (dh == 0) {  // P = exp(S - L), masked; queries of register r: (r/4)*8 + half*4 + r%4
         const bool masked = (CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-          const float lq = *(const float __attribute__((address_space(3)))*)(lbuf[b] + 4 * qr);
+          const float lq = *(const float __attribute__((address_space(3)))*)(lbuf(sl) + 4 * qr);
           float x = __builtin_fmaf(mine[r], c, -lq * kLog2e);
           if (masked) {
             bool keep = tq0 + qr < N;
@@ -137,45 +154,52 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
           }
           mine[r] = fast_exp2(x);
         }
-      }
+        // P rounded to bf16 once; both waves form dS from this rounded P
 #pragma unroll
-      for (int r = 0; r < 16; ++r) (dh == 0 ? xp : xdp)[r * 64] = mine[r];
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x2 pp[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pp[i] = pack_bf16(mine[cc * 8 + 2 * i], mine[cc * 8 + 2 * i + 1]);
+          xp(xb)[cc * 64] = join8(pp[0], pp[1], pp[2], pp[3]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xdp(xb)[r * 64] = mine[r];
+      }
     }
-    __syncthreads();
 
-    // 2. both waves: P and dS = P (dP - delta) as bf16 operands, then their half of dV and dK
-    if (work) {
+    // 2. tile t-1, both waves: P (bf16) and dS = P (dP - delta) as bf16
+    // operands from the exchange, then their half of dV and dK
+    if (t > t_begin && tile_work(t - 1)) {
+      const int sl = (t - 1) % 3, xb = (t - 1) & 1;
       bf16x8 ppk[2], dspk[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        bf16x2 pp[4], dd[4];
+        ppk[cc] = xp(xb)[cc * 64];
+        const bf16x2* pp = (const bf16x2*)&ppk[cc];
+        bf16x2 dd[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float pv[2], dsv[2];
+          float dsv[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = cc * 8 + 2 * i + u;
             const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-            const float p = dh == 0 ? mine[r] : xp[r * 64];
-            const float dp = dh == 1 ? mine[r] : xdp[r * 64];
-            const float dq = *(const float __attribute__((address_space(3)))*)(dbuf[b] + 4 * qr);
-            pv[u] = p;
-            dsv[u] = p * (dp - dq);
+            const float dq = *(const float __attribute__((address_space(3)))*)(dbuf(sl) + 4 * qr);
+            dsv[u] = (float)pp[i][u] * (xdp(xb)[r * 64] - dq);
           }
-          pp[i] = pack_bf16(pv[0], pv[1]);
           dd[i] = pack_bf16(dsv[0], dsv[1]);
         }
-        ppk[cc] = join8(pp[0], pp[1], pp[2], pp[3]);
         dspk[cc] = join8(dd[0], dd[1], dd[2], dd[3]);
       }
-      // dV^T += dO_t^T P,  dK^T += Q_t^T dS over d blocks dh*4 ..
+      // dV^T += dO^T P,  dK^T += Q^T dS over d blocks dh*4 ..
 #pragma unroll
       for (int i = 0; i < kHalfBlocks; ++i)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const int d0 = (dh * kHalfBlocks + i) * 32;
-          dv[i] = mfma32(read_tr_operand<D>(ot, cc * 16, d0, lane), ppk[cc], dv[i]);
-          dk[i] = mfma32(read_tr_operand<D>(qt, cc * 16, d0, lane), dspk[cc], dk[i]);
+          dv[i] = mfma32(read_tr_operand<D>(obuf(sl), cc * 16, d0, lane), ppk[cc], dv[i]);
+          dk[i] = mfma32(read_tr_operand<D>(qbuf(sl), cc * 16, d0, lane), dspk[cc], dk[i]);
         }
     }
   }

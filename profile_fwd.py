@@ -2,7 +2,7 @@
 
 Run on a GPU machine from the repository root:
 
-    python3 profile_fwd.py            # kernel trace + FETCH_SIZE / WRITE_SIZE passes
+    python3 profile_fwd.py            # kernel trace, FETCH_SIZE / WRITE_SIZE, SQ counter passes
 
 Writes its summaries under gpurun_out/profile_fwd/profiles/ (the GPU machine
 keeps only gpurun_out/); `python3 profile_fwd.py --summarize` rebuilds them
@@ -12,6 +12,8 @@ from the returned CSVs, under profiles/:
   fwd_bf16_c3_traffic.json     the same figure, keyed by a hash of the kernel
                                sources (bench.py reports it only while the
                                hash still matches)
+  fwd_bf16_c3_counters.md      shader clock, MFMA busy, VALU/LDS activity, LDS
+                               bank conflicts and the instruction mix
 
 The TCC FETCH_SIZE / WRITE_SIZE counters are calibrated against a plain
 device copy of known size: the factor (bytes moved / counter bytes) for each
@@ -39,6 +41,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 FWD_KERNEL = "fwd_bf16_kernel"
 COPY_BYTES = 1 << 30
 BENCH = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "30", "--warmup", "5", "--no-cpu", "--no-others"]
+# SQ counter passes (at most 8 SQ and 2 GRBM counters each)
+SQ_PASSES = {
+    "sq1": ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+            "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE"],
+    "sq2": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+            "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU", "SQ_WAVES", "GRBM_GUI_ACTIVE"],
+}
+FLOP_C3 = 4 * 8192 * 8192 * 128 * 2 * 16 // 2
 
 
 def copy_workload(nbytes: int) -> None:
@@ -105,6 +115,9 @@ def main() -> int:
                  os.path.join(OUT, f"fwd_{ctr}"), "-o", "run", "--", *BENCH], 300)
             run(["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", os.path.join(OUT, f"copy_{ctr}"), "-o",
                  "run", "--", *me, "--copy", str(COPY_BYTES)], 300)
+        for name, ctrs in SQ_PASSES.items():  # 3. SQ counters of the forward kernel
+            run(["rocprofv3", "--pmc", *ctrs, "--kernel-include-regex", FWD_KERNEL, "--output-format", "csv", "-d",
+                 os.path.join(OUT, name), "-o", "run", "--", *BENCH], 300)
     summarize(OUT, PROFILES if args.summarize else os.path.join(OUT, "profiles"))
     return 0
 
@@ -166,6 +179,74 @@ def summarize(out: str, dest: str) -> None:
              f"- ratio measured / algorithmic: {total / algo:.2f}",
              f"- kernel source hash: {rec['kernel_source_hash']}"]
     with open(os.path.join(dest, "fwd_bf16_c3_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if all(os.path.isdir(os.path.join(out, n)) for n in SQ_PASSES):
+        summarize_counters(out, dest)
+    print("\n".join(lines), flush=True)
+
+
+def per_dispatch_counters(outdir: str) -> tuple[dict, dict]:
+    """Counter totals and (start, end) timestamps per dispatch of the forward kernel."""
+    vals: dict[int, dict] = {}
+    span: dict[int, tuple] = {}
+    for r in counter_rows(outdir):
+        if FWD_KERNEL not in r["Kernel_Name"]:
+            continue
+        d = int(r["Dispatch_Id"])
+        v = vals.setdefault(d, {})
+        v[r["Counter_Name"]] = v.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            span[d] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    return vals, span
+
+
+def summarize_counters(out: str, dest: str) -> None:
+    """Medians over the dispatches of each SQ pass (the first one skipped).
+
+    GRBM_GUI_ACTIVE comes back summed over the 8 XCDs, so one XCD's busy
+    cycles are a eighth of it; with the dispatch duration that gives the
+    shader clock.  SQ_VALU_MFMA_BUSY_CYCLES is normalised by those cycles
+    times the 1024 SIMDs (the same normalisation matches the MFMA share
+    implied by the achieved TFLOPS at the measured clock, printed beside)."""
+    med = {}
+    clocks = []
+    for name in SQ_PASSES:
+        vals, span = per_dispatch_counters(os.path.join(out, name))
+        ids = sorted(vals)[1:]
+        for k in {k for d in ids for k in vals[d]}:
+            med[(name, k)] = statistics.median(vals[d][k] for d in ids)
+        for d in ids:
+            if d in span and span[d][1] > span[d][0]:
+                clocks.append((vals[d]["GRBM_GUI_ACTIVE"] / 8 / (span[d][1] - span[d][0]), span[d][1] - span[d][0]))
+    gui = med[("sq1", "GRBM_GUI_ACTIVE")] / 8
+    ghz = statistics.median(c for c, _ in clocks) if clocks else float("nan")
+    ns = statistics.median(t for _, t in clocks) if clocks else float("nan")
+    mfma = med[("sq1", "SQ_VALU_MFMA_BUSY_CYCLES")] / (gui * 1024)
+    coexec = med[("sq1", "SQ_VALU_MFMA_COEXEC_CYCLES")] / max(med[("sq1", "SQ_VALU_MFMA_BUSY_CYCLES")], 1)
+    implied = (FLOP_C3 / (ns * 1e-9)) / (1024 * 1024 * ghz * 1e9) if clocks else float("nan")
+    bank = med[("sq2", "SQ_LDS_BANK_CONFLICT")] / max(med[("sq2", "SQ_LDS_IDX_ACTIVE")], 1)
+    lds_active = med[("sq2", "SQ_LDS_IDX_ACTIVE")] / (gui * 256)
+    n_mfma = med[("sq2", "SQ_INSTS_MFMA")]
+    mix = {k: med[("sq2", k)] / n_mfma for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU")}
+    lines = ["# Forward kernel, causal B=2 H=16 N=8192 D=128 bf16: SQ counters", "",
+             "Command (repository root, GPU box): `python3 profile_fwd.py`; two `rocprofv3 --pmc` passes over",
+             "`bench.py --steps 30 --warmup 5 --no-cpu --no-others`, kernel filtered by name, medians over the",
+             "dispatches after the first:", ""]
+    for name, ctrs in SQ_PASSES.items():
+        lines.append(f"- pass {name}: `{' '.join(ctrs)}`")
+    lines += ["",
+              f"- dispatch duration (median): {ns / 1e3:.1f} us; cycles per XCD (GRBM_GUI_ACTIVE / 8): {gui:.0f};"
+              f" shader clock {ghz:.2f} GHz",
+              f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs) = {100 * mfma:.1f}%;"
+              f" MFMA share implied by the TFLOPS at that clock (1024 FLOP/clk/SIMD): {100 * implied:.1f}%",
+              f"- MFMA cycles co-executing VALU work: {100 * coexec:.1f}%",
+              f"- LDS: SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs) = {100 * lds_active:.1f}%;"
+              f" bank-conflict cycles / LDS active cycles = {100 * bank:.2f}%",
+              f"- instructions per MFMA: VALU (MFMA included) {mix['SQ_INSTS_VALU']:.2f}, of them transcendental"
+              f" {mix['SQ_INSTS_VALU_TRANS_F32']:.2f}; LDS {mix['SQ_INSTS_LDS']:.2f}; SALU {mix['SQ_INSTS_SALU']:.2f}",
+              f"- waves per dispatch: {med[('sq2', 'SQ_WAVES')]:.0f}",
+              f"- kernel source hash: {kernel_source_hash()}"]
+    with open(os.path.join(dest, "fwd_bf16_c3_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
 

@@ -44,6 +44,26 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def device_info() -> dict:
+    """CU count and peak shader clock of device 0, and the dense bf16 MFMA
+    peak they imply (4 SIMDs per CU, 1024 bf16 FLOP per SIMD per clock)."""
+    import ctypes
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    info = {"arch": props.gcnArchName, "cus": props.multi_processor_count, "max_sclk_mhz": None, "peak_implied_tflops": None}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) == 0 and khz.value > 0:  # 5: hipDeviceAttributeClockRate
+            info["max_sclk_mhz"] = khz.value / 1000
+            info["peak_implied_tflops"] = round(props.multi_processor_count * 4096 * khz.value * 1e3 / 1e12, 1)
+    except (OSError, AttributeError):  # no HIP runtime library or symbol: report the CU count only
+        pass
+    return info
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -268,6 +288,7 @@ def main() -> int:
             "traffic": traffic_from_profile(),
         },
         "cpu_baseline": cpu,
+        "device": device_info(),
         "others": others,
     }
     print(json.dumps(rec), flush=True)

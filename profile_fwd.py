@@ -47,8 +47,12 @@ SQ_PASSES = {
             "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE"],
     "sq2": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
             "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU", "SQ_WAVES", "GRBM_GUI_ACTIVE"],
+    "tcc": ["TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE"],
 }
+PASSES = ["ktrace", "traffic", *SQ_PASSES]
 FLOP_C3 = 4 * 8192 * 8192 * 128 * 2 * 16 // 2
+# 256-row query block t (of 32 per head) visits key tiles 0 .. 4t+3 of 64 keys
+EXP_C3 = 2 * 16 * sum(256 * 64 * (4 * t + 4) for t in range(8192 // 256))
 
 
 def copy_workload(nbytes: int) -> None:
@@ -101,7 +105,9 @@ def main() -> int:
     ap.add_argument("--copy", type=int, default=0, help="calibration workload: copy this many bytes")
     ap.add_argument("--summarize", action="store_true",
                     help="only rebuild profiles/ from the CSVs already under gpurun_out/profile_fwd")
+    ap.add_argument("--passes", default=",".join(PASSES), help=f"comma-separated subset of {','.join(PASSES)}")
     args = ap.parse_args()
+    passes = args.passes.split(",")
     if args.copy:
         copy_workload(args.copy)
         return 0
@@ -109,15 +115,21 @@ def main() -> int:
     if not args.summarize:
         os.makedirs(OUT, exist_ok=True)
         me = [sys.executable, os.path.abspath(__file__)]
-        run(cmd_kernel_trace(), 600)  # 1. kernel trace with per-kernel statistics
-        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):  # 2. one counter per pass: forward, then copy
+        if "ktrace" in passes:
+            run(cmd_kernel_trace(), 600)  # 1. kernel trace with per-kernel statistics
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE") if "traffic" in passes else ():  # 2. forward, then copy
             run(["rocprofv3", "--pmc", ctr, "--kernel-include-regex", FWD_KERNEL, "--output-format", "csv", "-d",
                  os.path.join(OUT, f"fwd_{ctr}"), "-o", "run", "--", *BENCH], 300)
             run(["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", os.path.join(OUT, f"copy_{ctr}"), "-o",
                  "run", "--", *me, "--copy", str(COPY_BYTES)], 300)
-        for name, ctrs in SQ_PASSES.items():  # 3. SQ counters of the forward kernel
+        for name, ctrs in SQ_PASSES.items():  # 3. SQ / TCC counters of the forward kernel
+            if name not in passes:
+                continue
             run(["rocprofv3", "--pmc", *ctrs, "--kernel-include-regex", FWD_KERNEL, "--output-format", "csv", "-d",
                  os.path.join(OUT, name), "-o", "run", "--", *BENCH], 300)
+    if not args.summarize and set(passes) != set(PASSES):
+        print("partial run: rebuild the summaries with --summarize once every pass has results", flush=True)
+        return 0
     summarize(OUT, PROFILES if args.summarize else os.path.join(OUT, "profiles"))
     return 0
 
@@ -180,7 +192,7 @@ def summarize(out: str, dest: str) -> None:
              f"- kernel source hash: {rec['kernel_source_hash']}"]
     with open(os.path.join(dest, "fwd_bf16_c3_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    if all(os.path.isdir(os.path.join(out, n)) for n in SQ_PASSES):
+    if all(os.path.isdir(os.path.join(out, n)) for n in ("sq1", "sq2")):
         summarize_counters(out, dest)
     print("\n".join(lines), flush=True)
 
@@ -200,6 +212,41 @@ def per_dispatch_counters(outdir: str) -> tuple[dict, dict]:
     return vals, span
 
 
+def tcc_lines(med: dict) -> list[str]:
+    if ("tcc", "TCC_HIT_sum") not in med:
+        return []
+    hit, miss = med[("tcc", "TCC_HIT_sum")], med[("tcc", "TCC_MISS_sum")]
+    return [f"- L2 (TCC) requests: {hit:.4g} hits, {miss:.4g} misses; hit rate {100 * hit / (hit + miss):.1f}%"]
+
+
+def build_metadata_lines() -> list[str]:
+    """Register, scratch and LDS use of the forward kernel instance the bench
+    line times, from the compiler's resource-usage remarks on our own build."""
+    sys.path.insert(0, ROOT)
+    from exact_attention_51_amd import build
+
+    src = os.path.join(ROOT, "exact_attention_51_amd", "csrc", "fa_fwd_bf16.hip")
+    cmd = [build.hipcc(), *build.COMMON_FLAGS, *build.source_flags("fa_fwd_bf16.hip"), "--offload-device-only",
+           "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", os.devnull]
+    try:
+        err = subprocess.run(cmd, capture_output=True, text=True, timeout=600).stderr.splitlines()
+    except (OSError, subprocess.TimeoutExpired):
+        return []
+    want = ("VGPRs:", "AGPRs:", "ScratchSize [bytes/lane]:", "Occupancy [waves/SIMD]:", "LDS Size [bytes/block]:")
+    for i, line in enumerate(err):
+        if "Function Name:" in line and "fwd_bf16_kernelILi128ELb1ELi1ELi8ELb0E" in line:
+            got = []
+            for rest in err[i + 1:i + 16]:
+                if "Function Name:" in rest:
+                    break
+                body = rest.split("remark: ")[-1].split(" [-Rpass")[0].strip()
+                if body.startswith(want):
+                    got.append(body)
+            return ["- compiler resource usage of this instance (D=128, causal, 8 waves; hipcc"
+                    " -Rpass-analysis=kernel-resource-usage): " + "; ".join(got)]
+    return []
+
+
 def summarize_counters(out: str, dest: str) -> None:
     """Medians over the dispatches of each SQ pass (the first one skipped).
 
@@ -211,6 +258,8 @@ def summarize_counters(out: str, dest: str) -> None:
     med = {}
     clocks = []
     for name in SQ_PASSES:
+        if not os.path.isdir(os.path.join(out, name)):
+            continue
         vals, span = per_dispatch_counters(os.path.join(out, name))
         ids = sorted(vals)[1:]
         for k in {k for d in ids for k in vals[d]}:
@@ -227,6 +276,8 @@ def summarize_counters(out: str, dest: str) -> None:
     bank = med[("sq2", "SQ_LDS_BANK_CONFLICT")] / max(med[("sq2", "SQ_LDS_IDX_ACTIVE")], 1)
     lds_active = med[("sq2", "SQ_LDS_IDX_ACTIVE")] / (gui * 256)
     n_mfma = med[("sq2", "SQ_INSTS_MFMA")]
+    valu_busy = 4 * med[("sq1", "SQ_ACTIVE_INST_VALU")] / (gui * 1024)  # quad-cycles, summed over waves
+    n_exp = 64 * med[("sq2", "SQ_INSTS_VALU_TRANS_F32")]
     mix = {k: med[("sq2", k)] / n_mfma for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU")}
     lines = ["# Forward kernel, causal B=2 H=16 N=8192 D=128 bf16: SQ counters", "",
              "Command (repository root, GPU box): `python3 profile_fwd.py`; two `rocprofv3 --pmc` passes over",
@@ -240,11 +291,18 @@ def summarize_counters(out: str, dest: str) -> None:
               f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs) = {100 * mfma:.1f}%;"
               f" MFMA share implied by the TFLOPS at that clock (1024 FLOP/clk/SIMD): {100 * implied:.1f}%",
               f"- MFMA cycles co-executing VALU work: {100 * coexec:.1f}%",
+              f"- VALU issue (SQ_ACTIVE_INST_VALU, quad-cycles summed over waves, x 4 / (cycles x 1024 SIMDs),"
+              f" MFMA issue included): {100 * valu_busy:.1f}%",
+              f"- transcendental lane-operations (SQ_INSTS_VALU_TRANS_F32 x 64): {n_exp / 1e9:.4f} G, against one"
+              f" exp2 per score of every key tile a 256-row query block visits (diagonal tiles included,"
+              f" masked scores too): {EXP_C3 / 1e9:.4f} G",
               f"- LDS: SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs) = {100 * lds_active:.1f}%;"
               f" bank-conflict cycles / LDS active cycles = {100 * bank:.2f}%",
               f"- instructions per MFMA: VALU (MFMA included) {mix['SQ_INSTS_VALU']:.2f}, of them transcendental"
               f" {mix['SQ_INSTS_VALU_TRANS_F32']:.2f}; LDS {mix['SQ_INSTS_LDS']:.2f}; SALU {mix['SQ_INSTS_SALU']:.2f}",
               f"- waves per dispatch: {med[('sq2', 'SQ_WAVES')]:.0f}",
+              *tcc_lines(med),
+              *build_metadata_lines(),
               f"- kernel source hash: {kernel_source_hash()}"]
     with open(os.path.join(dest, "fwd_bf16_c3_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")

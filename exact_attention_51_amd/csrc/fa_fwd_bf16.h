@@ -22,9 +22,7 @@
 //   does the transpose V needs.  P never touches LDS.
 // * Software pipeline inside each wave, written in issue order: phase A
 //   issues the score MFMAs of tile j+1, each carrying a share of the
-//   exponentials of tile j; phase B issues the P V MFMAs of tile j, each
-//   carrying a share of the row max of tile j+1.  The rescale decision for
-//   a tile sits before phase A.
+//   exponentials of tile j; phase B issues the P V MFMAs of tile j.
 // * K/V tiles go global -> LDS with 16-byte direct loads (no VGPR staging)
 //   into a ring of NB slots per tensor, issued 3-4 steps ahead.  The loop is
 //   unrolled over the ring so every LDS address is a per-lane offset
@@ -32,9 +30,14 @@
 //   16-byte chunks (see swz) so that both LDS read patterns are free of bank
 //   conflicts.
 // * exp is exp2 with scale*log2(e) folded into one FMA per score.  The
-//   rescale of O is skipped while the running max has grown by less than
-//   2^8 in the exp2 domain (the stale max is still an exact reference
-//   point: P and l are just both scaled by the same bounded factor).
+//   running max m is only a reference point: any m gives the same O and L
+//   as long as no exp2(s*c - m*c) overflows.  So the tiles after the first
+//   are exponentiated against the current m without computing their row
+//   max; each lane's share of the tile's row sum (its P values of the tile)
+//   is then checked against 2^16, which bounds every P of the tile.  Only
+//   when a lane of the wave exceeds it (or got inf) does the wave take the
+//   row max of the tile, raise m, rescale O and l, and redo the tile's
+//   exponentials, all before the P V products read P.
 // * Causal masking skips every key tile above the workgroup's last row.
 //   The tiles that need a mask (the block's diagonal region, or a ragged
 //   last tile) come first in the processing order and run through the same
@@ -55,6 +58,7 @@ namespace fwd {
 constexpr int kBlockN = 64;                // keys per K/V tile
 constexpr float kRescaleThreshold = 8.0f;  // exp2-domain growth allowed before O is rescaled
 constexpr float kMaxFloor = 1.0e30f;       // the running max starts at -kMaxFloor
+constexpr float kTileSumLimit = 65536.0f;  // bound on a lane's share of a tile's row sum
 
 template <int D, int QB, int W>
 struct FwdCfg {
@@ -110,7 +114,7 @@ struct FwdKernel {
   f32x16 o[QB][C::kDBlocks];  // O^T accumulators
   f32x16 s[2][KB][QB];        // two score tiles in ping-pong: [set][kb][qb]
   bf16x8 pk[QB][KB][2];       // P of the tile in flight, as B operands
-  float m[QB], l[QB], mx[QB];
+  float m[QB], l[QB], mx[QB], lt[QB];  // lt: this lane's share of the current tile's row sums
   int koff[C::kDSteps];      // per-lane K operand offsets within a K tile
   int voff[C::kDBlocks][2];  // per-lane V operand offsets, V region base included
   lds_char* smem;
@@ -180,7 +184,8 @@ struct FwdKernel {
   }
 
   // Raise the running max to include mx; rescale O and l when it grew by
-  // more than the threshold in any lane of the wave (a wave-uniform branch).
+  // more than the threshold in any lane of the wave (a wave-uniform branch;
+  // rows that grew less keep their reference point).
   // The running max starts at a finite floor, not -inf: a row may see only
   // masked keys in its first tiles, and exp2(-inf - floor) is then 0.
   __device__ __forceinline__ void update_max(float c) {
@@ -200,22 +205,61 @@ struct FwdKernel {
     }
   }
 
+  // Exponentials of a whole score tile against the running max: P as bf16
+  // B operands in pk, this lane's share of the row sums (over the rounded
+  // P) in lt.
+  __device__ __forceinline__ void exp_tile(const f32x16 (&sc)[KB][QB], float c) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mc = m[qb] * c;
+      lt[qb] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x2 pr[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pr[w] = pack_bf16(fast_exp2(__builtin_fmaf(sc[kb][qb][cc * 8 + 2 * w], c, -mc)),
+                              fast_exp2(__builtin_fmaf(sc[kb][qb][cc * 8 + 2 * w + 1], c, -mc)));
+            lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr[w], ones, lt[qb], false);
+          }
+          pk[qb][kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
+        }
+    }
+  }
+
+  // After the exponentials of tile sc: if a lane's share of a row sum is
+  // above kTileSumLimit or not finite, raise the running max to the tile's
+  // row max (rescaling O and l) and redo the tile; then add the tile's sums.
+  __device__ __forceinline__ void settle_tile(const f32x16 (&sc)[KB][QB], float c) {
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) over |= !(lt[qb] <= kTileSumLimit);
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      rowmax(sc);
+      update_max(c);
+      exp_tile(sc, c);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
+  }
+
   // ---- the two halves of a pipelined step, written in issue order -----
   // Phase A issues the score MFMAs of the next tile, each carrying its
   // share of this tile's exponentials (P rounded to bf16, row sum over the
-  // rounded P).  Phase B issues the P V MFMAs of this tile, each carrying a
-  // share of the next tile's row max.  LDS fragments are read kPf fragments
-  // ahead of the MFMA that consumes them.  sched_barrier fences keep the
-  // compiler from regrouping the sequence (it would otherwise cluster reads
-  // next to their use and the MFMAs of one product together).
+  // rounded P).  Phase B issues the P V MFMAs of this tile.  LDS fragments
+  // are read kPf fragments ahead of the MFMA that consumes them.
+  // sched_barrier fences keep the compiler from regrouping the sequence (it
+  // would otherwise cluster reads next to their use and the MFMAs of one
+  // product together).
   static constexpr int kKFrags = KB * C::kDSteps;      // K fragments per tile, QB MFMAs each
   static constexpr int kVFrags = 2 * KB * C::kDBlocks;  // V fragments per tile, QB MFMAs each
   static constexpr int kPf = 3;                    // read-ahead in fragments
   static constexpr int nS = kKFrags * QB;          // score MFMAs per step
   static constexpr int nP = kVFrags * QB;          // P V MFMAs per step
   static constexpr int kPairs = 8 * KB * QB;       // exp pairs per tile and lane
-  static constexpr int kMaxUnits = (4 * KB + 1) * QB;  // row-max work units per tile
-  static constexpr int kMaxStart = 2;              // first P V MFMA carrying row-max work
 
   // K fragment i = (ds, kb) = (i / KB, i % KB)
   __device__ __forceinline__ bf16x8 kfrag(const lds_char* kt, int i) const {
@@ -237,7 +281,10 @@ struct FwdKernel {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mc[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mc[qb] = m[qb] * c;
+    for (int qb = 0; qb < QB; ++qb) {
+      mc[qb] = m[qb] * c;
+      lt[qb] = 0.f;
+    }
     bf16x8 kf[kKFrags];
     bf16x2 pr[QB][KB][2][4];
 #pragma unroll
@@ -257,7 +304,7 @@ struct FwdKernel {
           const float e0 = fast_exp2(__builtin_fmaf(sc[kb2][eq][cc * 8 + 2 * w], c, -mc[eq]));
           const float e1 = fast_exp2(__builtin_fmaf(sc[kb2][eq][cc * 8 + 2 * w + 1], c, -mc[eq]));
           pr[eq][kb2][cc][w] = pack_bf16(e0, e1);
-          l[eq] = __builtin_amdgcn_fdot2_f32_bf16(pr[eq][kb2][cc][w], ones, l[eq], false);
+          lt[eq] = __builtin_amdgcn_fdot2_f32_bf16(pr[eq][kb2][cc][w], ones, lt[eq], false);
           if (w == 3)
             pk[eq][kb2][cc] = join8(pr[eq][kb2][cc][0], pr[eq][kb2][cc][1], pr[eq][kb2][cc][2], pr[eq][kb2][cc][3]);
         }
@@ -267,10 +314,9 @@ struct FwdKernel {
     }
   }
 
-  // P V of the tile whose P is in pk (V buffer vt) + row max of sn into mx.
-  __device__ __forceinline__ void phase_b(const lds_char* vt, const f32x16 (&sn)[KB][QB]) {
+  // P V of the tile whose P is in pk (V buffer vt).
+  __device__ __forceinline__ void phase_b(const lds_char* vt) {
     bf16x8 vf[kVFrags];
-    float t[QB][4 * KB];
 #pragma unroll
     for (int j = 0; j < kPf; ++j) vf[j] = vfrag(vt, j);
     __builtin_amdgcn_sched_barrier(0);
@@ -278,23 +324,7 @@ struct FwdKernel {
     for (int j = 0; j < kVFrags; ++j) {
       const int kc = j / C::kDBlocks, db = j % C::kDBlocks;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        o[qb][db] = mfma32(vf[j], pk[qb][kc >> 1][kc & 1], o[qb][db]);
-        const int mi = j * QB + qb;
-        if (mi >= kMaxStart) {
-          constexpr int nPos = nP - kMaxStart;
-          const int p = mi - kMaxStart;
-#pragma unroll
-          for (int u = p * kMaxUnits / nPos; u < (p + 1) * kMaxUnits / nPos; ++u) {
-            if (u < 4 * KB * QB) {
-              t[u / (4 * KB)][u % (4 * KB)] = max4(sn[(u % (4 * KB)) >> 2][u / (4 * KB)], (u % 4) * 4);
-            } else {
-              const int q2 = u - 4 * KB * QB;
-              mx[q2] = max_halves(maxn(t[q2]));
-            }
-          }
-        }
-      }
+      for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[j], pk[qb][kc >> 1][kc & 1], o[qb][db]);
       if (j + kPf < kVFrags) vf[j + kPf] = vfrag(vt, j + kPf);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -431,12 +461,15 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   k.scores(k.kbuf(0), k.s[0]);
   if (R > 0) mask_tile(k.s[0], 0);
   k.rowmax(k.s[0]);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) k.m[qb] = __builtin_fmaxf(k.m[qb], k.mx[qb]);  // O and l are still zero
   issue_rest_of_prologue();
 
-  // Step p: exp and P V of position p, S and row max of position p+1, as
-  // phase A (score MFMAs + exponentials) then phase B (P V MFMAs + row
-  // max).  The step's barrier publishes K(p+1) and V(p) and frees the slots
-  // of K(p) and V(p-1), which the step refills with positions p+LK, p+LV.
+  // Step p: exp and P V of position p, S of position p+1, as phase A
+  // (score MFMAs + exponentials), the overflow check of the exponentials,
+  // then phase B (P V MFMAs).  The step's barrier publishes K(p+1) and V(p)
+  // and frees the slots of K(p) and V(p-1), which the step refills with
+  // positions p+LK, p+LV.
   // Ring slot and score set are compile-time: the loop is unrolled NB times.
   auto step = [&](int p, auto jconst) {
     constexpr int j = decltype(jconst)::value;  // p % kUnroll
@@ -446,10 +479,10 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     __syncthreads();
     issue_k(p + LK, (b + LK) % NB);
     issue_v(p + LV, (b + LV) % NB);
-    k.update_max(c);
     k.phase_a(k.kbuf((b + 1) % NB), k.s[cur], k.s[cur ^ 1], c);
+    k.settle_tile(k.s[cur], c);
     if (p + 1 < R) mask_tile(k.s[cur ^ 1], p + 1);
-    k.phase_b(k.vslot(b), k.s[cur ^ 1]);
+    k.phase_b(k.vslot(b));
   };
   for (int i = 0; i < nt; i += C::kUnroll)
     unrolled(i, nt, step, std::make_integer_sequence<int, C::kUnroll>());

@@ -112,6 +112,35 @@ def test_forward_peaked_rows(D):
         _check_full(w, x, *_run(w, x))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_forward_growing_scores(D, causal):
+    """Scores that grow from key tile to key tile by G (exp2 units) along the
+    processing order, so a later tile's exponentials against the running max
+    exceed any fixed bound (G = 200 overflows float32 before the max is
+    raised), and the same keys in falling order."""
+    import torch
+
+    from fa_inputs import Inputs, bf16_round
+
+    n = 512
+    rng = np.random.default_rng(11 + D)
+    scale = 1.0 / np.sqrt(D)
+    for growth in (4.0, 30.0, 200.0):
+        for rising in (True, False):
+            log(f"test_forward_growing_scores D={D} causal={causal} growth={growth} rising={rising}")
+            q = 0.1 * rng.standard_normal((1, 1, n, D)).astype(np.float32)
+            q[..., 0] = 1.0
+            k = 0.1 * rng.standard_normal((1, 1, n, D)).astype(np.float32)
+            j = np.arange(n) if rising else np.arange(n)[::-1]
+            k[0, 0, :, 0] = j * growth / (64 * scale * np.log2(np.e))
+            v = rng.standard_normal((1, 1, n, D)).astype(np.float32)
+            (qv, qb), (kv, kb), (vv, vb) = bf16_round(q), bf16_round(k), bf16_round(v)
+            x = Inputs(q=qv, k=kv, v=vv, do=None, q_bits=qb, k_bits=kb, v_bits=vb)
+            w = WORKLOADS["c2"].with_(name="growing", B=1, H=1, N=n, D=D, causal=causal)
+            _check_full(w, x, *_run(w, x))
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_forward_invariants(D):
     import torch

@@ -79,10 +79,7 @@ struct FwdCfg {
   // K/V ring: kNB slots each; K of position p is issued kLeadK steps
   // before the step that first reads it, V kLeadV steps before.  Step p
   // reads K(p+1) and V(p) and refills the slots of K(p) and V(p-1).
-#ifndef FA_FWD_NB
-#define FA_FWD_NB 4
-#endif
-  static constexpr int kNB = D <= 128 ? FA_FWD_NB : 2;
+  static constexpr int kNB = D <= 128 ? 4 : 2;
   static constexpr int kLeadK = kNB;
   static constexpr int kLeadV = kNB - 1;
   static constexpr int kLdsBytes = 2 * kNB * kTileBytes;
@@ -101,6 +98,11 @@ struct FwdCfg {
   // 8-wave workgroups and for 4-wave workgroups at D = 64 (two workgroups per
   // CU, each with a 64 KB ring); one for D = 256 (4 waves, 128 KB ring).
   static constexpr int kWavesPerEU = (W == 8 || D == 64) ? 2 : 1;
+  // Where a step issues its ring refills: right after its barrier, or (D =
+  // 128, ring of 4) after phase A, which keeps the copies' address and M0
+  // set-up off the path from the barrier to the first score MFMAs.  The
+  // 2-slot ring of D = 256 cannot spare the half step of lead.
+  static constexpr bool kLateRefill = D == 128;
 };
 
 template <int D, bool CAUSAL, int QB, int W>
@@ -469,7 +471,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   // (score MFMAs + exponentials), the overflow check of the exponentials,
   // then phase B (P V MFMAs).  The step's barrier publishes K(p+1) and V(p)
   // and frees the slots of K(p) and V(p-1), which the step refills with
-  // positions p+LK, p+LV.
+  // positions p+LK, p+LV (after the barrier or after phase A).
   // Ring slot and score set are compile-time: the loop is unrolled NB times.
   auto step = [&](int p, auto jconst) {
     constexpr int j = decltype(jconst)::value;  // p % kUnroll
@@ -477,9 +479,15 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     constexpr int cur = j & 1;                  // p % 2
     wait_vmcnt<C::kStepsInFlight * 2 * C::kLoadsPerTile>();
     __syncthreads();
-    issue_k(p + LK, (b + LK) % NB);
-    issue_v(p + LV, (b + LV) % NB);
+    if constexpr (!C::kLateRefill) {
+      issue_k(p + LK, (b + LK) % NB);
+      issue_v(p + LV, (b + LV) % NB);
+    }
     k.phase_a(k.kbuf((b + 1) % NB), k.s[cur], k.s[cur ^ 1], c);
+    if constexpr (C::kLateRefill) {
+      issue_k(p + LK, (b + LK) % NB);
+      issue_v(p + LV, (b + LV) % NB);
+    }
     k.settle_tile(k.s[cur], c);
     if (p + 1 < R) mask_tile(k.s[cur ^ 1], p + 1);
     k.phase_b(k.vslot(b));

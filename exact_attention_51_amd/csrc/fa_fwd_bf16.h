@@ -79,7 +79,7 @@ struct FwdCfg {
   // K/V ring: kNB slots each; K of position p is issued kLeadK steps
   // before the step that first reads it, V kLeadV steps before.  Step p
   // reads K(p+1) and V(p) and refills the slots of K(p) and V(p-1).
-  static constexpr int kNB = D <= 128 ? 4 : 2;
+  static constexpr int kNB = D == 128 ? 4 : 2;
   static constexpr int kLeadK = kNB;
   static constexpr int kLeadV = kNB - 1;
   static constexpr int kLdsBytes = 2 * kNB * kTileBytes;
@@ -95,9 +95,11 @@ struct FwdCfg {
   static_assert(kNB % 2 == 0, "the loop is unrolled over the ring and the two score sets");
   static constexpr int kUnroll = kNB;
   // Waves per SIMD the register budget is cut for: two (<= 256 VGPRs) for
-  // 8-wave workgroups and for 4-wave workgroups at D = 64 (two workgroups per
-  // CU, each with a 64 KB ring); one for D = 256 (4 waves, 128 KB ring).
-  static constexpr int kWavesPerEU = (W == 8 || D == 64) ? 2 : 1;
+  // the 8-wave workgroups of D = 128; three (<= 168 VGPRs) at D = 64, where
+  // three 4-wave workgroups share a CU (32 KB ring each) and the third wave
+  // per SIMD hides more of the exponentials, which at D = 64 cost as much
+  // issue time as the MFMAs; one for D = 256 (4 waves, 128 KB ring).
+  static constexpr int kWavesPerEU = D == 64 ? 3 : W == 8 ? 2 : 1;
   // Where a step issues its ring refills: right after its barrier, or (D =
   // 128, ring of 4) after phase A, which keeps the copies' address and M0
   // set-up off the path from the barrier to the first score MFMAs.  The

@@ -161,6 +161,21 @@ __device__ __forceinline__ void load_lds16_sbase(const void* sbase, uint32_t vof
       : "v"(voff), "s"(sb), "{m0}"(base));
 }
 
+// Same copy for a base and an LDS address that are already wave-uniform
+// scalars (computed by scalar instructions, never rebuilt from a VGPR): only
+// the M0 write needs its wait state.  The hazard scan of the built assembly
+// checks that no VALU instruction writes the base SGPRs shortly before.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)sbase);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)sbase >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sb), "{m0}"(lds));
+}
+
 // Same, 4 bytes per lane: lane l's dword lands at lds_base + 4 * l.
 __device__ __forceinline__ void load_lds4(const void* gptr, const void __attribute__((address_space(3))) * lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
@@ -208,9 +223,11 @@ struct RowTileCopier {
   uint32_t off[kLoads];  // byte offset of this lane's chunk relative to the tile's first row
   int rowi[kLoads];      // its row within the tile
   int wave_slot0;
+  uint32_t lds_wave;     // byte offset of this wave's first chunk in a tile (wave-uniform)
 
   __device__ __forceinline__ void init(int wave, int lane) {
     wave_slot0 = wave * kChunksPerWave;
+    lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane(wave_slot0 * 16);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = wave_slot0 + i * 64 + lane;
@@ -219,6 +236,19 @@ struct RowTileCopier {
       rowi[i] = r;
       off[i] = (uint32_t)((r * D + c * 8) * 2);
     }
+  }
+
+  // Rows of the tile starting byte_off bytes into src (a whole tile inside
+  // the tensor).  All address arithmetic is scalar: src + byte_off as the
+  // SGPR base, the LDS address in M0.
+  __device__ __forceinline__ void copy_at(const __bf16* __restrict__ src, uint32_t byte_off, lds_char* buf) const {
+    // readfirstlane pins the offset to an SGPR before the 64-bit add (the
+    // compiler may otherwise strength-reduce it into a VGPR and rebuild the
+    // base with a VALU instruction right before the copy)
+    const char* base = (const char*)src + (uint32_t)__builtin_amdgcn_readfirstlane((int)byte_off);
+    const uint32_t lds = (uint32_t)(uintptr_t)buf + lds_wave;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_lds16_s(base, off[i], lds + i * 64 * 16);
   }
 
   // Rows row0 .. row0+ROWS-1 must all exist: a scalar base per copy.

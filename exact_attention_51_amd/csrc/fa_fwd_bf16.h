@@ -401,16 +401,25 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     k.mask(acc, tile_row0(t) + kpart * 32, t * kBlockN, wq0, N);
   };
 
+  // Byte offset of the tile at sequence position p within the head: the
+  // same tile as tile_row0(seq_tile(p)) (min(t * 64, N - 64) covers both
+  // clamps), in 32 bits (a head holds fewer than 2^31 elements).
+  const uint32_t last_tile_bytes = (uint32_t)(N - kBlockN) * (D * 2);
+  auto tile_bytes = [&](int p) {
+    const int t = p < R ? first_masked + p : p - R;
+    return min((uint32_t)t * (kBlockN * D * 2), last_tile_bytes);
+  };
+
   // K and V of sequence position p go to ring slot p % NB.
   RowTileCopier<D, kBlockN, kWaves> cp;
   cp.init(wave, lane);
   auto issue_k = [&](int p, int b) {
     if constexpr (SMALL) cp.copy_clamped(K, N, 0, k.kbuf(b));
-    else cp.copy(K, tile_row0(seq_tile(p)), k.kbuf(b));
+    else cp.copy_at(K, tile_bytes(p), k.kbuf(b));
   };
   auto issue_v = [&](int p, int b) {
     if constexpr (SMALL) cp.copy_clamped(V, N, 0, k.vbuf(b));
-    else cp.copy(V, tile_row0(seq_tile(p)), k.vbuf(b));
+    else cp.copy_at(V, tile_bytes(p), k.vbuf(b));
   };
   // Prologue loads, oldest first, in the order the first steps need them:
   // K0, then K(i+1), V(i) for i = 0, 1, ...  Only K0 K1 V0 go before the Q

@@ -22,13 +22,32 @@ def _sregs(tok: str) -> set[int]:
     return {int(m.group(1))} if m else set()
 
 
+# scalar instructions whose first operand is a source, not a destination
+_SALU_NO_SDST = ("s_cmp", "s_bitcmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop", "s_barrier", "s_setprio",
+                 "s_sendmsg", "s_endpgm", "s_sleep", "s_trap", "s_icache", "s_dcache", "s_set", "s_ttrace",
+                 "s_store", "s_buffer_store", "s_atomic", "s_scratch_store")
+
+
+def _sgpr_writes(op: str, args: list[str]) -> tuple[set[int], bool]:
+    """SGPRs an instruction writes through its first operand, and whether it
+    is a VALU instruction (v_readfirstlane, v_cmp with an SGPR pair, ...)."""
+    if not args:
+        return set(), False
+    if op.startswith("v_"):
+        return _sregs(args[0]), True
+    if op.startswith("s_") and not op.startswith(_SALU_NO_SDST):
+        return _sregs(args[0]), False
+    return set(), False
+
+
 def valu_sgpr_vmem_hazards(asm: str, wait_states: int = 5) -> tuple[int, list[str]]:
-    """VMEM instructions with an SGPR base (saddr) written by a VALU
-    instruction fewer than `wait_states` wait states earlier in the same
-    basic block.  Returns (number of saddr LDS-DMA sites, offending lines)."""
+    """VMEM instructions with an SGPR base (saddr) whose most recent writer,
+    in the same basic block, is a VALU instruction fewer than `wait_states`
+    wait states earlier (a later scalar write of the same SGPR supersedes
+    it).  Returns (number of saddr LDS-DMA sites, offending lines)."""
     sites = 0
     bad: list[str] = []
-    hist: list[tuple[int, set[int]]] = []
+    hist: list[tuple[int, set[int], bool]] = []
     for raw in asm.split("\n"):
         s = raw.strip()
         if not s or s.startswith(";"):
@@ -42,22 +61,26 @@ def valu_sgpr_vmem_hazards(asm: str, wait_states: int = 5) -> tuple[int, list[st
         args = [a.strip() for a in s[len(op):].split(",")]
         if op.startswith("global_load_lds") and len(args) > 1 and args[1].startswith("s["):
             sites += 1
-            need = _sregs(args[1])
+            need = set(_sregs(args[1]))
             ws = 0
-            for w, written in reversed(hist):
-                if written & need:
-                    if ws < wait_states:
+            for w, written, valu in reversed(hist):
+                hit = written & need
+                if hit:
+                    if valu and ws < wait_states:
                         bad.append(s)
-                    break
+                        break
+                    need -= hit  # this writer is the most recent one for these SGPRs
+                    if not need:
+                        break
                 ws += w
-                if ws >= wait_states:
+                if ws >= wait_states:  # older VALU writes are far enough back
                     break
         w = 1
         m = re.match(r"s_nop\s+(\d+)", s)
         if m:
             w = int(m.group(1)) + 1
-        written = _sregs(args[0]) if (op.startswith("v_") and args) else set()
-        hist.append((w, written))
+        written, valu = _sgpr_writes(op, args)
+        hist.append((w, written, valu))
     return sites, bad
 
 

@@ -251,13 +251,6 @@ struct RowTileCopier {
     for (int i = 0; i < kLoads; ++i) load_lds16_s(base, off[i], lds + i * 64 * 16);
   }
 
-  // Rows row0 .. row0+ROWS-1 must all exist: a scalar base per copy.
-  __device__ __forceinline__ void copy(const __bf16* __restrict__ src, int row0, lds_char* buf) const {
-    const __bf16* base = src + (size_t)row0 * D;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_lds16_sbase(base, off[i], buf + (wave_slot0 + i * 64) * 16);
-  }
-
   // A tile reaching past row N-1 (row0 <= N-1): rows past it are clamped
   // onto it per lane.
   __device__ __forceinline__ void copy_clamped(const __bf16* __restrict__ src, int N, int row0, lds_char* buf) const {

@@ -4,10 +4,10 @@
 #include "fa_fwd_bf16.h"
 
 // Query blocks of 32 rows per wave, and waves per workgroup by head
-// dimension.  Every instance puts two waves on each SIMD: at D = 128 as one
-// 8-wave workgroup per CU (the K/V ring takes 128 KB of LDS), at D = 64 as
-// two 4-wave workgroups per CU, which do not share barriers and so drift
-// into complementary phases (the D = 64 step is bound by its VALU work).
+// dimension: at D = 128 one 8-wave workgroup per CU (two waves per SIMD;
+// the K/V ring takes 128 KB of LDS), at D = 64 three 4-wave workgroups per
+// CU, which do not share barriers and so drift into complementary phases
+// (the D = 64 step is bound by its VALU work).
 #ifndef FA_FWD_QB
 #define FA_FWD_QB 1
 #endif

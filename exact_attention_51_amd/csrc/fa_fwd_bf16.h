@@ -1,9 +1,10 @@
 // fa_fwd_bf16.h -- exact-attention forward kernel template, bf16 in/out, gfx950.
 // Instantiated in fa_fwd_bf16.hip (D = 64, 128) and fa_fwd_bf16_d256.hip.
 //
-// One workgroup = 8 waves at D <= 128 (two per SIMD), 4 waves at D = 256;
-// each wave owns 32*QB query rows of one (batch, head) and the whole loop
-// over keys for them.  The streaming structure is the one every page
+// One workgroup = 8 waves at D = 128 (two per SIMD), 4 waves at D = 64
+// (three workgroups per CU) and at D = 256 (one wave per SIMD, each tile's
+// keys split between two waves of the same rows); a wave owns 32*QB query
+// rows of one (batch, head) and the loop over keys for them.  The streaming structure is the one every page
 // describes ("Learning Metal with FlashAttention", section FlashAttention;
 // "Flash Attention" page, kernel anatomy; metal-flash-attention README,
 // "Quantifying performance", forward pseudocode): the Q rows are loaded once
@@ -24,7 +25,8 @@
 //   issues the score MFMAs of tile j+1, each carrying a share of the
 //   exponentials of tile j; phase B issues the P V MFMAs of tile j.
 // * K/V tiles go global -> LDS with 16-byte direct loads (no VGPR staging)
-//   into a ring of NB slots per tensor, issued 3-4 steps ahead.  The loop is
+//   into a ring of NB slots per tensor (4 at D = 128, else 2), issued up to
+//   4 steps ahead.  The loop is
 //   unrolled over the ring so every LDS address is a per-lane offset
 //   computed once plus an instruction immediate.  Rows are XOR-swizzled in
 //   16-byte chunks (see swz) so that both LDS read patterns are free of bank

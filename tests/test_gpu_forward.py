@@ -82,6 +82,17 @@ def test_workload_forward(name):
         _check_full(w, x, o, lse)
 
 
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False), (256, True)])
+def test_forward_long_sequence(D, causal):
+    """N = 65536 (twice c4's length: 1024 key tiles per row, 32-bit tile
+    offsets within a head up to 32 MiB), checked on sampled rows."""
+    w = WORKLOADS["c4"].with_(name="long", B=1, H=1, N=65536, D=D, causal=causal, q_mult=1.0, seed=65536 + D)
+    log(f"test_forward_long_sequence N={w.N} D={D} causal={causal}")
+    x = make_inputs(w, with_do=False)
+    o, lse = _run(w, x)
+    _check_rows(w, x, o, lse, count=16)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 5, 64, 65, 130, 256, 300, 520])

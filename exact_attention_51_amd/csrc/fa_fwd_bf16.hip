@@ -3,21 +3,6 @@
 // translation unit, fa_fwd_bf16_d256.hip, built with different flags).
 #include "fa_fwd_bf16.h"
 
-// Query blocks of 32 rows per wave, and waves per workgroup by head
-// dimension: at D = 128 one 8-wave workgroup per CU (two waves per SIMD;
-// the K/V ring takes 128 KB of LDS), at D = 64 three 4-wave workgroups per
-// CU, which do not share barriers and so drift into complementary phases
-// (the D = 64 step is bound by its VALU work).
-#ifndef FA_FWD_QB
-#define FA_FWD_QB 1
-#endif
-#ifndef FA_FWD_W64
-#define FA_FWD_W64 4
-#endif
-#ifndef FA_FWD_W128
-#define FA_FWD_W128 8
-#endif
-
 namespace fa {
 namespace fwd {
 
@@ -38,8 +23,13 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 
 int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
 
+// Query blocks of 32 rows per wave, and waves per workgroup by head
+// dimension: at D = 128 one 8-wave workgroup per CU (two waves per SIMD;
+// the K/V ring takes 128 KB of LDS), at D = 64 three 4-wave workgroups per
+// CU, which do not share barriers and so drift into complementary phases
+// (the D = 64 step is bound by its VALU work).
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  constexpr int QB = FA_FWD_QB, W64 = FA_FWD_W64, W128 = FA_FWD_W128;
+  constexpr int QB = 1, W64 = 4, W128 = 8;
   if (a.D == 64) return a.causal ? fwd::launch<64, true, QB, W64>(a, stream) : fwd::launch<64, false, QB, W64>(a, stream);
   if (a.D == 128)
     return a.causal ? fwd::launch<128, true, QB, W128>(a, stream) : fwd::launch<128, false, QB, W128>(a, stream);

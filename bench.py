@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -79,7 +80,7 @@ def device_tensors(w, x):
 
 
 def time_forward(w, q, k, v, steps: int, warmup: int):
-    """Returns (wall ms per step, mean event ms per launch)."""
+    """Returns (wall ms per step, HIP-event ms of each launch)."""
     import torch
 
     import exact_attention_51_amd as fa
@@ -100,7 +101,7 @@ def time_forward(w, q, k, v, steps: int, warmup: int):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     per_launch = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]
-    return (t1 - t0) * 1e3 / steps, sum(per_launch) / len(per_launch)
+    return (t1 - t0) * 1e3 / steps, per_launch
 
 
 def time_backward(w, q, k, v, steps: int, warmup: int):
@@ -216,7 +217,8 @@ def main() -> int:
     w = WORKLOADS["c3"]
     x = make_inputs(w, with_do=False)
     q, k, v = device_tensors(w, x)
-    ms_step, ms_launch = time_forward(w, q, k, v, args.steps, args.warmup)
+    ms_step, launches = time_forward(w, q, k, v, args.steps, args.warmup)
+    ms_launch = statistics.fmean(launches)
     flop = w.fwd_flop()
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (ms_launch * 1e-3) / 1e12
@@ -230,7 +232,8 @@ def main() -> int:
             qo, ko, vo = device_tensors(wo, xo)
             steps = max(3, args.steps // (4 if name == "c4" else 1))
             try:
-                _, ms = time_forward(wo, qo, ko, vo, steps, max(1, args.warmup // 2))
+                _, lo = time_forward(wo, qo, ko, vo, steps, max(1, args.warmup // 2))
+                ms = statistics.fmean(lo)
                 tf = wo.fwd_flop() / (ms * 1e-3) / 1e12
                 others[f"{name}_fwd"] = {"ms": round(ms, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
                 log(f"bench: {name} fwd {ms:.4f} ms -> {tf:.1f} TFLOPS")
@@ -288,6 +291,11 @@ def main() -> int:
             "traffic": traffic_from_profile(),
         },
         "cpu_baseline": cpu,
+        "launch_ms": {  # HIP events around each timed launch of the bench workload
+            "mean": round(ms_launch, 5),
+            "median": round(statistics.median(launches), 5),
+            "best": round(min(launches), 5),
+        },
         "device": device_info(),
         "others": others,
     }

@@ -142,11 +142,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         mine = mfma32(read_row_operand<D>(at, l32, ds, half), kvf[ds], ds == 0 ? f32x16{} : mine);
       if (dh == 0) {  // P = exp(S - L), masked; queries of register r: (r/4)*8 + half*4 + r%4
         const bool masked = (CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N);
+        // L of the lane's 16 queries: four runs of four consecutive rows
+        float lq[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *(const f32x4 __attribute__((address_space(3)))*)(lbuf(sl) + 4 * (g * 8 + half * 4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lq[g * 4 + i] = l4[i];
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-          const float lq = *(const float __attribute__((address_space(3)))*)(lbuf(sl) + 4 * qr);
-          float x = __builtin_fmaf(mine[r], c, -lq * kLog2e);
+          float x = __builtin_fmaf(mine[r], c, -lq[r] * kLog2e);
           if (masked) {
             bool keep = tq0 + qr < N;
             if constexpr (CAUSAL) keep = keep && key <= tq0 + qr;
@@ -172,6 +179,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     // operands from the exchange, then their half of dV and dK
     if (t > t_begin && tile_work(t - 1)) {
       const int sl = (t - 1) % 3, xb = (t - 1) & 1;
+      float dl[16];  // delta of the lane's 16 queries, read as four runs of four
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 d4 = *(const f32x4 __attribute__((address_space(3)))*)(dbuf(sl) + 4 * (g * 8 + half * 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dl[g * 4 + i] = d4[i];
+      }
       bf16x8 ppk[2], dspk[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -184,9 +198,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = cc * 8 + 2 * i + u;
-            const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-            const float dq = *(const float __attribute__((address_space(3)))*)(dbuf(sl) + 4 * qr);
-            dsv[u] = (float)pp[i][u] * (xdp(xb)[r * 64] - dq);
+            dsv[u] = (float)pp[i][u] * (xdp(xb)[r * 64] - dl[r]);
           }
           dd[i] = pack_bf16(dsv[0], dsv[1]);
         }

@@ -150,17 +150,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
           for (int i = 0; i < 4; ++i) lq[g * 4 + i] = l4[i];
         }
+        // two instances: tiles that need no mask carry no selects
+        auto exp_p = [&](auto mconst) {
+          constexpr bool MASKED = decltype(mconst)::value;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-          float x = __builtin_fmaf(mine[r], c, -lq[r] * kLog2e);
-          if (masked) {
-            bool keep = tq0 + qr < N;
-            if constexpr (CAUSAL) keep = keep && key <= tq0 + qr;
-            x = keep ? x : -__builtin_inff();
+          for (int r = 0; r < 16; ++r) {
+            const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
+            float x = __builtin_fmaf(mine[r], c, -lq[r] * kLog2e);
+            if constexpr (MASKED) {
+              bool keep = tq0 + qr < N;
+              if constexpr (CAUSAL) keep = keep && key <= tq0 + qr;
+              x = keep ? x : -__builtin_inff();
+            }
+            mine[r] = fast_exp2(x);
           }
-          mine[r] = fast_exp2(x);
-        }
+        };
+        if (masked)
+          exp_p(std::integral_constant<bool, true>());
+        else
+          exp_p(std::integral_constant<bool, false>());
         // P rounded to bf16 once; both waves form dS from this rounded P
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {

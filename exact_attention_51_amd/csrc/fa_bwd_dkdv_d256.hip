@@ -43,7 +43,7 @@ struct KvDsplitCfg {
   static constexpr int kTileBytes = kQTile * D * 2;
   static constexpr int kStatBytes = 256;       // 64 floats of L or delta (rows past the tile are spare)
   static constexpr int kXpBytes = 2 * 64 * 16;  // P: two bf16x8 operands per lane
-  static constexpr int kXdBytes = 16 * 64 * 4;  // dP: a 32x32 fp32 accumulator, lane-major
+  static constexpr int kXdBytes = 16 * 64 * 4;  // dP: a 32x32 fp32 accumulator, [r/4][lane] x 4
   static constexpr int kSlotBytes = 2 * kTileBytes + 2 * kStatBytes;  // Q, dO, L, delta of one tile
   static constexpr int kXBytes = 2 * (kXpBytes + kXdBytes);            // both key groups
   static constexpr int kLdsBytes = 3 * kSlotBytes + 2 * kXBytes;
@@ -83,13 +83,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const bool group_active = wk0 < N;
   const int n_qtiles = (N + C::kQTile - 1) / C::kQTile;
   const int t_begin = CAUSAL ? k0 / C::kQTile : 0;  // earlier query tiles see none of these keys
-  // exchange of tile t in buffer t % 2: [key group][P (bf16x8 [cc][lane]), dP (fp32 [r][lane])]
+  // exchange of tile t in buffer t % 2: [key group][P (bf16x8 [cc][lane]),
+  // dP (fp32x4 [r/4][lane]: each lane's 16 values as four 16-byte runs)]
   auto xp = [&](int xb) {
     return (bf16x8 __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
                                                          kgrp * (C::kXpBytes + C::kXdBytes)) + lane;
   };
   auto xdp = [&](int xb) {
-    return (float __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
+    return (f32x4 __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
                                                       kgrp * (C::kXpBytes + C::kXdBytes) + C::kXpBytes) + lane;
   };
 
@@ -179,7 +180,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xdp(xb)[r * 64] = mine[r];
+        for (int g = 0; g < 4; ++g)
+          xdp(xb)[g * 64] = f32x4{mine[4 * g], mine[4 * g + 1], mine[4 * g + 2], mine[4 * g + 3]};
       }
     }
 
@@ -194,6 +196,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
         for (int i = 0; i < 4; ++i) dl[g * 4 + i] = d4[i];
       }
+      float dpv[16];  // dP of the lane's 16 queries
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 p4 = xdp(xb)[g * 64];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dpv[g * 4 + i] = p4[i];
+      }
       bf16x8 ppk[2], dspk[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -206,7 +215,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = cc * 8 + 2 * i + u;
-            dsv[u] = (float)pp[i][u] * (xdp(xb)[r * 64] - dl[r]);
+            dsv[u] = (float)pp[i][u] * (dpv[r] - dl[r]);
           }
           dd[i] = pack_bf16(dsv[0], dsv[1]);
         }

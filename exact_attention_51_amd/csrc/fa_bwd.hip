@@ -84,8 +84,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     wave_last = min(wq0 + 31, N - 1) / kKeyTile;
   }
 
-  copy_rows_lds<D, kKeyTile, kWavesQ>(K, N, 0, kbuf[0], wave, lane);
-  copy_rows_lds<D, kKeyTile, kWavesQ>(V, N, 0, vbuf[0], wave, lane);
+  // K/V tile t into ring slot b: scalar-base copies with loop-invariant
+  // per-lane offsets, rows clamped onto N-1 only for a ragged last tile
+  RowTileCopier<D, kKeyTile, kWavesQ> cp;
+  cp.init(wave, lane);
+  auto copy_tile = [&](int t, int b) {
+    const int row0 = t * kKeyTile;
+    if (row0 + kKeyTile <= N) {
+      cp.copy_at(K, (uint32_t)row0 * (D * 2), kbuf[b]);
+      cp.copy_at(V, (uint32_t)row0 * (D * 2), vbuf[b]);
+    } else {
+      cp.copy_clamped(K, N, row0, kbuf[b]);
+      cp.copy_clamped(V, N, row0, vbuf[b]);
+    }
+  };
+  copy_tile(0, 0);
 
   // Q^T and dO^T as B operands (lane = query column), delta and L per lane.
   const int row = wq0 + l32;
@@ -115,10 +128,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   for (int j = 0; j < nt; ++j) {
     wait_vmcnt<0>();
     __syncthreads();
-    if (j + 1 < nt) {
-      copy_rows_lds<D, kKeyTile, kWavesQ>(K, N, (j + 1) * kKeyTile, kbuf[(j + 1) & 1], wave, lane);
-      copy_rows_lds<D, kKeyTile, kWavesQ>(V, N, (j + 1) * kKeyTile, vbuf[(j + 1) & 1], wave, lane);
-    }
+    if (j + 1 < nt) copy_tile(j + 1, (j + 1) & 1);
     if (!wave_active || j > wave_last) continue;
     const lds_char* kt = kbuf[j & 1];
     const lds_char* vt = vbuf[j & 1];

@@ -14,6 +14,9 @@ from the returned CSVs, under profiles/:
                                hash still matches)
   fwd_bf16_c3_counters.md      shader clock, MFMA busy, VALU/LDS activity, LDS
                                bank conflicts and the instruction mix
+  kernels_all_workloads.md     kernel durations of the full `bench.py --no-cpu`
+                               (every workload: c2, c3, c4, c5 forward and c5
+                               backward), per workload and kernel
 
 The TCC FETCH_SIZE / WRITE_SIZE counters are calibrated against a plain
 device copy of known size: the factor (bytes moved / counter bytes) for each
@@ -49,7 +52,8 @@ SQ_PASSES = {
             "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU", "SQ_WAVES", "GRBM_GUI_ACTIVE"],
     "tcc": ["TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE"],
 }
-PASSES = ["ktrace", "traffic", *SQ_PASSES]
+PASSES = ["ktrace", "traffic", *SQ_PASSES, "ktrace_all"]
+BENCH_ALL = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "10", "--warmup", "3", "--no-cpu"]
 FLOP_C3 = 4 * 8192 * 8192 * 128 * 2 * 16 // 2
 # 256-row query block t (of 32 per head) visits key tiles 0 .. 4t+3 of 64 keys
 EXP_C3 = 2 * 16 * sum(256 * 64 * (4 * t + 4) for t in range(8192 // 256))
@@ -122,6 +126,9 @@ def main() -> int:
                  os.path.join(OUT, f"fwd_{ctr}"), "-o", "run", "--", *BENCH], 300)
             run(["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", os.path.join(OUT, f"copy_{ctr}"), "-o",
                  "run", "--", *me, "--copy", str(COPY_BYTES)], 300)
+        if "ktrace_all" in passes:  # 4. kernel trace of every workload
+            run(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                 os.path.join(OUT, "ktrace_all"), "-o", "run", "--", *BENCH_ALL], 600)
         for name, ctrs in SQ_PASSES.items():  # 3. SQ / TCC counters of the forward kernel
             if name not in passes:
                 continue
@@ -194,6 +201,8 @@ def summarize(out: str, dest: str) -> None:
         f.write("\n".join(lines) + "\n")
     if all(os.path.isdir(os.path.join(out, n)) for n in ("sq1", "sq2")):
         summarize_counters(out, dest)
+    if os.path.isdir(os.path.join(out, "ktrace_all")):
+        summarize_all_workloads(out, dest)
     print("\n".join(lines), flush=True)
 
 
@@ -210,6 +219,57 @@ def per_dispatch_counters(outdir: str) -> tuple[dict, dict]:
         if r.get("Start_Timestamp") and r.get("End_Timestamp"):
             span[d] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
     return vals, span
+
+
+def summarize_all_workloads(out: str, dest: str) -> None:
+    """Per-dispatch kernel trace of the full bench run, split by workload.
+
+    bench.py runs c3, then c2, c4, c5 forward and c5 backward (whose setup
+    runs one c5 forward); c3 and c4 share a kernel instance and are told
+    apart by order.  Medians skip each run's first launch."""
+    sys.path.insert(0, ROOT)
+    from fa_inputs import WORKLOADS
+
+    (path,) = glob.glob(os.path.join(out, "ktrace_all", "**", "*kernel_trace.csv"), recursive=True)
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    seen_c2, runs = False, {}
+    for r in rows:
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+        family = name.split("(")[0]  # the name without its argument list
+        if "bwd_" in family:
+            label = "c5 bwd"
+        elif "fwd_bf16_kernel<64" in family:
+            label, seen_c2 = "c2 fwd", True
+        elif "fwd_bf16_kernel<256" in family:
+            label = "c5 fwd"
+        elif "fwd_bf16_kernel<128" in family:
+            label = "c4 fwd" if seen_c2 else "c3 fwd"  # bench order: c3, c2, c4
+        else:
+            continue
+        runs.setdefault((label, family), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    flop = {"c2 fwd": WORKLOADS["c2"].fwd_flop(), "c3 fwd": WORKLOADS["c3"].fwd_flop(),
+            "c4 fwd": WORKLOADS["c4"].fwd_flop(), "c5 fwd": WORKLOADS["c5"].fwd_flop()}
+    w5 = WORKLOADS["c5"]
+    per_bwd = {"bwd_dq": 6 * w5.N * w5.N * w5.D * w5.B * w5.H, "bwd_dkdv": 8 * w5.N * w5.N * w5.D * w5.B * w5.H}
+    lines = ["# Kernel durations of every bench workload", "",
+             "Command (repository root, GPU box): `python3 profile_fwd.py`; pass `ktrace_all` =",
+             f"`rocprofv3 --kernel-trace --stats -- {' '.join(['python3', 'bench.py'] + BENCH_ALL[2:])}`.",
+             "Median and minimum over the launches of each run after its first; TFLOPS from the median, with",
+             "4N²D·B·H (halved under causal) for the forward, 6N²D·B·H for dQ and 8N²D·B·H for dK/dV.", "",
+             "| workload | kernel | launches | median µs | min µs | TFLOPS |", "|---|---|---|---|---|---|"]
+    for (label, kname), ts in runs.items():
+        body = ts[1:] if len(ts) > 1 else ts
+        med = statistics.median(body)
+        if label == "c5 bwd":
+            f = next((v for k, v in per_bwd.items() if k in kname), None)
+        else:
+            f = flop.get(label)
+        tf = f"{f / (med * 1e-6) / 1e12:.0f}" if f else ""
+        short = kname.replace("void ", "").replace("fa::", "")
+        lines.append(f"| {label} | `{short}` | {len(ts)} | {med:.1f} | {min(body):.1f} | {tf} |")
+    with open(os.path.join(dest, "kernels_all_workloads.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def tcc_lines(med: dict) -> list[str]:

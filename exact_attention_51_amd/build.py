@@ -53,19 +53,16 @@ COMMON_FLAGS = [
 # semantics.  MFMA results are kept in architectural VGPRs: with the default
 # accumulator-register form the compiler moved the O accumulators between
 # AGPRs and VGPRs on every key tile (hundreds of v_accvgpr moves per tile).
-# The D = 256 forward keeps its 128-register O accumulators in AGPRs (and
-# this compiler crashes on it in VGPR form), so it is built without it.
+# The D = 256 forward fits the VGPR form too because it keeps its Q rows in
+# LDS rather than registers.
 KERNEL_FLAGS = ["-fno-honor-nans"]
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 HOST_ONLY_SOURCES = {"fa_api.hip"}
-AGPR_FORM_SOURCES = {"fa_fwd_bf16_d256.hip"}
 
 
 def source_flags(name: str) -> list[str]:
     if name in HOST_ONLY_SOURCES:
         return []
-    if name in AGPR_FORM_SOURCES:
-        return list(KERNEL_FLAGS)
     return KERNEL_FLAGS + VGPR_FORM
 
 

@@ -84,7 +84,18 @@ struct FwdCfg {
   static constexpr int kNB = D == 128 ? 4 : 2;
   static constexpr int kLeadK = kNB;
   static constexpr int kLeadV = kNB - 1;
-  static constexpr int kLdsBytes = 2 * kNB * kTileBytes;
+  static constexpr int kRingBytes = 2 * kNB * kTileBytes;
+  // Q rows in LDS (D = 256) instead of registers: with them in registers
+  // the O accumulators no longer fit beside the rest and the compiler
+  // copies them between VGPRs and AGPRs around every P V MFMA.
+#ifndef FA_FWD_QLDS
+#define FA_FWD_QLDS 1
+#endif
+  static constexpr bool kQInLds = D == 256 && FA_FWD_QLDS;
+  static constexpr int kQBytes = kQInLds ? kQBlocks * 32 * QB * D * 2 : 0;
+  static constexpr int kLdsBytes = kRingBytes + kQBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
+  static_assert(!kQInLds || QB == 1, "Q fragments from LDS are read for one 32-row block");
   // merge of a key split: per query block, 64 lanes x (O accumulators + m + l) floats
   static constexpr int kMergeFloats = QB * kDBlocks * 16 + 2 * QB;
   static_assert(kSplit == 1 || kLdsBytes >= kQBlocks * 64 * 4 * kMergeFloats,
@@ -116,7 +127,10 @@ struct FwdKernel {
   static constexpr int KB = C::kKB;
 
   // per-wave state
-  bf16x8 qf[QB][C::kDSteps];  // Q^T as B operands: query column l32, d = ds*16 + half*8 + 0..7
+  // Q^T as B operands: query column l32, d = ds*16 + half*8 + 0..7 (in
+  // registers, or read from the LDS copy at qoff with kQInLds)
+  bf16x8 qf[C::kQInLds ? 1 : QB][C::kQInLds ? 1 : C::kDSteps];
+  int qoff[8];
   f32x16 o[QB][C::kDBlocks];  // O^T accumulators
   f32x16 s[2][KB][QB];        // two score tiles in ping-pong: [set][kb][qb]
   bf16x8 pk[QB][KB][2];       // P of the tile in flight, as B operands
@@ -141,7 +155,7 @@ struct FwdKernel {
       for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[ds] + kb * 32 * D * 2);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[kb][qb] = mfma32(kf, qf[qb][ds], ds == 0 ? f32x16{} : acc[kb][qb]);
+        for (int qb = 0; qb < QB; ++qb) acc[kb][qb] = mfma32(kf, qfrag(qb, ds), ds == 0 ? f32x16{} : acc[kb][qb]);
       }
   }
 
@@ -267,6 +281,15 @@ struct FwdKernel {
   static constexpr int nP = kVFrags * QB;          // P V MFMAs per step
   static constexpr int kPairs = 8 * KB * QB;       // exp pairs per tile and lane
 
+  // Q fragment for k-step ds (block qb): the swizzle of a D = 256 row
+  // repeats past chunk 16, so k-steps 8.. are the first eight + 256 bytes
+  __device__ __forceinline__ bf16x8 qfrag(int qb, int ds) const {
+    if constexpr (C::kQInLds)
+      return *(const bf16x8 __attribute__((address_space(3)))*)(smem + qoff[ds % 8] + (ds / 8) * 256);
+    else
+      return qf[qb][ds];
+  }
+
   // K fragment i = (ds, kb) = (i / KB, i % KB)
   __device__ __forceinline__ bf16x8 kfrag(const lds_char* kt, int i) const {
     return *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[i / KB] + (i % KB) * 32 * D * 2);
@@ -292,16 +315,20 @@ struct FwdKernel {
       lt[qb] = 0.f;
     }
     bf16x8 kf[kKFrags];
+    bf16x8 qv[C::kQInLds ? C::kDSteps : 1];  // Q fragments read with the K fragments (kQInLds)
     bf16x2 pr[QB][KB][2][4];
 #pragma unroll
-    for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kt, i);
+    for (int i = 0; i < kPf; ++i) {
+      kf[i] = kfrag(kt, i);
+      if (C::kQInLds && i % KB == 0) qv[i / KB] = qfrag(0, i / KB);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kKFrags; ++i) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int ds = i / KB, kb = i % KB;
-        sn[kb][qb] = mfma32(kf[i], qf[qb][ds], ds == 0 ? f32x16{} : sn[kb][qb]);
+        sn[kb][qb] = mfma32(kf[i], C::kQInLds ? qv[ds] : qf[qb][ds], ds == 0 ? f32x16{} : sn[kb][qb]);
         // exp pairs e = (qb, kb, cc, w) carried by this MFMA
         const int mi = i * QB + qb;
 #pragma unroll
@@ -315,7 +342,10 @@ struct FwdKernel {
             pk[eq][kb2][cc] = join8(pr[eq][kb2][cc][0], pr[eq][kb2][cc][1], pr[eq][kb2][cc][2], pr[eq][kb2][cc][3]);
         }
       }
-      if (i + kPf < kKFrags) kf[i + kPf] = kfrag(kt, i + kPf);
+      if (i + kPf < kKFrags) {
+        kf[i + kPf] = kfrag(kt, i + kPf);
+        if (C::kQInLds && (i + kPf) % KB == 0) qv[(i + kPf) / KB] = qfrag(0, (i + kPf) / KB);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -428,6 +458,13 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   // rows are loaded: the compiler cannot see these copies and waits for
   // every load in flight before it first uses Q, so the rest is issued
   // after the first score tile.
+  if constexpr (C::kQInLds) {
+    // this workgroup's query rows (clamped onto N-1) go to LDS after the
+    // ring, oldest of the prologue copies so the first wait covers them
+    RowTileCopier<D, C::kBlockM, kWaves> qcp;
+    qcp.init(wave, lane);
+    qcp.copy_clamped(Q, N, q0, k.smem + C::kRingBytes);
+  }
   issue_k(0, 0);
   issue_k(1, 1);
   issue_v(0, 0);
@@ -455,12 +492,18 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     }
   }
 
+  if constexpr (C::kQInLds) {
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) k.qoff[ds] = C::kRingBytes + lds_off_bytes<D>(qblk * 32 + k.l32, ds * 2 + k.half);
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     int row = wq0 + qb * 32 + k.l32;
     row = row < N ? row : N - 1;
+    if constexpr (!C::kQInLds) {
 #pragma unroll
-    for (int ds = 0; ds < C::kDSteps; ++ds) k.qf[qb][ds] = *(const bf16x8*)(Q + (size_t)row * D + ds * 16 + k.half * 8);
+      for (int ds = 0; ds < C::kDSteps; ++ds) k.qf[qb][ds] = *(const bf16x8*)(Q + (size_t)row * D + ds * 16 + k.half * 8);
+    }
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll

@@ -1,7 +1,7 @@
 // fa_fwd_bf16_d256.hip -- forward instance for D = 256 (one 32-row query
-// block per wave, two-deep K/V ring).  Built without forcing MFMA results
-// into architectural VGPRs: at D = 256 the O accumulators (128 registers)
-// belong in the accumulator registers.
+// block per wave, each tile's keys split between two waves, two-deep K/V
+// ring, the workgroup's Q rows in LDS so that the 128 O accumulator
+// registers and the rest fit the architectural VGPRs).
 #include "fa_fwd_bf16.h"
 
 namespace fa {

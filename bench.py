@@ -226,8 +226,12 @@ def main() -> int:
 
     others = {}
     if not args.no_others:
-        for name in ("c2", "c4", "c5"):
-            wo = WORKLOADS[name]
+        # the other workloads, then (context only) the one shape the pages
+        # benchmark, B=2 H=4 N=2048 D=128, in both masking modes
+        p1 = WORKLOADS["c3"].with_(B=2, H=4, N=2048, D=128, seed=6)
+        runs = [(n, WORKLOADS[n]) for n in ("c2", "c4", "c5")]
+        runs += [("p1", p1.with_(name="p1", causal=False)), ("p1_causal", p1.with_(name="p1_causal", causal=True))]
+        for name, wo in runs:
             xo = make_inputs(wo, with_do=False)
             qo, ko, vo = device_tensors(wo, xo)
             steps = max(3, args.steps // (4 if name == "c4" else 1))

@@ -225,31 +225,37 @@ def summarize_all_workloads(out: str, dest: str) -> None:
     """Per-dispatch kernel trace of the full bench run, split by workload.
 
     bench.py runs c3, then c2, c4, c5 forward and c5 backward (whose setup
-    runs one c5 forward); c3 and c4 share a kernel instance and are told
-    apart by order.  Medians skip each run's first launch."""
+    runs one c5 forward), then the pages' shape B=2 H=4 N=2048 D=128 in both
+    masking modes; runs of one kernel instance are told apart by that order.
+    Medians skip each run's first launch."""
     sys.path.insert(0, ROOT)
     from fa_inputs import WORKLOADS
 
     (path,) = glob.glob(os.path.join(out, "ktrace_all", "**", "*kernel_trace.csv"), recursive=True)
     with open(path) as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
-    seen_c2, runs = False, {}
+    seen_c2, seen_c5, runs = False, False, {}
     for r in rows:
         name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
         family = name.split("(")[0]  # the name without its argument list
         if "bwd_" in family:
-            label = "c5 bwd"
+            label, seen_c5 = "c5 bwd", True
         elif "fwd_bf16_kernel<64" in family:
             label, seen_c2 = "c2 fwd", True
         elif "fwd_bf16_kernel<256" in family:
-            label = "c5 fwd"
-        elif "fwd_bf16_kernel<128" in family:
-            label = "c4 fwd" if seen_c2 else "c3 fwd"  # bench order: c3, c2, c4
+            label, seen_c5 = "c5 fwd", True
+        elif "fwd_bf16_kernel<128" in family:  # bench order: c3, c2, c4, c5, then the pages' shape
+            if seen_c5:
+                label = "p1 causal fwd" if "<128, true" in family else "p1 fwd"
+            else:
+                label = "c4 fwd" if seen_c2 else "c3 fwd"
         else:
             continue
         runs.setdefault((label, family), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    p1 = WORKLOADS["c3"].with_(B=2, H=4, N=2048, D=128)
     flop = {"c2 fwd": WORKLOADS["c2"].fwd_flop(), "c3 fwd": WORKLOADS["c3"].fwd_flop(),
-            "c4 fwd": WORKLOADS["c4"].fwd_flop(), "c5 fwd": WORKLOADS["c5"].fwd_flop()}
+            "c4 fwd": WORKLOADS["c4"].fwd_flop(), "c5 fwd": WORKLOADS["c5"].fwd_flop(),
+            "p1 fwd": p1.with_(causal=False).fwd_flop(), "p1 causal fwd": p1.with_(causal=True).fwd_flop()}
     w5 = WORKLOADS["c5"]
     per_bwd = {"bwd_dq": 6 * w5.N * w5.N * w5.D * w5.B * w5.H, "bwd_dkdv": 8 * w5.N * w5.N * w5.D * w5.B * w5.H}
     lines = ["# Kernel durations of every bench workload", "",

@@ -94,6 +94,16 @@ def test_backward_causal_long(D):
     _check(w, x, _run_bwd(w, x))
 
 
+def test_backward_c3_shape():
+    """The causal backward at the c3 sequence length and head dimension
+    (N = 8192, D = 128) for one head against the dense oracle: heads are
+    independent, so the 32 heads of c3 only repeat this."""
+    w = WORKLOADS["c3"].with_(name="c3_bwd_head", B=1, H=1, backward=True, seed=13)
+    log(f"test_backward_c3_shape N={w.N} D={w.D} causal={w.causal}")
+    x = make_inputs(w, with_do=True)
+    _check(w, x, _run_bwd(w, x))
+
+
 def test_backward_deterministic():
     """No atomics anywhere: two runs agree bit for bit."""
     import torch

@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["probabilities", "forward_rows", "forward", "backward"]
+__all__ = ["probabilities", "forward_rows", "forward", "forward_kv", "backward"]
 
 
 def _as_f64(x) -> np.ndarray:
@@ -121,6 +121,53 @@ def forward(q, k, v, scale: float, causal: bool = False, row_block: int = 256):
             for r0 in range(0, n, row_block):
                 rows = np.arange(r0, min(n, r0 + row_block))
                 o[b, h, rows], lse[b, h, rows] = forward_rows(q[b, h], k[b, h], v[b, h], rows, scale, causal)
+    if single:
+        return o[0, 0], lse[0, 0]
+    return o, lse
+
+
+def forward_kv(q, k, v, scale: float, causal: bool = False):
+    """Attention of Nq query rows over Nk keys (Nq and Nk may differ).
+
+    q: [B, H, Nq, D] (or [Nq, D]); k, v: [B, H, Nk, D] (or [Nk, D]).
+    Returns (O [.., Nq, D], L [.., Nq]) in float64.
+
+    This is the definition above with the two lengths apart: the case of a
+    block of new query rows attending to a longer key sequence, and of
+    decoding one row at a time, which the "Flash Attention" page's section
+    on the technique's boundaries sets apart from the square case.  The
+    pages do not say how a causal mask lines up when Nq < Nk; the reading
+    taken here is that the query rows are the LAST Nq positions of the key
+    sequence (bottom-right alignment): query i sees key j iff
+    j <= i + (Nk - Nq).  With Nq = Nk this is the square mask of
+    ``forward``.  Under causal masking Nq must not exceed Nk (the first
+    rows would see no key at all).
+    """
+    q = np.asarray(q)
+    single = q.ndim == 2
+    if single:
+        q, k, v = q[None, None], np.asarray(k)[None, None], np.asarray(v)[None, None]
+    else:
+        k, v = np.asarray(k), np.asarray(v)
+    b_, h_, nq, d = q.shape
+    nk = k.shape[2]
+    if k.shape != (b_, h_, nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, D] with the batch, heads and D of q")
+    if causal and nq > nk:
+        raise ValueError("causal attention with more query rows than keys leaves rows with no key")
+    offset = nk - nq
+    o = np.empty((b_, h_, nq, d), dtype=np.float64)
+    lse = np.empty((b_, h_, nq), dtype=np.float64)
+    cols = np.arange(nk)
+    for b in range(b_):
+        for h in range(h_):
+            qh, kh, vh = (_as_f64(x[b, h]) for x in (q, k, v))
+            s = scale * (qh @ kh.T)
+            if causal:
+                s = np.where(cols[None, :] <= np.arange(nq)[:, None] + offset, s, -np.inf)
+            p, m, l = _softmax_two_pass(s)
+            o[b, h] = p @ vh
+            lse[b, h] = m + np.log(l)
     if single:
         return o[0, 0], lse[0, 0]
     return o, lse

@@ -7,7 +7,8 @@ device and passes raw device pointers and the current torch stream.  There
 is no CPU or PyTorch fallback: if the library is missing, calls raise.
 
 Layout: q, k, v, o, dO, dq, dk, dv are [B, H, N, D] contiguous; lse and
-delta are float32 [B, H, N].
+delta are float32 [B, H, N].  ``fwd_kv`` takes q [B, H, Nq, D] and k, v
+[B, H, Nk, D].
 """
 
 from __future__ import annotations
@@ -17,7 +18,7 @@ import math
 from . import _lib
 from ._lib import FAError  # noqa: F401
 
-__all__ = ["fwd", "bwd_dq", "bwd_dkdv", "bwd", "FAError", "library_path", "version"]
+__all__ = ["fwd", "fwd_kv", "kv_splits", "bwd_dq", "bwd_dkdv", "bwd", "FAError", "library_path", "version"]
 
 
 def library_path() -> str:
@@ -106,6 +107,55 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
     name = "fa_fwd" if dtype == torch.bfloat16 else "fa_fwd_f32"
     rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D, float(scale), int(bool(causal)), _stream_ptr(q, stream))
     _lib.check(name, rc)
+    return out, lse
+
+
+def kv_splits(B: int, H: int, Nq: int, Nk: int, D: int, causal: bool = False) -> int:
+    """The key-range count ``fa_fwd_kv`` picks for ``num_splits=0``."""
+    n = _lib.load().fa_fwd_kv_splits(B, H, Nq, Nk, D, int(bool(causal)))
+    _lib.check("fa_fwd_kv_splits", min(n, 0))
+    return n
+
+
+def fwd_kv(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int = 0, out=None, lse=None,
+           workspace=None, stream=None):
+    """``fa_fwd_kv``: attention of q [B, H, Nq, D] over k, v [B, H, Nk, D].
+
+    Under ``causal`` the query rows are the last Nq positions of the key
+    sequence (row i sees keys 0 .. i + Nk - Nq).  The keys of each query
+    block are split into ``num_splits`` ranges (0: the library's choice)
+    whose results are merged on the GPU.  The workspace they need is
+    allocated here with torch unless one is passed (a uint8 GPU tensor of at
+    least ``fa_fwd_kv_workspace_bytes`` bytes).  Returns (o, lse).
+    """
+    torch = _torch()
+    _check_bhnd("q", q, torch.bfloat16)
+    B, H, Nq, D = q.shape
+    _check_bhnd("k", k, torch.bfloat16)
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected ({B}, {H}, Nk, {D})")
+    _check_bhnd("v", v, torch.bfloat16, k.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _lib.load()
+    splits = int(num_splits) if num_splits else kv_splits(B, H, Nq, Nk, D, causal)
+    need = lib.fa_fwd_kv_workspace_bytes(B, H, Nq, D, splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and (not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    ws_ptr = _ptr(workspace) if workspace is not None else ctypes_void(None)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    out = torch.empty_like(q) if out is None else out
+    _check_bhnd("out", out, torch.bfloat16, q.shape)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_rows("lse", lse, (B, H, Nq))
+    rc = lib.fa_fwd_kv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D, float(scale), int(bool(causal)), splits,
+        ws_ptr, ws_bytes, _stream_ptr(q, stream),
+    )
+    _lib.check("fa_fwd_kv", rc)
     return out, lse
 
 

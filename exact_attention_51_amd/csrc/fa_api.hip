@@ -42,7 +42,46 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.causal = causal;
+  a.Nk = N;
+  a.n_split = 1;
+  a.part_o = nullptr;
+  a.part_l = nullptr;
   return a;
+}
+
+constexpr int kMaxSplits = 256;
+
+// Key ranges per query block when the caller leaves the choice to the
+// library: enough (query block, key range) workgroups to give every CU its
+// share of workgroups at once, and at least two key tiles of 64 per range.
+int choose_splits(int B, int H, int Nq, int Nk, int D) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t slots = (int64_t)cus * fa::fwd_workgroups_per_cu(D);
+  const int rows = fa::fwd_rows_per_workgroup(D);
+  const int64_t blocks = (int64_t)((Nq + rows - 1) / rows) * B * H;
+  if (blocks >= slots) return 1;
+  int64_t s = (slots + blocks - 1) / blocks;
+  const int64_t tiles = (Nk + 63) / 64;
+  s = s < tiles / 2 ? s : tiles / 2;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t kv_workspace_bytes(int B, int H, int Nq, int D, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)splits * B * H * Nq * (size_t)(D + 1) * sizeof(float);
+}
+
+int check_kv(int B, int H, int Nq, int Nk, int D, float scale, int causal) {
+  if (Nk <= 0) return FA_ERR_INVALID_ARG;
+  int rc = check_common(B, H, Nq, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  if ((int64_t)B * H * Nk * D > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+  return FA_OK;
 }
 
 }  // namespace
@@ -73,6 +112,38 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (rc != FA_OK) return rc;
   const fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, D, scale, causal);
   return map_launch(fa::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+int fa_fwd_kv_splits(int B, int H, int Nq, int Nk, int D, int causal) {
+  const int rc = check_kv(B, H, Nq, Nk, D, 1.0f, causal);
+  if (rc != FA_OK) return rc;
+  return choose_splits(B, H, Nq, Nk, D);
+}
+
+size_t fa_fwd_kv_workspace_bytes(int B, int H, int Nq, int D, int num_splits) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || D <= 0 || num_splits <= 0) return 0;
+  return kv_workspace_bytes(B, H, Nq, D, num_splits);
+}
+
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
+              float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  const int rc = check_kv(B, H, Nq, Nk, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  const int splits = num_splits == 0 ? choose_splits(B, H, Nq, Nk, D) : num_splits;
+  const size_t need = kv_workspace_bytes(B, H, Nq, D, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, D, scale, causal);
+  a.Nk = Nk;
+  a.n_split = splits;
+  if (splits > 1) {
+    a.part_o = (float*)workspace;
+    a.part_l = (float*)workspace + (size_t)splits * B * H * Nq * D;
+  }
+  int lrc = fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
+  if (lrc == 0 && splits > 1) lrc = fa::launch_fwd_kv_merge(a, (hipStream_t)stream);
+  return map_launch(lrc);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int D,

@@ -373,8 +373,13 @@ __device__ __forceinline__ void unrolled(int i, int n, F& f, std::integer_sequen
   (void)((i + J < n && (f(i + J, std::integral_constant<int, J>()), true)) && ...);
 }
 
-// SMALL: N < 64, a single tile whose missing rows are clamped per lane.
-template <int D, bool CAUSAL, int QB, int W, bool SMALL>
+// SMALL: fewer than 64 keys, a single tile whose missing rows are clamped
+// per lane.  KV: query and key lengths apart (a.N queries, a.Nk keys; the
+// causal mask lines the queries up with the last keys), and with
+// a.n_split > 1 the key tiles of a query block divided into a.n_split
+// ranges, one workgroup each, whose results go to a.part_o / a.part_l for
+// the merge kernel.  Without KV the kernel is the square forward.
+template <int D, bool CAUSAL, int QB, int W, bool SMALL, bool KV = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W),
                           amdgpu_waves_per_eu(FwdCfg<D, QB, W>::kWavesPerEU, FwdCfg<D, QB, W>::kWavesPerEU))) void
 fwd_bf16_kernel(FwdArgs a, TileSched sched) {
@@ -395,21 +400,53 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   // query block and key half of this wave (kpart = 0 without a key split)
   const int qblk = wave % C::kQBlocks, kpart = wave / C::kQBlocks;
 
-  int qtile, bh;
-  sched_item(sched, blockIdx.x, qtile, bh);
-  const int N = a.N;
+  int qtile, bh, split = 0;
+  if constexpr (KV) {
+    // the scheduler's items are (query tile, key range) pairs, heaviest
+    // query tile first under causal masking
+    int item;
+    sched_item(sched, blockIdx.x, item, bh);
+    qtile = item / a.n_split;
+    split = item - qtile * a.n_split;
+  } else {
+    sched_item(sched, blockIdx.x, qtile, bh);
+  }
+  const int N = a.N;                                  // query rows
+  const int Nk = KV ? a.Nk : N;                       // keys
+  const int off = (KV && CAUSAL) ? Nk - N : 0;        // query i sees keys <= i + off
   const size_t head_off = (size_t)bh * N * D;
+  const size_t kv_head_off = KV ? (size_t)bh * Nk * D : head_off;
   const __bf16* __restrict__ Q = (const __bf16*)a.q + head_off;
-  const __bf16* __restrict__ K = (const __bf16*)a.k + head_off;
-  const __bf16* __restrict__ V = (const __bf16*)a.v + head_off;
+  const __bf16* __restrict__ K = (const __bf16*)a.k + kv_head_off;
+  const __bf16* __restrict__ V = (const __bf16*)a.v + kv_head_off;
 
   const int q0 = qtile * C::kBlockM;
   const int wq0 = q0 + qblk * C::kRowsPerWave;
   const bool wave_active = wq0 < N;
-  const int n_ktiles_all = (N + kBlockN - 1) / kBlockN;
-  int nt = n_ktiles_all;
-  if constexpr (CAUSAL) nt = min(q0 + C::kBlockM - 1, N - 1) / kBlockN + 1;
-  const bool ragged = (N % kBlockN) != 0;
+  const int n_ktiles_all = (Nk + kBlockN - 1) / kBlockN;
+  int nt_q = n_ktiles_all;  // key tiles the block sees
+  if constexpr (CAUSAL) nt_q = min(q0 + C::kBlockM - 1 + off, Nk - 1) / kBlockN + 1;
+  // this workgroup's key tiles [t_lo, t_hi)
+  int t_lo = 0, t_hi = nt_q;
+  if constexpr (KV) {
+    t_lo = nt_q * split / a.n_split;
+    t_hi = nt_q * (split + 1) / a.n_split;
+    if (t_lo == t_hi) {
+      // an empty key range (fewer tiles than ranges): its rows get L = -inf,
+      // which gives the range weight 0 in the merge
+      if (wave_active && kpart == 0 && k.half == 0) {
+        float* __restrict__ Lp = a.part_l + ((size_t)split * a.B * a.H + bh) * N;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int row = wq0 + qb * 32 + k.l32;
+          if (row < N) Lp[row] = -__builtin_inff();
+        }
+      }
+      return;
+    }
+  }
+  const int nt = t_hi - t_lo;
+  const bool ragged = (Nk % kBlockN) != 0;
 
   // Processing order.  Online softmax does not depend on the order of the
   // key tiles, so the R tiles that need a mask go first: the block's
@@ -417,28 +454,29 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   // ragged last tile (or the single tile of a short tensor), else none.
   // Every wave processes every tile of its block; keys a wave may not see
   // are masked.
-  int first_masked = nt;
+  int first_masked = nt_q;
   if (SMALL) first_masked = 0;
-  else if (CAUSAL) first_masked = q0 / kBlockN;
+  else if (CAUSAL) first_masked = (q0 + off) / kBlockN;
   else if (ragged) first_masked = n_ktiles_all - 1;
-  const int R = nt - first_masked;
+  if constexpr (KV) first_masked = min(max(first_masked, t_lo), t_hi);
+  const int R = t_hi - first_masked;
   // tile at sequence position p (positions past the end load a valid tile
   // that is never read)
-  auto seq_tile = [&](int p) { return p < R ? first_masked + p : p - R; };
+  auto seq_tile = [&](int p) { return p < R ? first_masked + p : t_lo + p - R; };
   // First row of key tile t: tiles lie inside the tensor, a ragged last
-  // tile is shifted back to end at row N-1 (its keys below t*64 are masked).
-  auto tile_row0 = [&](int t) { return SMALL ? 0 : min(min(t, n_ktiles_all - 1) * kBlockN, N - kBlockN); };
+  // tile is shifted back to end at row Nk-1 (its keys below t*64 are masked).
+  auto tile_row0 = [&](int t) { return SMALL ? 0 : min(min(t, n_ktiles_all - 1) * kBlockN, Nk - kBlockN); };
   auto mask_tile = [&](f32x16 (&acc)[C::kKB][QB], int p) {
     const int t = seq_tile(p);
-    k.mask(acc, tile_row0(t) + kpart * 32, t * kBlockN, wq0, N);
+    k.mask(acc, tile_row0(t) + kpart * 32, t * kBlockN, wq0 + off, Nk);
   };
 
   // Byte offset of the tile at sequence position p within the head: the
   // same tile as tile_row0(seq_tile(p)) (min(t * 64, N - 64) covers both
   // clamps), in 32 bits (a head holds fewer than 2^31 elements).
-  const uint32_t last_tile_bytes = (uint32_t)(N - kBlockN) * (D * 2);
+  const uint32_t last_tile_bytes = (uint32_t)(Nk - kBlockN) * (D * 2);
   auto tile_bytes = [&](int p) {
-    const int t = p < R ? first_masked + p : p - R;
+    const int t = p < R ? first_masked + p : t_lo + p - R;
     return min((uint32_t)t * (kBlockN * D * 2), last_tile_bytes);
   };
 
@@ -446,11 +484,11 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   RowTileCopier<D, kBlockN, kWaves> cp;
   cp.init(wave, lane);
   auto issue_k = [&](int p, int b) {
-    if constexpr (SMALL) cp.copy_clamped(K, N, 0, k.kbuf(b));
+    if constexpr (SMALL) cp.copy_clamped(K, Nk, 0, k.kbuf(b));
     else cp.copy_at(K, tile_bytes(p), k.kbuf(b));
   };
   auto issue_v = [&](int p, int b) {
-    if constexpr (SMALL) cp.copy_clamped(V, N, 0, k.vbuf(b));
+    if constexpr (SMALL) cp.copy_clamped(V, Nk, 0, k.vbuf(b));
     else cp.copy_at(V, tile_bytes(p), k.vbuf(b));
   };
   // Prologue loads, oldest first, in the order the first steps need them:
@@ -592,6 +630,36 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
 
   // ---- epilogue: O = acc / l, L = m*scale + ln l
   if (!wave_active) return;
+  if constexpr (KV) {
+    if (a.n_split > 1) {
+      // one key range of several: normalised O in float32 and L of the
+      // range; a row that sees no key of the range gets L = -inf (weight 0)
+      float* __restrict__ Op = a.part_o + ((size_t)split * a.B * a.H + bh) * N * D;
+      float* __restrict__ Lp = a.part_l + ((size_t)split * a.B * a.H + bh) * N;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float lt = sum_halves(k.l[qb]);
+        const int row = wq0 + qb * 32 + k.l32;
+        if (row < N) {
+          if (lt > 0.f) {
+            const float inv = 1.0f / lt;
+#pragma unroll
+            for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 w = {k.o[qb][db][g4 * 4 + 0] * inv, k.o[qb][db][g4 * 4 + 1] * inv,
+                                 k.o[qb][db][g4 * 4 + 2] * inv, k.o[qb][db][g4 * 4 + 3] * inv};
+                *(f32x4*)(Op + (size_t)row * D + db * 32 + g4 * 8 + k.half * 4) = w;
+              }
+            if (k.half == 0) Lp[row] = k.m[qb] * a.scale + fast_log2(lt) * kLn2;
+          } else if (k.half == 0) {
+            Lp[row] = -__builtin_inff();
+          }
+        }
+      }
+      return;
+    }
+  }
   __bf16* __restrict__ O = (__bf16*)a.o + head_off;
   float* __restrict__ Lse = a.lse + (size_t)bh * N;
 #pragma unroll

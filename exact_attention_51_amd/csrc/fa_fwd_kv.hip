@@ -1,0 +1,101 @@
+// fa_fwd_kv.hip -- forward with query and key lengths apart and the key
+// tiles of each query block optionally split over several workgroups
+// (instances for D = 64 and D = 128; D = 256 in fa_fwd_kv_d256.hip), and
+// the kernel that merges the key ranges.
+//
+// Splitting the keys serves the shapes whose (query block, batch, head)
+// grid is too small for 256 CUs: a short query block over a long key
+// sequence (one decoded row is the extreme case) or few heads.  Each range
+// yields the exact attention of its keys, normalised, with its own L; the
+// ranges combine exactly as L = ln sum_s e^{L_s} and
+// O = sum_s e^{L_s - L} O_s, the same combination the saved L of the
+// metal-flash-attention README's forward ("Quantifying performance") makes
+// possible and that the D = 256 kernel already performs between the two
+// key halves of a tile inside one workgroup.
+#include "fa_fwd_bf16.h"
+
+namespace fa {
+namespace fwd {
+
+template <int D, bool CAUSAL, int QB, int W>
+int launch_kv(const FwdArgs& a, hipStream_t stream) {
+  using C = FwdCfg<D, QB, W>;
+  const int n_qtiles = (a.N + C::kBlockM - 1) / C::kBlockM;
+  const TileSched sched = make_sched(n_qtiles * a.n_split, a.B * a.H, CAUSAL);
+  const long grid = (long)n_qtiles * a.n_split * a.B * a.H;
+  if (a.Nk < 64)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QB, W, true, true>), dim3((unsigned)grid), dim3(64 * W), 0, stream,
+                       a, sched);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QB, W, false, true>), dim3((unsigned)grid), dim3(64 * W), 0,
+                       stream, a, sched);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// One thread per four consecutive d of a row: the row's L_s of every range
+// give L, then O = sum_s e^{L_s - L} O_s (ranges of weight 0 are not read),
+// rounded to bf16.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_kv_merge_kernel(FwdArgs a) {
+  constexpr int kThreadsPerRow = D / 4;
+  constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  const long rows = (long)a.B * a.H * a.N;
+  const long r = (long)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
+  if (r >= rows) return;
+  const int t = threadIdx.x % kThreadsPerRow;
+  const int S = a.n_split;
+  const float* __restrict__ Lp = a.part_l + r;
+  const float* __restrict__ Op = a.part_o + r * D + t * 4;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < S; ++s) mx = __builtin_fmaxf(mx, Lp[(size_t)s * rows]);
+  float sum = 0.f;
+  for (int s = 0; s < S; ++s) sum += fast_exp2((Lp[(size_t)s * rows] - mx) * kLog2e);
+  const float L = mx + fast_log2(sum) * kLn2;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float w = fast_exp2((Lp[(size_t)s * rows] - L) * kLog2e);
+    if (w > 0.f) {
+      const f32x4 x = *(const f32x4*)(Op + (size_t)s * rows * D);
+      acc[0] = __builtin_fmaf(w, x[0], acc[0]);
+      acc[1] = __builtin_fmaf(w, x[1], acc[1]);
+      acc[2] = __builtin_fmaf(w, x[2], acc[2]);
+      acc[3] = __builtin_fmaf(w, x[3], acc[3]);
+    }
+  }
+  const u32x2 packed = {pack_bf16_u32(acc[0], acc[1]), pack_bf16_u32(acc[2], acc[3])};
+  *(u32x2*)((__bf16*)a.o + r * D + t * 4) = packed;
+  if (t == 0) a.lse[r] = L;
+}
+
+}  // namespace fwd
+
+int fwd_workgroups_per_cu(int D) { return D == 64 ? 3 : 1; }
+int fwd_rows_per_workgroup(int D) {
+  if (D == 64) return fwd::FwdCfg<64, 1, 4>::kBlockM;
+  if (D == 128) return fwd::FwdCfg<128, 1, 8>::kBlockM;
+  return fwd::FwdCfg<256, 1, 4>::kBlockM;
+}
+
+// Workgroup shapes as for the square forward (fa_fwd_bf16.hip).
+int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream) {
+  if (a.D == 64) return a.causal ? fwd::launch_kv<64, true, 1, 4>(a, stream) : fwd::launch_kv<64, false, 1, 4>(a, stream);
+  if (a.D == 128)
+    return a.causal ? fwd::launch_kv<128, true, 1, 8>(a, stream) : fwd::launch_kv<128, false, 1, 8>(a, stream);
+  if (a.D == 256) return launch_fwd_bf16_kv_d256(a, stream);
+  return -2;
+}
+
+int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream) {
+  const long rows = (long)a.B * a.H * a.N;
+  auto go = [&](auto kern, int rows_per_block) {
+    const long blocks = (rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  };
+  if (a.D == 64) return go(fwd::fwd_kv_merge_kernel<64>, 256 / 16);
+  if (a.D == 128) return go(fwd::fwd_kv_merge_kernel<128>, 256 / 32);
+  if (a.D == 256) return go(fwd::fwd_kv_merge_kernel<256>, 256 / 64);
+  return -2;
+}
+
+}  // namespace fa

@@ -17,6 +17,15 @@ struct FwdArgs {
   float scale;       // multiplies Q K^T
   float scale_log2;  // scale * log2(e)
   int causal;
+  // Query and key lengths apart (fa_fwd_kv): N is the query length, Nk the
+  // key length; causal masking aligns the queries with the last keys.  With
+  // n_split > 1 each key range writes its normalised O (float32) and its L
+  // to part_o [n_split][B*H][N][D] and part_l [n_split][B*H][N], and a
+  // second kernel merges them into o and lse.
+  int Nk;
+  int n_split;
+  float* part_o;
+  float* part_l;
 };
 
 struct BwdArgs {
@@ -39,6 +48,14 @@ struct BwdArgs {
 // Each returns 0 on a successful launch, -1 when the launch failed and -2
 // when no kernel instance exists for the shape.
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// fa_fwd_kv.hip: query and key lengths apart, keys optionally split over
+// n_split workgroups per query block, then the merge of the key ranges.
+int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream);
+int launch_fwd_bf16_kv_d256(const FwdArgs& a, hipStream_t stream);  // fa_fwd_kv_d256.hip
+int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream);
+// Workgroups of the forward kernel one CU runs at a time, by head dimension.
+int fwd_workgroups_per_cu(int D);
+int fwd_rows_per_workgroup(int D);
 int launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 int launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);

@@ -51,6 +51,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -69,6 +71,60 @@ extern "C" {
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
            float scale, int causal, void* stream);
+
+/*
+ * Forward with query and key lengths apart, keys optionally split over
+ * several workgroups per query block (bf16 in and out, float32
+ * accumulation).
+ *   q       : bf16 [B][H][Nq][D]       (read)
+ *   k, v    : bf16 [B][H][Nk][D]       (read)
+ *   o       : bf16 [B][H][Nq][D]       (written)
+ *   lse     : f32  [B][H][Nq]          (written; natural log)
+ * Query row i sees every key without causal masking.  With causal = 1 the
+ * query rows are the last Nq positions of the key sequence: row i sees keys
+ * 0 .. i + (Nk - Nq), so Nq = Nk is fa_fwd's mask and Nq = 1 (decoding one
+ * row) sees every key.  The pages fix no alignment for Nq != Nk; this is
+ * the reading taken.  causal = 1 requires Nq <= Nk.
+ *
+ * The "Flash Attention" page (section on the technique's boundaries) sets
+ * decoding apart: a few query rows cannot fill a matrix tile, so the
+ * (query block, batch, head) grid is too small to occupy the GPU.  Here the
+ * key tiles a query block sees are divided into num_splits contiguous
+ * ranges, one workgroup each; every range writes the attention of its keys
+ * (O normalised by its own row sum, float32) and its L_s into the
+ * workspace, and a second kernel merges them exactly:
+ * L = ln sum_s e^{L_s}, O = sum_s e^{L_s - L} O_s.
+ *
+ *   num_splits      : 0 = the library's choice (fa_fwd_kv_splits), else
+ *                     1..256.  1 runs without workspace or merge.
+ *   workspace       : device memory of at least
+ *                     fa_fwd_kv_workspace_bytes(B, H, Nq, D, splits) bytes,
+ *                     16-byte aligned, owned by the caller (may be NULL when
+ *                     that size is 0).  Its contents on entry do not
+ *                     matter; it is overwritten.  Two calls in flight at
+ *                     once must not share it.
+ * D in {64, 128, 256}; any Nq, Nk >= 1.  Errors: FA_ERR_INVALID_ARG also
+ * for causal with Nq > Nk, num_splits outside 0..256, or a missing, short
+ * or misaligned workspace.
+ */
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
+              float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The key-range count fa_fwd_kv uses for num_splits = 0: enough
+ * workgroups to occupy every CU of the current device, at least two key
+ * tiles of 64 per range, at most 256.  Returns a count >= 1, or a negative
+ * FA_ERR_* code for invalid sizes.  Queries the current device's CU count
+ * (no device state is changed).
+ */
+int fa_fwd_kv_splits(int B, int H, int Nq, int Nk, int D, int causal);
+
+/*
+ * Workspace bytes fa_fwd_kv needs for num_splits ranges:
+ * num_splits * B * H * Nq * (D + 1) * 4 when num_splits > 1, else 0
+ * (also 0 for non-positive arguments).
+ */
+size_t fa_fwd_kv_workspace_bytes(int B, int H, int Nq, int D, int num_splits);
 
 /*
  * Forward, float32 in and out, float32 arithmetic throughout.  Same

@@ -22,7 +22,19 @@ def _declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
-    assert names == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_dq", "fa_bwd_dkdv", "fa_strerror", "fa_version"])
+    assert names == sorted(
+        [
+            "fa_fwd",
+            "fa_fwd_f32",
+            "fa_fwd_kv",
+            "fa_fwd_kv_splits",
+            "fa_fwd_kv_workspace_bytes",
+            "fa_bwd_dq",
+            "fa_bwd_dkdv",
+            "fa_strerror",
+            "fa_version",
+        ]
+    )
 
 
 def test_library_exports_every_declared_symbol():
@@ -44,6 +56,8 @@ def test_header_signatures_match_binding():
                 assert a is ctypes.c_void_p, (name, p)
             elif p.startswith("float"):
                 assert a is ctypes.c_float, (name, p)
+            elif p.startswith("size_t"):
+                assert a is ctypes.c_size_t, (name, p)
             else:
                 assert p.startswith("int") and a is ctypes.c_int, (name, p)
 
@@ -100,6 +114,41 @@ def test_backward_argument_validation(fn, nptr):
     assert f(*ptrs, 1, 1, 128, 64, float("nan"), 0, None) == inv
     assert f(*ptrs, 1, 1, 128, 64, 0.125, 7, None) == inv
     assert f(*ptrs, 1, 1, 128, 80, 0.125, 0, None) == uns
+
+
+def _fwd_kv(lib, ptrs=None, B=1, H=1, Nq=16, Nk=300, D=128, scale=0.125, causal=0, splits=4, ws=None, ws_bytes=0):
+    ptrs = ptrs or [FAKE] * 5
+    return lib.fa_fwd_kv(*ptrs, B, H, Nq, Nk, D, scale, causal, splits, ws, ws_bytes, None)
+
+
+def test_forward_kv_argument_validation():
+    lib = _lib.load()
+    inv, uns = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    need = lib.fa_fwd_kv_workspace_bytes(1, 1, 16, 128, 4)
+    assert need == 4 * 16 * 129 * 4
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert _fwd_kv(lib, ptrs=ptrs, ws=FAKE, ws_bytes=need) == inv
+    ok = dict(ws=FAKE, ws_bytes=need)
+    assert _fwd_kv(lib, Nq=0, **ok) == inv
+    assert _fwd_kv(lib, Nk=0, **ok) == inv
+    assert _fwd_kv(lib, scale=float("nan"), **ok) == inv
+    assert _fwd_kv(lib, causal=1, Nq=301, Nk=300, **ok) == inv  # causal needs Nq <= Nk
+    assert _fwd_kv(lib, splits=-1, **ok) == inv
+    assert _fwd_kv(lib, splits=257, **ok) == inv
+    assert _fwd_kv(lib, splits=4) == inv  # no workspace
+    assert _fwd_kv(lib, splits=4, ws=FAKE, ws_bytes=need - 1) == inv  # short workspace
+    assert _fwd_kv(lib, splits=4, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == inv  # misaligned
+    assert _fwd_kv(lib, B=1024, H=1024, Nq=16, Nk=4096, D=64, **ok) == inv  # K holds 2^38 elements
+    for d in (32, 96, 160):
+        assert _fwd_kv(lib, D=d, **ok) == uns
+    # sizes of the workspace
+    assert lib.fa_fwd_kv_workspace_bytes(2, 3, 5, 64, 1) == 0
+    assert lib.fa_fwd_kv_workspace_bytes(2, 3, 5, 64, 7) == 7 * 2 * 3 * 5 * 65 * 4
+    assert lib.fa_fwd_kv_workspace_bytes(0, 3, 5, 64, 7) == 0
+    assert lib.fa_fwd_kv_splits(1, 1, 0, 10, 64, 0) == inv
+    assert lib.fa_fwd_kv_splits(1, 1, 10, 5, 64, 1) == inv
 
 
 def test_python_binding_rejects_cpu_tensors():

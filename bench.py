@@ -12,7 +12,9 @@ Prints ONE JSON line.  Besides the contract fields it carries
 ``roofline`` (the forward kernel against the bf16 dense MFMA peak, timed
 with HIP events on the launch stream), ``cpu_baseline`` (the float64 CPU
 oracle timed on a bounded sample of the same workload) and ``others``
-(TFLOPS of the other workloads, measured the same way).
+(TFLOPS of the other workloads, measured the same way, and ``fa_fwd_kv``
+with split key ranges on the pages' shape and on decoding one row per head,
+where the K/V read rate against the 8 TB/s HBM peak is the figure).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
 """
@@ -33,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd attention TFLOPS (4N²D·B·H, causal halved) + % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
 KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_bf16.h", "fa_device.h", "fa_sched.h"]
 
@@ -102,6 +105,42 @@ def time_forward(w, q, k, v, steps: int, warmup: int):
     t1 = time.perf_counter()
     per_launch = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]
     return (t1 - t0) * 1e3 / steps, per_launch
+
+
+def time_forward_kv(B, H, Nq, Nk, D, causal, seed, steps: int, warmup: int):
+    """``fa_fwd_kv`` at the library's split count on seeded inputs (K, V at
+    the key length, Q the last Nq rows of the drawn Q).  Returns
+    (split count, mean HIP-event ms per call, K/V bytes read per call)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_51_amd as fa
+    from fa_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS["c3"].with_(B=B, H=H, N=Nk, D=D, causal=causal, seed=seed)
+    x = make_inputs(w, with_do=False)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, k, v = bf(x.q_bits[:, :, Nk - Nq :]), bf(x.k_bits), bf(x.v_bits)
+    del x
+    splits = fa.kv_splits(B, H, Nq, Nk, D, causal)
+    need = fa._lib.load().fa_fwd_kv_workspace_bytes(B, H, Nq, D, splits)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    for _ in range(warmup):
+        fa.fwd_kv(q, k, v, w.scale, causal, splits, out=o, lse=lse, workspace=ws)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fa.fwd_kv(q, k, v, w.scale, causal, splits, out=o, lse=lse, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return splits, e0.elapsed_time(e1) / steps, 2 * B * H * Nk * D * 2
 
 
 def time_backward(w, q, k, v, steps: int, warmup: int):
@@ -261,6 +300,33 @@ def main() -> int:
                 except fa.FAError as e:
                     others[f"{name}_bwd"] = {"error": str(e)}
             del qo, ko, vo
+            torch.cuda.empty_cache()
+
+        # fa_fwd_kv at the library's split count: the pages' shape (its
+        # 64 query blocks leave most CUs idle unsplit) and one decoded row
+        # per head over long key sequences (bound by reading K and V)
+        kv_runs = [
+            ("p1_fwd_kv", (2, 4, 2048, 2048, 128, False, 6)),
+            ("p1_causal_fwd_kv", (2, 4, 2048, 2048, 128, True, 6)),
+            ("decode_1x8_32768_fwd_kv", (1, 8, 1, 32768, 128, True, 4)),
+            ("decode_8x16_8192_fwd_kv", (8, 16, 1, 8192, 128, True, 7)),
+        ]
+        for name, (B, H, Nq, Nk, D, causal, seed) in kv_runs:
+            try:
+                splits, ms, kv_bytes = time_forward_kv(B, H, Nq, Nk, D, causal, seed, args.steps, max(1, args.warmup // 2))
+                kv_flop = 4 * B * H * Nq * Nk * D // (2 if causal and Nq == Nk else 1)
+                gbs = kv_bytes / (ms * 1e-3) / 1e9
+                others[name] = {
+                    "shape": {"B": B, "H": H, "Nq": Nq, "Nk": Nk, "D": D, "causal": causal},
+                    "splits": splits,
+                    "ms": round(ms, 5),
+                    "tflops": round(kv_flop / (ms * 1e-3) / 1e12, 2),
+                    "kv_read_gbs": round(gbs, 1),
+                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                }
+                log(f"bench: {name} splits={splits} {ms:.4f} ms, K/V read {gbs:.0f} GB/s")
+            except fa.FAError as e:
+                others[name] = {"error": str(e)}
             torch.cuda.empty_cache()
 
     cpu = None

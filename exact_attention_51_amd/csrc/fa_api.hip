@@ -52,13 +52,26 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
 constexpr int kMaxSplits = 256;
 
 // Key ranges per query block when the caller leaves the choice to the
-// library: enough (query block, key range) workgroups to give every CU its
-// share of workgroups at once, and at least two key tiles of 64 per range.
+// library.  Matrix-core path: enough (query block, key range) workgroups to
+// give every CU its share of workgroups at once, and at least two key tiles
+// of 64 per range.  Decode path (Nq <= 4): about one workgroup per CU (two
+// for three or four rows), at least two ranges, each over at least 256 keys
+// (measured: 256 to 512 decode workgroups beat both fewer and more).
 int choose_splits(int B, int H, int Nq, int Nk, int D) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
+  if (Nq <= fa::kDecodeMaxRows) {
+    const int64_t heads = (int64_t)B * H;
+    int64_t s = (cus + heads - 1) / heads;
+    if (s < 2) s = 2;
+    if (Nq > 2) s *= 2;
+    const int64_t ranges = (Nk + 255) / 256;
+    s = s < ranges ? s : ranges;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : (int)s;
+  }
   const int64_t slots = (int64_t)cus * fa::fwd_workgroups_per_cu(D);
   const int rows = fa::fwd_rows_per_workgroup(D);
   const int64_t blocks = (int64_t)((Nq + rows - 1) / rows) * B * H;
@@ -141,7 +154,8 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
     a.part_o = (float*)workspace;
     a.part_l = (float*)workspace + (size_t)splits * B * H * Nq * D;
   }
-  int lrc = fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
+  int lrc = Nq <= fa::kDecodeMaxRows ? fa::launch_fwd_decode(a, (hipStream_t)stream)
+                                     : fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
   if (lrc == 0 && splits > 1) lrc = fa::launch_fwd_kv_merge(a, (hipStream_t)stream);
   return map_launch(lrc);
 }

@@ -67,6 +67,65 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_kernel(FwdArgs a) {
   if (t == 0) a.lse[r] = L;
 }
 
+// The same merge for many key ranges: one workgroup per row, the ranges
+// divided among kP groups of D/4 threads (range s goes to group s % kP), so
+// the loads of different ranges are in flight together; the groups' partial
+// max, sums and O combine through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
+  constexpr int kThreadsPerRow = D / 4;
+  constexpr int kP = 256 / kThreadsPerRow;
+  __shared__ float red[kP];
+  __shared__ f32x4 ored[kP][kThreadsPerRow];
+  const long rows = (long)a.B * a.H * a.N;
+  const long r = blockIdx.x;
+  const int t = threadIdx.x % kThreadsPerRow, p = threadIdx.x / kThreadsPerRow;
+  const int S = a.n_split;
+  const float* __restrict__ Lp = a.part_l + r;
+  const float* __restrict__ Op = a.part_o + r * D + t * 4;
+  float mx = -__builtin_inff();
+  for (int s = p; s < S; s += kP) mx = __builtin_fmaxf(mx, Lp[(size_t)s * rows]);
+  if (t == 0) red[p] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int i = 1; i < kP; ++i) mx = __builtin_fmaxf(mx, red[i]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int s = p; s < S; s += kP) sum += fast_exp2((Lp[(size_t)s * rows] - mx) * kLog2e);
+  if (t == 0) red[p] = sum;
+  __syncthreads();
+  sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kP; ++i) sum += red[i];
+  const float L = mx + fast_log2(sum) * kLn2;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = p; s < S; s += kP) {
+    const float w = fast_exp2((Lp[(size_t)s * rows] - L) * kLog2e);
+    if (w > 0.f) {
+      const f32x4 x = *(const f32x4*)(Op + (size_t)s * rows * D);
+      acc[0] = __builtin_fmaf(w, x[0], acc[0]);
+      acc[1] = __builtin_fmaf(w, x[1], acc[1]);
+      acc[2] = __builtin_fmaf(w, x[2], acc[2]);
+      acc[3] = __builtin_fmaf(w, x[3], acc[3]);
+    }
+  }
+  ored[p][t] = acc;
+  __syncthreads();
+  if (p != 0) return;
+#pragma unroll
+  for (int i = 1; i < kP; ++i) {
+    const f32x4 x = ored[i][t];
+    acc[0] += x[0];
+    acc[1] += x[1];
+    acc[2] += x[2];
+    acc[3] += x[3];
+  }
+  const u32x2 packed = {pack_bf16_u32(acc[0], acc[1]), pack_bf16_u32(acc[2], acc[3])};
+  *(u32x2*)((__bf16*)a.o + r * D + t * 4) = packed;
+  if (t == 0) a.lse[r] = L;
+}
+
 }  // namespace fwd
 
 int fwd_workgroups_per_cu(int D) { return D == 64 ? 3 : 1; }
@@ -85,8 +144,19 @@ int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream) {
   return -2;
 }
 
+// Few ranges: one thread per 4 columns of a row walks every range.  Many
+// ranges (more than 8): one workgroup per row with the ranges spread over
+// its threads, so a row's loads do not form one long dependent chain.
 int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream) {
   const long rows = (long)a.B * a.H * a.N;
+  if (a.n_split > 8) {
+    const dim3 grid((unsigned)rows), block(256);
+    if (a.D == 64) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<64>, grid, block, 0, stream, a);
+    else if (a.D == 128) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<128>, grid, block, 0, stream, a);
+    else if (a.D == 256) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<256>, grid, block, 0, stream, a);
+    else return -2;
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   auto go = [&](auto kern, int rows_per_block) {
     const long blocks = (rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, a);

@@ -53,6 +53,11 @@ int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_bf16_kv_d256(const FwdArgs& a, hipStream_t stream);  // fa_fwd_kv_d256.hip
 int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream);
+// fa_decode.hip: a.N <= kDecodeMaxRows query rows per head on the vector
+// ALUs, keys split over a.n_split workgroups (same partial-result layout and
+// merge as above).
+constexpr int kDecodeMaxRows = 4;
+int launch_fwd_decode(const FwdArgs& a, hipStream_t stream);
 // Workgroups of the forward kernel one CU runs at a time, by head dimension.
 int fwd_workgroups_per_cu(int D);
 int fwd_rows_per_workgroup(int D);

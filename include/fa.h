@@ -89,11 +89,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
  * The "Flash Attention" page (section on the technique's boundaries) sets
  * decoding apart: a few query rows cannot fill a matrix tile, so the
  * (query block, batch, head) grid is too small to occupy the GPU.  Here the
- * key tiles a query block sees are divided into num_splits contiguous
- * ranges, one workgroup each; every range writes the attention of its keys
- * (O normalised by its own row sum, float32) and its L_s into the
- * workspace, and a second kernel merges them exactly:
+ * keys a query block sees are divided into num_splits contiguous ranges,
+ * one workgroup each; every range writes the attention of its keys (O
+ * normalised by its own row sum, float32) and its L_s into the workspace,
+ * and a second kernel merges them exactly:
  * L = ln sum_s e^{L_s}, O = sum_s e^{L_s - L} O_s.
+ * Nq <= 4 runs a vector kernel (the pages' "separate vector kernel" for
+ * decoding; P kept in float32), larger Nq the matrix-core forward kernel
+ * (P rounded to bf16 for the P V product, as in fa_fwd).
  *
  *   num_splits      : 0 = the library's choice (fa_fwd_kv_splits), else
  *                     1..256.  1 runs without workspace or merge.
@@ -111,9 +114,11 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
               float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The key-range count fa_fwd_kv uses for num_splits = 0: enough
- * workgroups to occupy every CU of the current device, at least two key
- * tiles of 64 per range, at most 256.  Returns a count >= 1, or a negative
+ * The key-range count fa_fwd_kv uses for num_splits = 0, at most 256.  For
+ * Nq > 4 (matrix-core kernel): enough workgroups to occupy every CU of the
+ * current device, at least two key tiles of 64 per range.  For Nq <= 4
+ * (vector decode kernel): about one workgroup per CU (two for Nq > 2), at
+ * least two ranges, each over at least 256 keys.  Returns a count >= 1, or a negative
  * FA_ERR_* code for invalid sizes.  Queries the current device's CU count
  * (no device state is changed).
  */

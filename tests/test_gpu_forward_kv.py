@@ -7,8 +7,8 @@ query block holds when it is the end of the sequence).  Cases cover one
 decoded row over long key sequences, ragged lengths, fewer keys than a tile,
 more key ranges than key tiles (empty ranges), causal ranges that some rows
 of a block do not reach, more queries than keys without a mask, peaked rows,
-each head dimension, and the pages' benchmark shape with the library's own
-split count.
+each head dimension, the vector decode kernel that serves up to four query
+rows, and the pages' benchmark shape with the library's own split count.
 """
 
 import numpy as np
@@ -71,6 +71,15 @@ CASES = [
     (1, 2, 300, 100, 128, False, 3),  # more queries than keys, no mask
     (1, 2, 512, 512, 128, True, 4),  # equal lengths, split
     (1, 4, 200, 3000, 64, False, 0),
+    (1, 2, 64, 4096, 128, True, 12),  # more than 8 ranges: the wide merge
+    (2, 1, 33, 3000, 256, False, 20),
+    # up to four query rows run on the vector decode kernel
+    (1, 2, 4, 777, 64, True, 3),  # causal: the last three keys are partly masked
+    (2, 2, 2, 1500, 256, True, 0),
+    (1, 2, 3, 2049, 128, True, 1),  # one key range: O and L written directly
+    (1, 2, 2, 130, 128, False, 12),  # more ranges than 64-key chunks: empty ranges
+    (1, 1, 4, 4, 256, True, 2),  # as many keys as rows: row r sees keys 0..r
+    (3, 5, 1, 20000, 64, True, 0),
 ]
 
 

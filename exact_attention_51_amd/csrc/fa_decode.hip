@@ -216,12 +216,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(FwdArgs a) {
       if (d == 0) a.lse[orow] = (M + fast_log2(lsum)) * kLn2;
     } else {
       const size_t prow = (size_t)split * a.B * a.H * Nq + orow;
-      if (lsum > 0.f) {
-        a.part_o[prow * D + d] = osum / lsum;
-        if (d == 0) a.part_l[prow] = (M + fast_log2(lsum)) * kLn2;
-      } else if (d == 0) {
-        a.part_l[prow] = -__builtin_inff();
-      }
+      // a range the row does not reach: O_s = 0, L_s = -inf (weight 0 in the merge)
+      a.part_o[prow * D + d] = lsum > 0.f ? osum / lsum : 0.f;
+      if (d == 0) a.part_l[prow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : -__builtin_inff();
     }
   }
 }

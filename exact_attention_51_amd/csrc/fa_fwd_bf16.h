@@ -432,14 +432,20 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     t_lo = nt_q * split / a.n_split;
     t_hi = nt_q * (split + 1) / a.n_split;
     if (t_lo == t_hi) {
-      // an empty key range (fewer tiles than ranges): its rows get L = -inf,
-      // which gives the range weight 0 in the merge
-      if (wave_active && kpart == 0 && k.half == 0) {
+      // an empty key range (fewer tiles than ranges): its rows get O = 0 and
+      // L = -inf, which gives the range weight 0 in the merge
+      if (wave_active && kpart == 0) {
+        float* __restrict__ Op = a.part_o + ((size_t)split * a.B * a.H + bh) * N * D;
         float* __restrict__ Lp = a.part_l + ((size_t)split * a.B * a.H + bh) * N;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const int row = wq0 + qb * 32 + k.l32;
-          if (row < N) Lp[row] = -__builtin_inff();
+          if (row < N) {
+#pragma unroll
+            for (int c = 0; c < D / 8; ++c)
+              *(f32x4*)(Op + (size_t)row * D + c * 8 + k.half * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (k.half == 0) Lp[row] = -__builtin_inff();
+          }
         }
       }
       return;
@@ -633,7 +639,8 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   if constexpr (KV) {
     if (a.n_split > 1) {
       // one key range of several: normalised O in float32 and L of the
-      // range; a row that sees no key of the range gets L = -inf (weight 0)
+      // range; a row that sees no key of the range gets O = 0 and L = -inf
+      // (weight 0)
       float* __restrict__ Op = a.part_o + ((size_t)split * a.B * a.H + bh) * N * D;
       float* __restrict__ Lp = a.part_l + ((size_t)split * a.B * a.H + bh) * N;
 #pragma unroll
@@ -652,8 +659,11 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
                 *(f32x4*)(Op + (size_t)row * D + db * 32 + g4 * 8 + k.half * 4) = w;
               }
             if (k.half == 0) Lp[row] = k.m[qb] * a.scale + fast_log2(lt) * kLn2;
-          } else if (k.half == 0) {
-            Lp[row] = -__builtin_inff();
+          } else {
+#pragma unroll
+            for (int c = 0; c < D / 8; ++c)
+              *(f32x4*)(Op + (size_t)row * D + c * 8 + k.half * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (k.half == 0) Lp[row] = -__builtin_inff();
           }
         }
       }

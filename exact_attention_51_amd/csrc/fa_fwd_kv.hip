@@ -32,9 +32,11 @@ int launch_kv(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// One thread per four consecutive d of a row: the row's L_s of every range
-// give L, then O = sum_s e^{L_s - L} O_s (ranges of weight 0 are not read),
-// rounded to bf16.
+// One thread per four consecutive d of a row, for at most kMaxNarrow ranges:
+// the row's L_s of every range give L, then O = sum_s e^{L_s - L} O_s,
+// rounded to bf16.  Every range's loads are issued together; a range a row
+// does not reach holds O_s = 0 and L_s = -inf, so its term is exactly 0.
+constexpr int kMaxNarrow = 8;
 template <int D>
 __global__ __launch_bounds__(256) void fwd_kv_merge_kernel(FwdArgs a) {
   constexpr int kThreadsPerRow = D / 4;
@@ -46,21 +48,30 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_kernel(FwdArgs a) {
   const int S = a.n_split;
   const float* __restrict__ Lp = a.part_l + r;
   const float* __restrict__ Op = a.part_o + r * D + t * 4;
-  float mx = -__builtin_inff();
-  for (int s = 0; s < S; ++s) mx = __builtin_fmaxf(mx, Lp[(size_t)s * rows]);
-  float sum = 0.f;
-  for (int s = 0; s < S; ++s) sum += fast_exp2((Lp[(size_t)s * rows] - mx) * kLog2e);
+  float ls[kMaxNarrow];
+  f32x4 xs[kMaxNarrow];
+#pragma unroll
+  for (int s = 0; s < kMaxNarrow; ++s) {
+    ls[s] = s < S ? Lp[(size_t)s * rows] : -__builtin_inff();
+    xs[s] = s < S ? *(const f32x4*)(Op + (size_t)s * rows * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float mx = ls[0];
+#pragma unroll
+  for (int s = 1; s < kMaxNarrow; ++s) mx = __builtin_fmaxf(mx, ls[s]);
+  float w[kMaxNarrow], sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxNarrow; ++s) {
+    w[s] = fast_exp2((ls[s] - mx) * kLog2e);
+    sum += w[s];
+  }
+  const float inv = 1.0f / sum;
   const float L = mx + fast_log2(sum) * kLn2;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float w = fast_exp2((Lp[(size_t)s * rows] - L) * kLog2e);
-    if (w > 0.f) {
-      const f32x4 x = *(const f32x4*)(Op + (size_t)s * rows * D);
-      acc[0] = __builtin_fmaf(w, x[0], acc[0]);
-      acc[1] = __builtin_fmaf(w, x[1], acc[1]);
-      acc[2] = __builtin_fmaf(w, x[2], acc[2]);
-      acc[3] = __builtin_fmaf(w, x[3], acc[3]);
-    }
+#pragma unroll
+  for (int s = 0; s < kMaxNarrow; ++s) {
+    const float ws = w[s] * inv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(ws, xs[s][e], acc[e]);
   }
   const u32x2 packed = {pack_bf16_u32(acc[0], acc[1]), pack_bf16_u32(acc[2], acc[3])};
   *(u32x2*)((__bf16*)a.o + r * D + t * 4) = packed;
@@ -144,12 +155,12 @@ int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream) {
   return -2;
 }
 
-// Few ranges: one thread per 4 columns of a row walks every range.  Many
-// ranges (more than 8): one workgroup per row with the ranges spread over
+// Few ranges (at most 8): one thread per 4 columns of a row loads every
+// range at once.  Many ranges: one workgroup per row with the ranges spread over
 // its threads, so a row's loads do not form one long dependent chain.
 int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream) {
   const long rows = (long)a.B * a.H * a.N;
-  if (a.n_split > 8) {
+  if (a.n_split > fwd::kMaxNarrow) {
     const dim3 grid((unsigned)rows), block(256);
     if (a.D == 64) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<64>, grid, block, 0, stream, a);
     else if (a.D == 128) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<128>, grid, block, 0, stream, a);

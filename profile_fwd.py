@@ -226,52 +226,81 @@ def summarize_all_workloads(out: str, dest: str) -> None:
 
     bench.py runs c3, then c2, c4, c5 forward and c5 backward (whose setup
     runs one c5 forward), then the pages' shape B=2 H=4 N=2048 D=128 in both
-    masking modes; runs of one kernel instance are told apart by that order.
-    Medians skip each run's first launch."""
+    masking modes, the causal backward at the c3 shape (whose setup runs one
+    c3-shape forward), then fa_fwd_kv on the pages' shape in both masking
+    modes and on two decode shapes (one row per head: 1x8 heads over 32768
+    keys, split 32 ways, then 8x16 heads over 8192 keys, split 2 ways); runs
+    of one kernel instance are told apart by that order, and a merge kernel
+    belongs to the kernel launched just before it.  Medians skip each run's
+    first launch."""
     sys.path.insert(0, ROOT)
     from fa_inputs import WORKLOADS
 
     (path,) = glob.glob(os.path.join(out, "ktrace_all", "**", "*kernel_trace.csv"), recursive=True)
     with open(path) as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
-    seen_c2, seen_c5, runs = False, False, {}
-    for r in rows:
-        name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
-        family = name.split("(")[0]  # the name without its argument list
-        if "bwd_" in family:
-            label, seen_c5 = "c5 bwd", True
+    families = [r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0] for r in rows]
+    seen_c2, seen_c5, seen_c3_bwd, runs, last = False, False, False, {}, None
+    for i, (r, family) in enumerate(zip(rows, families)):
+        if "merge" in family:
+            label = last
+        elif "decode_kernel" in family:
+            # the run's own merge (next launch) tells the two decode shapes apart
+            nxt = families[i + 1] if i + 1 < len(families) else ""
+            label = "decode 1x8x32768 kv" if "merge_wide" in nxt else "decode 8x16x8192 kv"
+        elif "fwd_bf16_kernel" in family and family.rstrip().endswith("true>"):  # the fa_fwd_kv instances
+            label = "p1 causal fwd kv" if "<128, true" in family else "p1 fwd kv"
+        elif "bwd_" in family:
+            if "<256" in family or "d256" in family:
+                label, seen_c5 = "c5 bwd", True
+            else:
+                label, seen_c3_bwd = "c3 bwd", True
         elif "fwd_bf16_kernel<64" in family:
             label, seen_c2 = "c2 fwd", True
         elif "fwd_bf16_kernel<256" in family:
             label, seen_c5 = "c5 fwd", True
-        elif "fwd_bf16_kernel<128" in family:  # bench order: c3, c2, c4, c5, then the pages' shape
+        elif "fwd_bf16_kernel<128" in family:  # bench order: c3, c2, c4, c5, the pages' shape, c3-shape bwd
             if seen_c5:
                 label = "p1 causal fwd" if "<128, true" in family else "p1 fwd"
+                if i + 1 < len(families) and "bwd_dq" in families[i + 1]:
+                    label = "c3 bwd setup fwd"
             else:
                 label = "c4 fwd" if seen_c2 else "c3 fwd"
         else:
             continue
+        last = label
         runs.setdefault((label, family), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     p1 = WORKLOADS["c3"].with_(B=2, H=4, N=2048, D=128)
     flop = {"c2 fwd": WORKLOADS["c2"].fwd_flop(), "c3 fwd": WORKLOADS["c3"].fwd_flop(),
             "c4 fwd": WORKLOADS["c4"].fwd_flop(), "c5 fwd": WORKLOADS["c5"].fwd_flop(),
             "p1 fwd": p1.with_(causal=False).fwd_flop(), "p1 causal fwd": p1.with_(causal=True).fwd_flop()}
-    w5 = WORKLOADS["c5"]
+    flop["p1 fwd kv"], flop["p1 causal fwd kv"] = flop["p1 fwd"], flop["p1 causal fwd"]
+    kv_bytes = {"decode 1x8x32768 kv": 2 * 8 * 32768 * 128 * 2, "decode 8x16x8192 kv": 2 * 128 * 8192 * 128 * 2}
+    w5, w3 = WORKLOADS["c5"], WORKLOADS["c3"]
     per_bwd = {"bwd_dq": 6 * w5.N * w5.N * w5.D * w5.B * w5.H, "bwd_dkdv": 8 * w5.N * w5.N * w5.D * w5.B * w5.H}
+    per_bwd3 = {"bwd_dq": 3 * w3.N * w3.N * w3.D * w3.B * w3.H, "bwd_dkdv": 4 * w3.N * w3.N * w3.D * w3.B * w3.H}
     lines = ["# Kernel durations of every bench workload", "",
              "Command (repository root, GPU box): `python3 profile_fwd.py`; pass `ktrace_all` =",
              f"`rocprofv3 --kernel-trace --stats -- {' '.join(['python3', 'bench.py'] + BENCH_ALL[2:])}`.",
              "Median and minimum over the launches of each run after its first; TFLOPS from the median, with",
-             "4N²D·B·H (halved under causal) for the forward, 6N²D·B·H for dQ and 8N²D·B·H for dK/dV.", "",
-             "| workload | kernel | launches | median µs | min µs | TFLOPS |", "|---|---|---|---|---|---|"]
+             "4N²D·B·H (halved under causal) for the forward, 6N²D·B·H for dQ and 8N²D·B·H for dK/dV (halved",
+             "for the causal c3-shape backward).  Decode rows give the K/V read rate of the decode kernel",
+             "(2·B·H·Nk·D·2 bytes per launch) instead; a merge kernel is listed under the run it serves.", "",
+             "| workload | kernel | launches | median µs | min µs | TFLOPS or K/V GB/s |", "|---|---|---|---|---|---|"]
     for (label, kname), ts in runs.items():
         body = ts[1:] if len(ts) > 1 else ts
         med = statistics.median(body)
         if label == "c5 bwd":
             f = next((v for k, v in per_bwd.items() if k in kname), None)
+        elif label == "c3 bwd":
+            f = next((v for k, v in per_bwd3.items() if k in kname), None)
+        elif "merge" in kname:
+            f = None
         else:
             f = flop.get(label)
         tf = f"{f / (med * 1e-6) / 1e12:.0f}" if f else ""
+        if label in kv_bytes and "decode_kernel" in kname:
+            tf = f"{kv_bytes[label] / (med * 1e-6) / 1e9:.0f} GB/s"
         short = kname.replace("void ", "").replace("fa::", "")
         lines.append(f"| {label} | `{short}` | {len(ts)} | {med:.1f} | {min(body):.1f} | {tf} |")
     with open(os.path.join(dest, "kernels_all_workloads.md"), "w") as f:

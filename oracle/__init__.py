@@ -19,7 +19,8 @@ Modules
 attention
     ``forward`` / ``forward_rows`` (O and the per-row log-sum-exp L),
     ``forward_kv`` (the same with query and key lengths apart, causal
-    masking aligned to the last query rows),
+    masking aligned to the last query rows), ``forward_block_sparse`` (the
+    same restricted to the (query block, key block) pairs of a block mask),
     ``probabilities`` (the softmax matrix P) and ``backward`` (dQ, dK, dV
     and delta = rowsum(dO * O)).
 online
@@ -33,5 +34,5 @@ finite differences and an independent library routine
 (``scipy.special.logsumexp``).  No function here is "parity unpinned".
 """
 
-from .attention import backward, forward, forward_kv, forward_rows, probabilities  # noqa: F401
+from .attention import backward, forward, forward_block_sparse, forward_kv, forward_rows, probabilities  # noqa: F401
 from .online import online_forward  # noqa: F401

@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["probabilities", "forward_rows", "forward", "forward_kv", "backward"]
+__all__ = ["probabilities", "forward_rows", "forward", "forward_kv", "forward_block_sparse", "backward"]
 
 
 def _as_f64(x) -> np.ndarray:
@@ -168,6 +168,56 @@ def forward_kv(q, k, v, scale: float, causal: bool = False):
             p, m, l = _softmax_two_pass(s)
             o[b, h] = p @ vh
             lse[b, h] = m + np.log(l)
+    if single:
+        return o[0, 0], lse[0, 0]
+    return o, lse
+
+
+def forward_block_sparse(q, k, v, scale: float, causal: bool, block_mask, block: int = 64):
+    """Attention restricted to the (query block, key block) pairs a block mask keeps.
+
+    q, k, v: [B, H, N, D] (or [N, D]).  block_mask: array of shape
+    [nb, nb] or [B*H, nb, nb] (or [B, H, nb, nb]) with nb = ceil(N / block); a nonzero entry
+    (a, c) lets the queries of rows a*block .. a*block+block-1 see the keys
+    of rows c*block .. c*block+block-1.  With causal masking a key must in
+    addition satisfy j <= i.  Returns (O, L) in float64.
+
+    The pages name skipping whole blocks beyond the causal ones as the
+    natural extension of the tile skip (metal-flash-attention README,
+    closing sections; "Flash Attention" page, kernel anatomy) without fixing
+    a format; this is the plainest reading: the definition of ``forward``
+    with the scores of dropped blocks set to -inf.  A row that sees no key
+    at all has no softmax; it is given O = 0 and L = -inf (the limit of a
+    row whose scores all tend to -inf contributes nothing, and L = -inf
+    gives it weight 0 in any merge by log-sum-exp).
+    """
+    q = np.asarray(q)
+    single = q.ndim == 2
+    if single:
+        q, k, v = q[None, None], np.asarray(k)[None, None], np.asarray(v)[None, None]
+    else:
+        k, v = np.asarray(k), np.asarray(v)
+    b_, h_, n, d = q.shape
+    nb = -(-n // block)
+    mask = np.asarray(block_mask)
+    if mask.ndim == 2:
+        mask = np.broadcast_to(mask, (b_ * h_, nb, nb))
+    mask = mask.reshape(b_ * h_, nb, nb) != 0
+    blk = np.arange(n) // block
+    o = np.zeros((b_, h_, n, d), dtype=np.float64)
+    lse = np.full((b_, h_, n), -np.inf, dtype=np.float64)
+    for b in range(b_):
+        for h in range(h_):
+            vis = mask[b * h_ + h][blk[:, None], blk[None, :]]
+            if causal:
+                vis = vis & (np.arange(n)[None, :] <= np.arange(n)[:, None])
+            qh, kh, vh = (_as_f64(x[b, h]) for x in (q, k, v))
+            s = np.where(vis, scale * (qh @ kh.T), -np.inf)
+            rows = vis.any(axis=1)
+            if rows.any():
+                p, m, l = _softmax_two_pass(s[rows])
+                o[b, h, rows] = p @ vh
+                lse[b, h, rows] = m + np.log(l)
     if single:
         return o[0, 0], lse[0, 0]
     return o, lse

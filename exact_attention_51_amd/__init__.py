@@ -18,7 +18,7 @@ import math
 from . import _lib
 from ._lib import FAError  # noqa: F401
 
-__all__ = ["fwd", "fwd_kv", "kv_splits", "bwd_dq", "bwd_dkdv", "bwd", "FAError", "library_path", "version"]
+__all__ = ["fwd", "fwd_kv", "kv_splits", "fwd_sparse", "SPARSE_BLOCK", "bwd_dq", "bwd_dkdv", "bwd", "FAError", "library_path", "version"]
 
 
 def library_path() -> str:
@@ -156,6 +156,47 @@ def fwd_kv(q, k, v, scale: float | None = None, causal: bool = False, num_splits
         ws_ptr, ws_bytes, _stream_ptr(q, stream),
     )
     _lib.check("fa_fwd_kv", rc)
+    return out, lse
+
+
+SPARSE_BLOCK = 64  # rows of a query block and of a key block in fa_fwd_sparse's mask
+
+
+def fwd_sparse(q, k, v, block_mask, scale: float | None = None, causal: bool = False, out=None, lse=None, stream=None):
+    """``fa_fwd_sparse``: the forward restricted to the (query block, key
+    block) pairs of ``block_mask``.
+
+    block_mask: uint8 GPU tensor [nb, nb] (one mask for every head) or
+    [B, H, nb, nb] / [B*H, nb, nb] (per head), nb = ceil(N / 64); a nonzero
+    entry (a, c) lets query rows 64a.. see key rows 64c...  Rows that see no
+    key get O = 0 and L = -inf.  Returns (o, lse).
+    """
+    torch = _torch()
+    _check_bhnd("q", q, torch.bfloat16)
+    B, H, N, D = q.shape
+    _check_bhnd("k", k, torch.bfloat16, q.shape)
+    _check_bhnd("v", v, torch.bfloat16, q.shape)
+    nb = -(-N // SPARSE_BLOCK)
+    if not (isinstance(block_mask, torch.Tensor) and block_mask.is_cuda and block_mask.dtype == torch.uint8
+            and block_mask.is_contiguous()):
+        raise TypeError("block_mask must be a contiguous uint8 GPU tensor")
+    if tuple(block_mask.shape) == (nb, nb):
+        heads = 1
+    elif tuple(block_mask.shape) in ((B, H, nb, nb), (B * H, nb, nb)):
+        heads = B * H
+    else:
+        raise ValueError(f"block_mask has shape {tuple(block_mask.shape)}, expected ({nb}, {nb}) or per head")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    _check_bhnd("out", out, torch.bfloat16, q.shape)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_rows("lse", lse, (B, H, N))
+    rc = _lib.load().fa_fwd_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D, float(scale), int(bool(causal)),
+        _ptr(block_mask), heads, _stream_ptr(q, stream),
+    )
+    _lib.check("fa_fwd_sparse", rc)
     return out, lse
 
 

@@ -21,6 +21,7 @@ SIGNATURES = {
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, ctypes.c_size_t, _P]),
     "fa_fwd_kv_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "fa_fwd_sparse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P]),
     "fa_fwd_kv_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),

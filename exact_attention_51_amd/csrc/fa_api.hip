@@ -46,6 +46,8 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
   a.n_split = 1;
   a.part_o = nullptr;
   a.part_l = nullptr;
+  a.block_mask = nullptr;
+  a.mask_heads = 0;
   return a;
 }
 
@@ -158,6 +160,20 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
                                      : fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
   if (lrc == 0 && splits > 1) lrc = fa::launch_fwd_kv_merge(a, (hipStream_t)stream);
   return map_launch(lrc);
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
+                  float scale, int causal, const unsigned char* block_mask, int mask_heads, void* stream) {
+  if (!q || !k || !v || !o || !lse || !block_mask) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  if (mask_heads != 1 && (int64_t)mask_heads != (int64_t)B * H) return FA_ERR_INVALID_ARG;
+  const int64_t nb = ((int64_t)N + fa::kSparseBlock - 1) / fa::kSparseBlock;
+  if (nb > fa::kSparseMaxTiles) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, D, scale, causal);
+  a.block_mask = block_mask;
+  a.mask_heads = mask_heads;
+  return map_launch(fa::launch_fwd_bf16_sparse(a, (hipStream_t)stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int D,

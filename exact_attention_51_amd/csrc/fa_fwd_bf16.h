@@ -378,8 +378,10 @@ __device__ __forceinline__ void unrolled(int i, int n, F& f, std::integer_sequen
 // causal mask lines the queries up with the last keys), and with
 // a.n_split > 1 the key tiles of a query block divided into a.n_split
 // ranges, one workgroup each, whose results go to a.part_o / a.part_l for
-// the merge kernel.  Without KV the kernel is the square forward.
-template <int D, bool CAUSAL, int QB, int W, bool SMALL, bool KV = false>
+// the merge kernel.  SPARSE: the square forward over the key tiles a block
+// mask keeps (a.block_mask; see the list built below).  Without KV and
+// SPARSE the kernel is the square forward.
+template <int D, bool CAUSAL, int QB, int W, bool SMALL, bool KV = false, bool SPARSE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W),
                           amdgpu_waves_per_eu(FwdCfg<D, QB, W>::kWavesPerEU, FwdCfg<D, QB, W>::kWavesPerEU))) void
 fwd_bf16_kernel(FwdArgs a, TileSched sched) {
@@ -451,7 +453,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
       return;
     }
   }
-  const int nt = t_hi - t_lo;
+  int nt = t_hi - t_lo;
   const bool ragged = (Nk % kBlockN) != 0;
 
   // Processing order.  Online softmax does not depend on the order of the
@@ -466,15 +468,99 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   else if (ragged) first_masked = n_ktiles_all - 1;
   if constexpr (KV) first_masked = min(max(first_masked, t_lo), t_hi);
   const int R = t_hi - first_masked;
+
+  // Block-sparse: the list of key tiles the block processes, in LDS.  Tile
+  // t is kept if any 64-row sub-block of the query block sees it; its entry
+  // is t | (sub-blocks that see it) << 16 | (needs an elementwise mask) << 23.
+  // A tile needs the mask if some sub-block does not see it, or it is in
+  // the causal diagonal region, the ragged last tile or the single tile of
+  // a short tensor.  Kept tiles go in ascending order (the online softmax
+  // does not depend on the order).
+  constexpr int kSubBlocks = C::kBlockM / kSparseBlock;
+  static_assert(!SPARSE || (kSubBlocks >= 1 && kSubBlocks <= 7 && C::kRowsPerWave <= kSparseBlock),
+                "sub-block bits of a list entry");
+  __shared__ uint8_t sp_flags[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ uint32_t sp_list[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int sp_count[1];
+  const int sub_block = qblk * C::kRowsPerWave / kSparseBlock;  // this wave's 64-row sub-block
+  if constexpr (SPARSE) {
+    const int nb = n_ktiles_all;
+    const unsigned char* __restrict__ bm = a.block_mask + (a.mask_heads == 1 ? (size_t)0 : (size_t)bh * nb * nb);
+    const int a0 = q0 / kSparseBlock;
+    unsigned valid = 0;
+#pragma unroll
+    for (int sb = 0; sb < kSubBlocks; ++sb) valid |= (a0 + sb < nb ? 1u : 0u) << sb;
+    for (int t = tid; t < nt; t += 64 * kWaves) {
+      unsigned vis = 0;
+#pragma unroll
+      for (int sb = 0; sb < kSubBlocks; ++sb)
+        if (a0 + sb < nb && bm[(size_t)(a0 + sb) * nb + t] != 0) vis |= 1u << sb;
+      const bool needs = vis != valid || t >= first_masked;
+      sp_flags[t] = (uint8_t)(vis == 0 ? 0u : (vis | (needs ? 0x80u : 0u)));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int count = 0;
+      for (int c0 = 0; c0 < nt; c0 += 64) {
+        const int t = c0 + lane;
+        const unsigned f = t < nt ? sp_flags[t] : 0u;
+        const uint64_t kept = __builtin_amdgcn_ballot_w64(f != 0);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(kept >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kept, 0u));
+        if (f != 0) sp_list[count + below] = (uint32_t)t | (f << 16);
+        count += __builtin_popcountll(kept);
+      }
+      if (lane == 0) sp_count[0] = count;
+    }
+    __syncthreads();
+    nt = __builtin_amdgcn_readfirstlane(sp_count[0]);
+    if (nt == 0) {
+      // no key tile kept: every row sees no key, O = 0 and L = -inf
+      if (wave_active && kpart == 0) {
+        __bf16* __restrict__ O = (__bf16*)a.o + head_off;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int row = wq0 + qb * 32 + k.l32;
+          if (row < N) {
+#pragma unroll
+            for (int c = 0; c < D / 8; ++c) *(u32x2*)(O + (size_t)row * D + c * 8 + k.half * 4) = u32x2{0u, 0u};
+            if (k.half == 0) a.lse[(size_t)bh * N + row] = -__builtin_inff();
+          }
+        }
+      }
+      return;
+    }
+  }
+  // list entry of sequence position p (clamped to the last one)
+  auto sp_entry = [&](int p) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(sp_list[min(p, nt - 1)]);
+  };
+  auto needs_mask = [&](int p) -> bool {
+    if constexpr (SPARSE) return (sp_entry(p) >> 23) & 1u;
+    else return p < R;
+  };
   // tile at sequence position p (positions past the end load a valid tile
   // that is never read)
-  auto seq_tile = [&](int p) { return p < R ? first_masked + p : t_lo + p - R; };
+  auto seq_tile = [&](int p) -> int {
+    if constexpr (SPARSE) return (int)(sp_entry(p) & 0xffffu);
+    else return p < R ? first_masked + p : t_lo + p - R;
+  };
   // First row of key tile t: tiles lie inside the tensor, a ragged last
   // tile is shifted back to end at row Nk-1 (its keys below t*64 are masked).
   auto tile_row0 = [&](int t) { return SMALL ? 0 : min(min(t, n_ktiles_all - 1) * kBlockN, Nk - kBlockN); };
   auto mask_tile = [&](f32x16 (&acc)[C::kKB][QB], int p) {
     const int t = seq_tile(p);
     k.mask(acc, tile_row0(t) + kpart * 32, t * kBlockN, wq0 + off, Nk);
+    if constexpr (SPARSE) {
+      // the whole tile is invisible to this wave's sub-block
+      if (((sp_entry(p) >> (16 + sub_block)) & 1u) == 0) {
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[kb][qb][r] = -__builtin_inff();
+      }
+    }
   };
 
   // Byte offset of the tile at sequence position p within the head: the
@@ -482,7 +568,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   // clamps), in 32 bits (a head holds fewer than 2^31 elements).
   const uint32_t last_tile_bytes = (uint32_t)(Nk - kBlockN) * (D * 2);
   auto tile_bytes = [&](int p) {
-    const int t = p < R ? first_masked + p : t_lo + p - R;
+    const int t = seq_tile(p);
     return min((uint32_t)t * (kBlockN * D * 2), last_tile_bytes);
   };
 
@@ -561,7 +647,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   wait_vmcnt<kPrologueAfterK0 * C::kLoadsPerTile>();
   __syncthreads();
   k.scores(k.kbuf(0), k.s[0]);
-  if (R > 0) mask_tile(k.s[0], 0);
+  if (needs_mask(0)) mask_tile(k.s[0], 0);
   k.rowmax(k.s[0]);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) k.m[qb] = __builtin_fmaxf(k.m[qb], k.mx[qb]);  // O and l are still zero
@@ -589,7 +675,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
       issue_v(p + LV, (b + LV) % NB);
     }
     k.settle_tile(k.s[cur], c);
-    if (p + 1 < R) mask_tile(k.s[cur ^ 1], p + 1);
+    if (needs_mask(p + 1)) mask_tile(k.s[cur ^ 1], p + 1);
     k.phase_b(k.vslot(b));
   };
   for (int i = 0; i < nt; i += C::kUnroll)
@@ -675,7 +761,8 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = sum_halves(k.l[qb]);
-    const float inv = 1.0f / lt;
+    // block-sparse: a row that sees no key gets O = 0 and L = -inf
+    const float inv = SPARSE ? (lt > 0.f ? 1.0f / lt : 0.f) : 1.0f / lt;
     const int row = wq0 + qb * 32 + k.l32;
     if (row < N) {
 #pragma unroll
@@ -686,7 +773,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
                      pack_bf16_u32(k.o[qb][db][g4 * 4 + 2] * inv, k.o[qb][db][g4 * 4 + 3] * inv)};
           *(u32x2*)(O + (size_t)row * D + db * 32 + g4 * 8 + k.half * 4) = w;
         }
-      if (k.half == 0) Lse[row] = k.m[qb] * a.scale + fast_log2(lt) * kLn2;
+      if (k.half == 0) Lse[row] = (SPARSE && !(lt > 0.f)) ? -__builtin_inff() : k.m[qb] * a.scale + fast_log2(lt) * kLn2;
     }
   }
 }

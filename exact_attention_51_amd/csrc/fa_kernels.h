@@ -26,6 +26,11 @@ struct FwdArgs {
   int n_split;
   float* part_o;
   float* part_l;
+  // Block-sparse forward (fa_fwd_sparse): uint8 [mask_heads][nb][nb] with
+  // nb = ceil(N / 64); entry (a, c) != 0 lets query rows 64a.. see keys 64c..
+  // mask_heads is 1 (one mask for every head) or B*H.
+  const unsigned char* block_mask;
+  int mask_heads;
 };
 
 struct BwdArgs {
@@ -57,6 +62,11 @@ int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream);
 // ALUs, keys split over a.n_split workgroups (same partial-result layout and
 // merge as above).
 constexpr int kDecodeMaxRows = 4;
+// fa_fwd_sparse.hip: the square forward over the key tiles a block mask
+// keeps (at most kSparseMaxTiles key tiles of 64; D = 64 and 128).
+constexpr int kSparseBlock = 64;
+constexpr int kSparseMaxTiles = 4096;
+int launch_fwd_bf16_sparse(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_decode(const FwdArgs& a, hipStream_t stream);
 // Workgroups of the forward kernel one CU runs at a time, by head dimension.
 int fwd_workgroups_per_cu(int D);

@@ -132,6 +132,28 @@ int fa_fwd_kv_splits(int B, int H, int Nq, int Nk, int D, int causal);
 size_t fa_fwd_kv_workspace_bytes(int B, int H, int Nq, int D, int num_splits);
 
 /*
+ * Block-sparse forward (bf16 in and out, float32 accumulation): fa_fwd
+ * restricted to the (query block, key block) pairs a block mask keeps.
+ *   q, k, v, o, lse : as fa_fwd ([B][H][N][D] bf16, lse f32 [B][H][N])
+ *   block_mask      : DEVICE pointer, uint8 [mask_heads][nb][nb] with
+ *                     nb = ceil(N / 64); entry (a, c) != 0 lets query rows
+ *                     64a .. 64a+63 see key rows 64c .. 64c+63 (read only).
+ *   mask_heads      : 1 (one mask for every batch and head) or B*H (mask
+ *                     of head h of batch b at index b*H + h).
+ * With causal = 1 a key must also satisfy j <= i.  Key tiles no row of a
+ * workgroup may see are never loaded or multiplied: this is the causal
+ * tile skip of the "Flash Attention" page's kernel anatomy generalised to
+ * any block pattern, the extension the metal-flash-attention README names.
+ * A row that sees no key at all gets O = 0 and L = -inf (the pages do not
+ * define it; -inf gives such a row weight 0 in any log-sum-exp merge).
+ * D in {64, 128} (D = 256: FA_ERR_UNSUPPORTED; its forward kernel has no
+ * LDS left for the tile list); 1 <= N <= 4096 * 64 (FA_ERR_UNSUPPORTED
+ * above); FA_ERR_INVALID_ARG for a null mask or another mask_heads.
+ */
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
+                  float scale, int causal, const unsigned char* block_mask, int mask_heads, void* stream);
+
+/*
  * Forward, float32 in and out, float32 arithmetic throughout.  Same
  * arguments and semantics as fa_fwd.  D in {64, 128, 256}; any N >= 1.
  */

@@ -29,6 +29,7 @@ def test_header_declares_expected_entry_points():
             "fa_fwd_kv",
             "fa_fwd_kv_splits",
             "fa_fwd_kv_workspace_bytes",
+            "fa_fwd_sparse",
             "fa_bwd_dq",
             "fa_bwd_dkdv",
             "fa_strerror",
@@ -149,6 +150,28 @@ def test_forward_kv_argument_validation():
     assert lib.fa_fwd_kv_workspace_bytes(0, 3, 5, 64, 7) == 0
     assert lib.fa_fwd_kv_splits(1, 1, 0, 10, 64, 0) == inv
     assert lib.fa_fwd_kv_splits(1, 1, 10, 5, 64, 1) == inv
+
+
+def test_forward_sparse_argument_validation():
+    lib = _lib.load()
+    inv, uns = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+
+    def call(ptrs=None, mask=FAKE, heads=1, B=1, H=2, N=300, D=128, scale=0.125, causal=0):
+        ptrs = ptrs or [FAKE] * 5
+        return lib.fa_fwd_sparse(*ptrs, B, H, N, D, scale, causal, mask, heads, None)
+
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == inv
+    assert call(mask=None) == inv
+    assert call(heads=0) == inv
+    assert call(heads=3) == inv  # neither 1 nor B*H
+    assert call(N=0) == inv
+    assert call(scale=float("nan")) == inv
+    assert call(D=256) == uns
+    assert call(D=96) == uns
+    assert call(B=1, H=1, N=4096 * 64 + 1, D=64) == uns  # more key tiles than the tile list holds
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -14,7 +14,8 @@ with HIP events on the launch stream), ``cpu_baseline`` (the float64 CPU
 oracle timed on a bounded sample of the same workload) and ``others``
 (TFLOPS of the other workloads, measured the same way, and ``fa_fwd_kv``
 with split key ranges on the pages' shape and on decoding one row per head,
-where the K/V read rate against the 8 TB/s HBM peak is the figure).
+where the K/V read rate against the 8 TB/s HBM peak is the figure, and
+``fa_fwd_sparse`` at the c3 shape with two block masks).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
 """
@@ -141,6 +142,53 @@ def time_forward_kv(B, H, Nq, Nk, D, causal, seed, steps: int, warmup: int):
     e1.record(stream)
     torch.cuda.synchronize()
     return splits, e0.elapsed_time(e1) / steps, 2 * B * H * Nk * D * 2
+
+
+def sparse_band_mask(nb: int, width: int = 16):
+    """Local-window block mask: query block a sees key blocks a-width+1 .. a
+    and block 0."""
+    import numpy as np
+
+    m = np.zeros((nb, nb), np.uint8)
+    for a in range(nb):
+        m[a, max(0, a - width + 1) : a + 1] = 1
+        m[a, 0] = 1
+    return m
+
+
+def sparse_visible_pairs(m, n: int, causal: bool, block: int = 64) -> int:
+    """(query, key) pairs a block mask (and the causal mask) leaves, per head."""
+    import numpy as np
+
+    sizes = np.minimum(block, n - np.arange(m.shape[0]) * block)
+    full = sizes[:, None] * sizes[None, :]
+    if causal:
+        diag = sizes * (sizes + 1) // 2
+        tri = np.tril(np.ones_like(m), -1)
+        return int((m * tri * full).sum() + (np.diag(m) * diag).sum())
+    return int((m * full).sum())
+
+
+def time_forward_sparse(w, q, k, v, mask, steps: int, warmup: int):
+    """Mean HIP-event ms per ``fa_fwd_sparse`` call."""
+    import torch
+
+    import exact_attention_51_amd as fa
+
+    mk = torch.from_numpy(mask).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    for _ in range(warmup):
+        fa.fwd_sparse(q, k, v, mk, w.scale, w.causal, out=o, lse=lse)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fa.fwd_sparse(q, k, v, mk, w.scale, w.causal, out=o, lse=lse, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def time_backward(w, q, k, v, steps: int, warmup: int):
@@ -301,6 +349,29 @@ def main() -> int:
                     others[f"{name}_bwd"] = {"error": str(e)}
             del qo, ko, vo
             torch.cuda.empty_cache()
+
+        # fa_fwd_sparse at the c3 shape: a local window of 16 key blocks plus
+        # block 0, and a random half of the blocks; TFLOPS count only the
+        # (query, key) pairs the masks leave (4 D FLOP each)
+        import numpy as np
+
+        w3 = WORKLOADS["c3"]
+        q3, k3, v3 = q, k, v
+        nb3 = -(-w3.N // 64)
+        for name, mask in (
+            ("c3_sparse_window16_fwd", sparse_band_mask(nb3)),
+            ("c3_sparse_random50_fwd", (np.random.default_rng(8).random((nb3, nb3)) < 0.5).astype(np.uint8)),
+        ):
+            try:
+                ms = time_forward_sparse(w3, q3, k3, v3, mask, args.steps, max(1, args.warmup // 2))
+                pairs = sparse_visible_pairs(mask, w3.N, w3.causal) * w3.B * w3.H
+                tf = 4 * pairs * w3.D / (ms * 1e-3) / 1e12
+                dense = w3.B * w3.H * w3.N * (w3.N + 1) // 2
+                others[name] = {"ms": round(ms, 5), "tflops_visible": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                                "visible_fraction_of_causal": round(pairs / dense, 4)}
+                log(f"bench: {name} {ms:.4f} ms -> {tf:.1f} TFLOPS on the visible pairs ({pairs / dense:.3f} of causal)")
+            except fa.FAError as e:
+                others[name] = {"error": str(e)}
 
         # fa_fwd_kv at the library's split count: the pages' shape (its
         # 64 query blocks leave most CUs idle unsplit) and one decoded row

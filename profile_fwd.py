@@ -104,6 +104,16 @@ def kernel_source_hash() -> str:
     return bench.kernel_source_hash()
 
 
+def collected_source_hash(out: str) -> str:
+    """The kernel source hash recorded when the traffic counters were taken
+    (not the hash of the sources at summary time, which may be newer)."""
+    try:
+        with open(os.path.join(out, "traffic_source_hash.txt")) as f:
+            return f.read().strip()
+    except OSError:
+        return "unknown"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--copy", type=int, default=0, help="calibration workload: copy this many bytes")
@@ -121,6 +131,9 @@ def main() -> int:
         me = [sys.executable, os.path.abspath(__file__)]
         if "ktrace" in passes:
             run(cmd_kernel_trace(), 600)  # 1. kernel trace with per-kernel statistics
+        if "traffic" in passes:
+            with open(os.path.join(OUT, "traffic_source_hash.txt"), "w") as f:
+                f.write(kernel_source_hash() + "\n")
         for ctr in ("FETCH_SIZE", "WRITE_SIZE") if "traffic" in passes else ():  # 2. forward, then copy
             run(["rocprofv3", "--pmc", ctr, "--kernel-include-regex", FWD_KERNEL, "--output-format", "csv", "-d",
                  os.path.join(OUT, f"fwd_{ctr}"), "-o", "run", "--", *BENCH], 300)
@@ -166,7 +179,7 @@ def summarize(out: str, dest: str) -> None:
     rec = {
         "kernel": FWD_KERNEL,
         "workload": "causal forward B=2 H=16 N=8192 D=128 bf16",
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": collected_source_hash(out),
         "bytes_per_launch": round(total),
         "fetch_bytes": round(fetch_b),
         "write_bytes": round(write_b),
@@ -227,7 +240,10 @@ def summarize_all_workloads(out: str, dest: str) -> None:
     bench.py runs c3, then c2, c4, c5 forward and c5 backward (whose setup
     runs one c5 forward), then the pages' shape B=2 H=4 N=2048 D=128 in both
     masking modes, the causal backward at the c3 shape (whose setup runs one
-    c3-shape forward), then fa_fwd_kv on the pages' shape in both masking
+    c3-shape forward), then fa_fwd_sparse at the c3 shape with a window of
+    16 key blocks and with a random half of the blocks (the same kernel
+    instance: the first half of its launches is the window run), then
+    fa_fwd_kv on the pages' shape in both masking
     modes and on two decode shapes (one row per head: 1x8 heads over 32768
     keys, split 32 ways, then 8x16 heads over 8192 keys, split 2 ways); runs
     of one kernel instance are told apart by that order, and a merge kernel
@@ -240,15 +256,29 @@ def summarize_all_workloads(out: str, dest: str) -> None:
     with open(path) as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
     families = [r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0] for r in rows]
-    seen_c2, seen_c5, seen_c3_bwd, runs, last = False, False, False, {}, None
+
+    def targs(family):  # template arguments of a forward kernel instance
+        return family[family.index("<") + 1 : family.rindex(">")].split(", ") if "<" in family else []
+
+    def is_kv(family):
+        return "fwd_bf16_kernel" in family and len(targs(family)) >= 6 and targs(family)[5] == "true"
+
+    def is_sparse(family):
+        return "fwd_bf16_kernel" in family and len(targs(family)) >= 7 and targs(family)[6] == "true"
+
+    n_sparse = sum(is_sparse(f) for f in families)
+    seen_c2, seen_c5, seen_c3_bwd, runs, last, i_sparse = False, False, False, {}, None, 0
     for i, (r, family) in enumerate(zip(rows, families)):
-        if "merge" in family:
+        if is_sparse(family):
+            label = "c3 sparse window16" if i_sparse < n_sparse // 2 else "c3 sparse random50"
+            i_sparse += 1
+        elif "merge" in family:
             label = last
         elif "decode_kernel" in family:
             # the run's own merge (next launch) tells the two decode shapes apart
             nxt = families[i + 1] if i + 1 < len(families) else ""
             label = "decode 1x8x32768 kv" if "merge_wide" in nxt else "decode 8x16x8192 kv"
-        elif "fwd_bf16_kernel" in family and family.rstrip().endswith("true>"):  # the fa_fwd_kv instances
+        elif is_kv(family):  # the fa_fwd_kv instances
             label = "p1 causal fwd kv" if "<128, true" in family else "p1 fwd kv"
         elif "bwd_" in family:
             if "<256" in family or "d256" in family:
@@ -275,6 +305,14 @@ def summarize_all_workloads(out: str, dest: str) -> None:
             "c4 fwd": WORKLOADS["c4"].fwd_flop(), "c5 fwd": WORKLOADS["c5"].fwd_flop(),
             "p1 fwd": p1.with_(causal=False).fwd_flop(), "p1 causal fwd": p1.with_(causal=True).fwd_flop()}
     flop["p1 fwd kv"], flop["p1 causal fwd kv"] = flop["p1 fwd"], flop["p1 causal fwd"]
+    import bench
+    import numpy as np
+
+    w3 = WORKLOADS["c3"]
+    nb3 = w3.N // 64
+    for lab, m in (("c3 sparse window16", bench.sparse_band_mask(nb3)),
+                   ("c3 sparse random50", (np.random.default_rng(8).random((nb3, nb3)) < 0.5).astype(np.uint8))):
+        flop[lab] = 4 * w3.D * w3.B * w3.H * bench.sparse_visible_pairs(m, w3.N, True)
     kv_bytes = {"decode 1x8x32768 kv": 2 * 8 * 32768 * 128 * 2, "decode 8x16x8192 kv": 2 * 128 * 8192 * 128 * 2}
     w5, w3 = WORKLOADS["c5"], WORKLOADS["c3"]
     per_bwd = {"bwd_dq": 6 * w5.N * w5.N * w5.D * w5.B * w5.H, "bwd_dkdv": 8 * w5.N * w5.N * w5.D * w5.B * w5.H}
@@ -284,7 +322,8 @@ def summarize_all_workloads(out: str, dest: str) -> None:
              f"`rocprofv3 --kernel-trace --stats -- {' '.join(['python3', 'bench.py'] + BENCH_ALL[2:])}`.",
              "Median and minimum over the launches of each run after its first; TFLOPS from the median, with",
              "4N²D·B·H (halved under causal) for the forward, 6N²D·B·H for dQ and 8N²D·B·H for dK/dV (halved",
-             "for the causal c3-shape backward).  Decode rows give the K/V read rate of the decode kernel",
+             "for the causal c3-shape backward), and for the block-sparse rows 4D per (query, key) pair the",
+             "block and causal masks leave.  Decode rows give the K/V read rate of the decode kernel",
              "(2·B·H·Nk·D·2 bytes per launch) instead; a merge kernel is listed under the run it serves.", "",
              "| workload | kernel | launches | median µs | min µs | TFLOPS or K/V GB/s |", "|---|---|---|---|---|---|"]
     for (label, kname), ts in runs.items():
@@ -398,7 +437,7 @@ def summarize_counters(out: str, dest: str) -> None:
               f"- waves per dispatch: {med[('sq2', 'SQ_WAVES')]:.0f}",
               *tcc_lines(med),
               *build_metadata_lines(),
-              f"- kernel source hash: {kernel_source_hash()}"]
+              f"- kernel source hash: {collected_source_hash(out)}"]
     with open(os.path.join(dest, "fwd_bf16_c3_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)

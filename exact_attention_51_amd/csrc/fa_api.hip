@@ -17,7 +17,9 @@ int check_common(int B, int H, int N, int D, float scale, int causal) {
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   const int64_t elems = (int64_t)B * H * N * D;
   if (elems > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  // head dims some kernel serves; each launcher returns "unsupported" for
+  // the ones it does not (the backward and the float32 forward: 64, 128, 256)
+  if (D != 64 && D != 96 && D != 128 && D != 160 && D != 256) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -53,6 +55,11 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
 
 constexpr int kMaxSplits = 256;
 
+// The vector decode kernel serves up to kDecodeMaxRows rows at D = 64, 128,
+// 256 (a K row split over D/8 lanes must divide the wave); the rest runs on
+// the matrix-core kernel.
+bool use_decode(int Nq, int D) { return Nq <= fa::kDecodeMaxRows && (D == 64 || D == 128 || D == 256); }
+
 // Key ranges per query block when the caller leaves the choice to the
 // library.  Matrix-core path: enough (query block, key range) workgroups to
 // give every CU its share of workgroups at once, and at least two key tiles
@@ -64,7 +71,7 @@ int choose_splits(int B, int H, int Nq, int Nk, int D) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (Nq <= fa::kDecodeMaxRows) {
+  if (use_decode(Nq, D)) {
     const int64_t heads = (int64_t)B * H;
     int64_t s = (cus + heads - 1) / heads;
     if (s < 2) s = 2;
@@ -112,7 +119,8 @@ const char* fa_strerror(int code) {
     case FA_ERR_INVALID_ARG:
       return "invalid argument (null pointer, non-positive size, bad scale or causal flag, or size overflow)";
     case FA_ERR_UNSUPPORTED:
-      return "unsupported shape (head dimension must be 64, 128 or 256)";
+      return "unsupported shape (head dimension: 64, 96, 128, 160 or 256 for the bf16 forward, 64, 128 or 256 "
+             "elsewhere; 64, 96 or 128 for the block-sparse forward)";
     case FA_ERR_LAUNCH:
       return "kernel launch failed";
     default:
@@ -156,8 +164,8 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
     a.part_o = (float*)workspace;
     a.part_l = (float*)workspace + (size_t)splits * B * H * Nq * D;
   }
-  int lrc = Nq <= fa::kDecodeMaxRows ? fa::launch_fwd_decode(a, (hipStream_t)stream)
-                                     : fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
+  int lrc = use_decode(Nq, D) ? fa::launch_fwd_decode(a, (hipStream_t)stream)
+                              : fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
   if (lrc == 0 && splits > 1) lrc = fa::launch_fwd_kv_merge(a, (hipStream_t)stream);
   return map_launch(lrc);
 }

@@ -86,7 +86,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
   // K/V tile t into ring slot b: scalar-base copies with loop-invariant
   // per-lane offsets, rows clamped onto N-1 only for a ragged last tile
-  RowTileCopier<D, kKeyTile, kWavesQ> cp;
+  RowTileCopier<D, D, kKeyTile, kWavesQ> cp;
   cp.init(wave, lane);
   auto copy_tile = [&](int t, int b) {
     const int row0 = t * kKeyTile;

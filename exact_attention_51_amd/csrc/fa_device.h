@@ -213,10 +213,14 @@ __device__ __forceinline__ void copy_rows_lds(const __bf16* __restrict__ src, in
 // starting at a uniform row go to a swizzled LDS tile with a scalar base per
 // copy.  Callers keep every tile inside the tensor (a ragged last tile is
 // taken shifted back so that it ends at row N-1); only tensors shorter than
-// a tile need per-lane clamping.
-template <int D, int ROWS, int WAVES>
+// a tile need per-lane clamping.  The LDS rows are DP >= D wide (DP in
+// {64, 128, 256}); a slot whose chunk lies past D (D = 96, 160) copies the
+// row's first chunk again into the unused part of the LDS row, so every
+// lane of a copy stays inside the global row.
+template <int D, int DP, int ROWS, int WAVES>
 struct RowTileCopier {
-  static constexpr int kRowChunks = D / 8;
+  static_assert(D <= DP && D % 8 == 0, "row widths");
+  static constexpr int kRowChunks = DP / 8;
   static constexpr int kChunksPerWave = ROWS * kRowChunks / WAVES;
   static constexpr int kLoads = kChunksPerWave / 64;
   static_assert(kChunksPerWave % 64 == 0, "tile must split into whole wave loads");
@@ -232,7 +236,8 @@ struct RowTileCopier {
     for (int i = 0; i < kLoads; ++i) {
       const int slot = wave_slot0 + i * 64 + lane;
       const int r = slot / kRowChunks;
-      const int c = (slot % kRowChunks) ^ swz<D>(r);
+      int c = (slot % kRowChunks) ^ swz<DP>(r);
+      c = c < D / 8 ? c : 0;
       rowi[i] = r;
       off[i] = (uint32_t)((r * D + c * 8) * 2);
     }

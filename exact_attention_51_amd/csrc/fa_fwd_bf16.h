@@ -66,22 +66,27 @@ template <int D, int QB, int W>
 struct FwdCfg {
   static constexpr int kWaves = W;                       // waves per workgroup (4 or 8)
   static constexpr int kRowsPerWave = 32 * QB;
+  // Row width of the LDS tiles: D rounded up to 64, 128 or 256.  D = 96 and
+  // D = 160 keep the layout (and swizzle) of D = 128 and D = 256 with the
+  // chunks past D unused; global rows are D wide.
+  static constexpr int kDP = D <= 64 ? 64 : D <= 128 ? 128 : 256;
+  static_assert(D % 32 == 0 && D <= 256, "head dimension");
   // Key split: with kSplit = 2 the two 32-key halves of every tile go to two
   // waves that own the same query rows; their partial results are merged
   // at the end.  D = 256 uses it: its work is B*H*N/32 waves of 32 rows,
   // which without the split fills only half of the SIMDs at the sizes of
   // interest (and it halves the score registers of a wave).
-  static constexpr int kSplit = D == 256 ? 2 : 1;
+  static constexpr int kSplit = kDP == 256 ? 2 : 1;
   static constexpr int kKB = 2 / kSplit;                 // 32-key blocks a wave takes per tile
   static constexpr int kQBlocks = kWaves / kSplit;       // waves with distinct query rows
   static constexpr int kBlockM = kQBlocks * kRowsPerWave;  // query rows per workgroup
   static constexpr int kDSteps = D / 16;                 // k-steps of the S product
   static constexpr int kDBlocks = D / 32;                // 32-wide d blocks of O
-  static constexpr int kTileBytes = kBlockN * D * 2;     // one K or V tile
+  static constexpr int kTileBytes = kBlockN * kDP * 2;   // one K or V tile in LDS
   // K/V ring: kNB slots each; K of position p is issued kLeadK steps
   // before the step that first reads it, V kLeadV steps before.  Step p
   // reads K(p+1) and V(p) and refills the slots of K(p) and V(p-1).
-  static constexpr int kNB = D == 128 ? 4 : 2;
+  static constexpr int kNB = kDP == 128 ? 4 : 2;
   static constexpr int kLeadK = kNB;
   static constexpr int kLeadV = kNB - 1;
   static constexpr int kRingBytes = 2 * kNB * kTileBytes;
@@ -91,8 +96,8 @@ struct FwdCfg {
 #ifndef FA_FWD_QLDS
 #define FA_FWD_QLDS 1
 #endif
-  static constexpr bool kQInLds = D == 256 && FA_FWD_QLDS;
-  static constexpr int kQBytes = kQInLds ? kQBlocks * 32 * QB * D * 2 : 0;
+  static constexpr bool kQInLds = kDP == 256 && FA_FWD_QLDS;
+  static constexpr int kQBytes = kQInLds ? kQBlocks * 32 * QB * kDP * 2 : 0;
   static constexpr int kLdsBytes = kRingBytes + kQBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
   static_assert(!kQInLds || QB == 1, "Q fragments from LDS are read for one 32-row block");
@@ -117,7 +122,7 @@ struct FwdCfg {
   // 128, ring of 4) after phase A, which keeps the copies' address and M0
   // set-up off the path from the barrier to the first score MFMAs.  The
   // 2-slot ring of D = 256 cannot spare the half step of lead.
-  static constexpr bool kLateRefill = D == 128;
+  static constexpr bool kLateRefill = kDP == 128;
 };
 
 template <int D, bool CAUSAL, int QB, int W>
@@ -153,7 +158,7 @@ struct FwdKernel {
     for (int ds = 0; ds < C::kDSteps; ++ds)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[ds] + kb * 32 * D * 2);
+        const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[ds] + kb * 32 * C::kDP * 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[kb][qb] = mfma32(kf, qfrag(qb, ds), ds == 0 ? f32x16{} : acc[kb][qb]);
       }
@@ -292,12 +297,12 @@ struct FwdKernel {
 
   // K fragment i = (ds, kb) = (i / KB, i % KB)
   __device__ __forceinline__ bf16x8 kfrag(const lds_char* kt, int i) const {
-    return *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[i / KB] + (i % KB) * 32 * D * 2);
+    return *(const bf16x8 __attribute__((address_space(3)))*)(kt + koff[i / KB] + (i % KB) * 32 * C::kDP * 2);
   }
   // V fragment j = (kb, cc, db): (kb, cc) = j / kDBlocks, db = j % kDBlocks
   __device__ __forceinline__ bf16x8 vfrag(const lds_char* vt, int j) const {
     const int kc = j / C::kDBlocks, db = j % C::kDBlocks;
-    const int rows = ((kc >> 1) * 32 + (kc & 1) * 16) * D * 2;
+    const int rows = ((kc >> 1) * 32 + (kc & 1) * 16) * C::kDP * 2;
     const s16x4 va = ds_read_tr(vt + voff[db][0] + rows);
     const s16x4 vb = ds_read_tr(vt + voff[db][1] + rows);
     const s16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
@@ -573,7 +578,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   };
 
   // K and V of sequence position p go to ring slot p % NB.
-  RowTileCopier<D, kBlockN, kWaves> cp;
+  RowTileCopier<D, C::kDP, kBlockN, kWaves> cp;
   cp.init(wave, lane);
   auto issue_k = [&](int p, int b) {
     if constexpr (SMALL) cp.copy_clamped(K, Nk, 0, k.kbuf(b));
@@ -591,7 +596,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
   if constexpr (C::kQInLds) {
     // this workgroup's query rows (clamped onto N-1) go to LDS after the
     // ring, oldest of the prologue copies so the first wait covers them
-    RowTileCopier<D, C::kBlockM, kWaves> qcp;
+    RowTileCopier<D, C::kDP, C::kBlockM, kWaves> qcp;
     qcp.init(wave, lane);
     qcp.copy_clamped(Q, N, q0, k.smem + C::kRingBytes);
   }
@@ -609,7 +614,7 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
 
   // per-lane loop-invariant LDS offsets (row offsets of kb/cc blocks keep the swizzle)
 #pragma unroll
-  for (int ds = 0; ds < C::kDSteps; ++ds) k.koff[ds] = lds_off_bytes<D>(kpart * 32 + k.l32, ds * 2 + k.half);
+  for (int ds = 0; ds < C::kDSteps; ++ds) k.koff[ds] = lds_off_bytes<C::kDP>(kpart * 32 + k.l32, ds * 2 + k.half);
   {
     const int g = lane >> 4, j16 = lane & 15;
 #pragma unroll
@@ -618,13 +623,13 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
       const int r1 = kpart * 32 + k.half * 4 + (j16 >> 2);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        k.voff[db][t] = NB * C::kTileBytes + lds_off_bytes<D>(r1 + 8 * t, dcol >> 3) + (dcol & 7) * 2;
+        k.voff[db][t] = NB * C::kTileBytes + lds_off_bytes<C::kDP>(r1 + 8 * t, dcol >> 3) + (dcol & 7) * 2;
     }
   }
 
   if constexpr (C::kQInLds) {
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) k.qoff[ds] = C::kRingBytes + lds_off_bytes<D>(qblk * 32 + k.l32, ds * 2 + k.half);
+    for (int ds = 0; ds < 8; ++ds) k.qoff[ds] = C::kRingBytes + lds_off_bytes<C::kDP>(qblk * 32 + k.l32, ds * 2 + k.half);
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {

@@ -22,7 +22,10 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace fwd
 
+// D = 256, and D = 160 with the same workgroup shape and LDS layout (96
+// columns of each LDS row unused).
 int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream) {
+  if (a.D == 160) return a.causal ? fwd::launch<160, true, 1, 4>(a, stream) : fwd::launch<160, false, 1, 4>(a, stream);
   return a.causal ? fwd::launch<256, true, 1, 4>(a, stream) : fwd::launch<256, false, 1, 4>(a, stream);
 }
 

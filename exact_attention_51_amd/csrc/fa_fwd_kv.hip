@@ -41,6 +41,7 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_kv_merge_kernel(FwdArgs a) {
   constexpr int kThreadsPerRow = D / 4;
   constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  if (threadIdx.x >= kRowsPerBlock * kThreadsPerRow) return;  // threads past the last whole row
   const long rows = (long)a.B * a.H * a.N;
   const long r = (long)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
   if (r >= rows) return;
@@ -90,13 +91,15 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
   __shared__ f32x4 ored[kP][kThreadsPerRow];
   const long rows = (long)a.B * a.H * a.N;
   const long r = blockIdx.x;
+  // threads past kP whole groups (D/4 need not divide 256) take no range
+  const bool in_group = threadIdx.x < kP * kThreadsPerRow;
   const int t = threadIdx.x % kThreadsPerRow, p = threadIdx.x / kThreadsPerRow;
-  const int S = a.n_split;
+  const int S = in_group ? a.n_split : 0;  // no range for threads outside the groups
   const float* __restrict__ Lp = a.part_l + r;
   const float* __restrict__ Op = a.part_o + r * D + t * 4;
   float mx = -__builtin_inff();
   for (int s = p; s < S; s += kP) mx = __builtin_fmaxf(mx, Lp[(size_t)s * rows]);
-  if (t == 0) red[p] = mx;
+  if (t == 0 && in_group) red[p] = mx;
   __syncthreads();
   mx = red[0];
 #pragma unroll
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
   __syncthreads();
   float sum = 0.f;
   for (int s = p; s < S; s += kP) sum += fast_exp2((Lp[(size_t)s * rows] - mx) * kLog2e);
-  if (t == 0) red[p] = sum;
+  if (t == 0 && in_group) red[p] = sum;
   __syncthreads();
   sum = 0.f;
 #pragma unroll
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
       acc[3] = __builtin_fmaf(w, x[3], acc[3]);
     }
   }
-  ored[p][t] = acc;
+  if (in_group) ored[p][t] = acc;
   __syncthreads();
   if (p != 0) return;
 #pragma unroll
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
 int fwd_workgroups_per_cu(int D) { return D == 64 ? 3 : 1; }
 int fwd_rows_per_workgroup(int D) {
   if (D == 64) return fwd::FwdCfg<64, 1, 4>::kBlockM;
-  if (D == 128) return fwd::FwdCfg<128, 1, 8>::kBlockM;
+  if (D == 96 || D == 128) return fwd::FwdCfg<128, 1, 8>::kBlockM;
   return fwd::FwdCfg<256, 1, 4>::kBlockM;
 }
 
@@ -151,7 +154,8 @@ int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream) {
   if (a.D == 64) return a.causal ? fwd::launch_kv<64, true, 1, 4>(a, stream) : fwd::launch_kv<64, false, 1, 4>(a, stream);
   if (a.D == 128)
     return a.causal ? fwd::launch_kv<128, true, 1, 8>(a, stream) : fwd::launch_kv<128, false, 1, 8>(a, stream);
-  if (a.D == 256) return launch_fwd_bf16_kv_d256(a, stream);
+  if (a.D == 96) return a.causal ? fwd::launch_kv<96, true, 1, 8>(a, stream) : fwd::launch_kv<96, false, 1, 8>(a, stream);
+  if (a.D == 256 || a.D == 160) return launch_fwd_bf16_kv_d256(a, stream);
   return -2;
 }
 
@@ -163,7 +167,9 @@ int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream) {
   if (a.n_split > fwd::kMaxNarrow) {
     const dim3 grid((unsigned)rows), block(256);
     if (a.D == 64) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<64>, grid, block, 0, stream, a);
+    else if (a.D == 96) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<96>, grid, block, 0, stream, a);
     else if (a.D == 128) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<128>, grid, block, 0, stream, a);
+    else if (a.D == 160) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<160>, grid, block, 0, stream, a);
     else if (a.D == 256) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<256>, grid, block, 0, stream, a);
     else return -2;
     return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -174,7 +180,9 @@ int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
   };
   if (a.D == 64) return go(fwd::fwd_kv_merge_kernel<64>, 256 / 16);
+  if (a.D == 96) return go(fwd::fwd_kv_merge_kernel<96>, 256 / 24);
   if (a.D == 128) return go(fwd::fwd_kv_merge_kernel<128>, 256 / 32);
+  if (a.D == 160) return go(fwd::fwd_kv_merge_kernel<160>, 256 / 40);
   if (a.D == 256) return go(fwd::fwd_kv_merge_kernel<256>, 256 / 64);
   return -2;
 }

@@ -80,6 +80,12 @@ CASES = [
     (1, 2, 2, 130, 128, False, 12),  # more ranges than 64-key chunks: empty ranges
     (1, 1, 4, 4, 256, True, 2),  # as many keys as rows: row r sees keys 0..r
     (3, 5, 1, 20000, 64, True, 0),
+    # head dims 96 and 160 (matrix-core kernel also for up to four rows)
+    (1, 2, 300, 1000, 96, True, 6),
+    (1, 2, 2, 3000, 96, True, 0),
+    (1, 2, 130, 700, 160, True, 4),
+    (2, 1, 1, 5000, 160, False, 0),
+    (1, 2, 40, 3000, 160, False, 12),
 ]
 
 

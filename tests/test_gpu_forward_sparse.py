@@ -78,6 +78,8 @@ CASES = [
     (1, 2, 2048, 128, True, "ones", False),
     (1, 2, 2048, 128, False, "rand0.1", False),
     (1, 1, 300, 128, False, "rand0.0", False),  # nothing kept: O = 0, L = -inf everywhere
+    (1, 2, 1000, 96, True, "rand0.5", True),
+    (1, 2, 777, 96, False, "band", False),
 ]
 
 

@@ -19,7 +19,7 @@ int check_common(int B, int H, int N, int D, float scale, int causal) {
   if (elems > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
   // head dims some kernel serves; each launcher returns "unsupported" for
   // the ones it does not (the backward and the float32 forward: 64, 128, 256)
-  if (D != 64 && D != 96 && D != 128 && D != 160 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 96 && D != 128 && D != 160 && D != 256) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -119,8 +119,8 @@ const char* fa_strerror(int code) {
     case FA_ERR_INVALID_ARG:
       return "invalid argument (null pointer, non-positive size, bad scale or causal flag, or size overflow)";
     case FA_ERR_UNSUPPORTED:
-      return "unsupported shape (head dimension: 64, 96, 128, 160 or 256 for the bf16 forward, 64, 128 or 256 "
-             "elsewhere; 64, 96 or 128 for the block-sparse forward)";
+      return "unsupported shape (head dimension: 32, 64, 96, 128, 160 or 256 for the bf16 forward, 64, 128 or "
+             "256 elsewhere; 32, 64, 96 or 128 for the block-sparse forward)";
     case FA_ERR_LAUNCH:
       return "kernel launch failed";
     default:

@@ -66,8 +66,8 @@ template <int D, int QB, int W>
 struct FwdCfg {
   static constexpr int kWaves = W;                       // waves per workgroup (4 or 8)
   static constexpr int kRowsPerWave = 32 * QB;
-  // Row width of the LDS tiles: D rounded up to 64, 128 or 256.  D = 96 and
-  // D = 160 keep the layout (and swizzle) of D = 128 and D = 256 with the
+  // Row width of the LDS tiles: D rounded up to 64, 128 or 256.  D = 32, 96
+  // and 160 keep the layout (and swizzle) of D = 64, 128 and 256 with the
   // chunks past D unused; global rows are D wide.
   static constexpr int kDP = D <= 64 ? 64 : D <= 128 ? 128 : 256;
   static_assert(D % 32 == 0 && D <= 256, "head dimension");
@@ -117,7 +117,7 @@ struct FwdCfg {
   // three 4-wave workgroups share a CU (32 KB ring each) and the third wave
   // per SIMD hides more of the exponentials, which at D = 64 cost as much
   // issue time as the MFMAs; one for D = 256 (4 waves, 128 KB ring).
-  static constexpr int kWavesPerEU = D == 64 ? 3 : W == 8 ? 2 : 1;
+  static constexpr int kWavesPerEU = kDP == 64 ? 3 : W == 8 ? 2 : 1;
   // Where a step issues its ring refills: right after its barrier, or (D =
   // 128, ring of 4) after phase A, which keeps the copies' address and M0
   // set-up off the path from the barrier to the first score MFMAs.  The

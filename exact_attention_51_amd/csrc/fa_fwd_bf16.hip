@@ -31,6 +31,8 @@ int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   constexpr int QB = 1, W64 = 4, W128 = 8;
   if (a.D == 64) return a.causal ? fwd::launch<64, true, QB, W64>(a, stream) : fwd::launch<64, false, QB, W64>(a, stream);
+  if (a.D == 32)  // the D = 64 workgroup shape and LDS layout, 32 columns unused
+    return a.causal ? fwd::launch<32, true, QB, W64>(a, stream) : fwd::launch<32, false, QB, W64>(a, stream);
   if (a.D == 128)
     return a.causal ? fwd::launch<128, true, QB, W128>(a, stream) : fwd::launch<128, false, QB, W128>(a, stream);
   if (a.D == 96)  // the D = 128 workgroup shape and LDS layout, 32 columns unused

@@ -142,9 +142,9 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
 
 }  // namespace fwd
 
-int fwd_workgroups_per_cu(int D) { return D == 64 ? 3 : 1; }
+int fwd_workgroups_per_cu(int D) { return D <= 64 ? 3 : 1; }
 int fwd_rows_per_workgroup(int D) {
-  if (D == 64) return fwd::FwdCfg<64, 1, 4>::kBlockM;
+  if (D <= 64) return fwd::FwdCfg<64, 1, 4>::kBlockM;
   if (D == 96 || D == 128) return fwd::FwdCfg<128, 1, 8>::kBlockM;
   return fwd::FwdCfg<256, 1, 4>::kBlockM;
 }
@@ -155,6 +155,7 @@ int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream) {
   if (a.D == 128)
     return a.causal ? fwd::launch_kv<128, true, 1, 8>(a, stream) : fwd::launch_kv<128, false, 1, 8>(a, stream);
   if (a.D == 96) return a.causal ? fwd::launch_kv<96, true, 1, 8>(a, stream) : fwd::launch_kv<96, false, 1, 8>(a, stream);
+  if (a.D == 32) return a.causal ? fwd::launch_kv<32, true, 1, 4>(a, stream) : fwd::launch_kv<32, false, 1, 4>(a, stream);
   if (a.D == 256 || a.D == 160) return launch_fwd_bf16_kv_d256(a, stream);
   return -2;
 }
@@ -166,7 +167,8 @@ int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream) {
   const long rows = (long)a.B * a.H * a.N;
   if (a.n_split > fwd::kMaxNarrow) {
     const dim3 grid((unsigned)rows), block(256);
-    if (a.D == 64) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<64>, grid, block, 0, stream, a);
+    if (a.D == 32) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<32>, grid, block, 0, stream, a);
+    else if (a.D == 64) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<64>, grid, block, 0, stream, a);
     else if (a.D == 96) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<96>, grid, block, 0, stream, a);
     else if (a.D == 128) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<128>, grid, block, 0, stream, a);
     else if (a.D == 160) hipLaunchKernelGGL(fwd::fwd_kv_merge_wide_kernel<160>, grid, block, 0, stream, a);
@@ -179,6 +181,7 @@ int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   };
+  if (a.D == 32) return go(fwd::fwd_kv_merge_kernel<32>, 256 / 8);
   if (a.D == 64) return go(fwd::fwd_kv_merge_kernel<64>, 256 / 16);
   if (a.D == 96) return go(fwd::fwd_kv_merge_kernel<96>, 256 / 24);
   if (a.D == 128) return go(fwd::fwd_kv_merge_kernel<128>, 256 / 32);

@@ -1,5 +1,5 @@
-// fa_fwd_sparse.hip -- block-sparse forward instances for D = 64, 96 and
-// 128.  (The D = 160 and D = 256 forward fills all 160 KB of LDS with its
+// fa_fwd_sparse.hip -- block-sparse forward instances for D = 32, 64, 96
+// and 128.  (The D = 160 and D = 256 forward fills all 160 KB of LDS with its
 // K/V ring and Q rows, leaving no room for the tile list: not built.)
 //
 // The causal tile skip generalised: a block mask over (64-row query block,
@@ -39,6 +39,8 @@ int launch_fwd_bf16_sparse(const FwdArgs& a, hipStream_t stream) {
     return a.causal ? fwd::launch_sparse<128, true, 1, 8>(a, stream) : fwd::launch_sparse<128, false, 1, 8>(a, stream);
   if (a.D == 96)
     return a.causal ? fwd::launch_sparse<96, true, 1, 8>(a, stream) : fwd::launch_sparse<96, false, 1, 8>(a, stream);
+  if (a.D == 32)
+    return a.causal ? fwd::launch_sparse<32, true, 1, 4>(a, stream) : fwd::launch_sparse<32, false, 1, 4>(a, stream);
   return -2;
 }
 

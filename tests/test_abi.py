@@ -99,7 +99,7 @@ def test_forward_argument_validation(fn):
     assert _fwd(lib, fn, B=1024, H=1024, N=4096, D=64) == inv  # 2^38 elements
     # head dims no kernel serves (the float32 forward also rejects 96 and 160
     # in its launcher, before any launch)
-    for d in (1, 32, 100, 512) + ((96, 160) if fn == "fa_fwd_f32" else ()):
+    for d in (1, 48, 100, 512) + ((32, 96, 160) if fn == "fa_fwd_f32" else ()):
         assert _fwd(lib, fn, D=d) == uns
 
 
@@ -117,7 +117,7 @@ def test_backward_argument_validation(fn, nptr):
     assert f(*ptrs, 1, 1, 128, 64, float("nan"), 0, None) == inv
     assert f(*ptrs, 1, 1, 128, 64, 0.125, 7, None) == inv
     assert f(*ptrs, 1, 1, 128, 80, 0.125, 0, None) == uns
-    for d in (96, 160):  # forward-only head dims: the backward launchers reject them before launching
+    for d in (32, 96, 160):  # forward-only head dims: the backward launchers reject them before launching
         assert f(*ptrs, 1, 1, 128, d, 0.125, 0, None) == uns
 
 
@@ -146,7 +146,7 @@ def test_forward_kv_argument_validation():
     assert _fwd_kv(lib, splits=4, ws=FAKE, ws_bytes=need - 1) == inv  # short workspace
     assert _fwd_kv(lib, splits=4, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == inv  # misaligned
     assert _fwd_kv(lib, B=1024, H=1024, Nq=16, Nk=4096, D=64, **ok) == inv  # K holds 2^38 elements
-    for d in (32, 80):
+    for d in (48, 80):
         assert _fwd_kv(lib, D=d, **ok) == uns
     # sizes of the workspace
     assert lib.fa_fwd_kv_workspace_bytes(2, 3, 5, 64, 1) == 0
@@ -175,7 +175,7 @@ def test_forward_sparse_argument_validation():
     assert call(scale=float("nan")) == inv
     assert call(D=256) == uns  # rejected by its launcher before launching
     assert call(D=160) == uns
-    assert call(D=32) == uns
+    assert call(D=48) == uns
     assert call(B=1, H=1, N=4096 * 64 + 1, D=64) == uns  # more key tiles than the tile list holds
 
 

@@ -5,7 +5,7 @@ in seconds (c1, c2, c5) and on sampled rows otherwise (c3, c4: every head,
 the ends, tile boundaries and random rows; attention rows are independent,
 so the oracle computes just those rows).  Small shapes cover ragged lengths,
 several tiles and both masking modes, for every head dimension of the bf16
-forward (64, 96, 128, 160, 256).
+forward (32, 64, 96, 128, 160, 256).
 """
 
 import numpy as np
@@ -83,7 +83,7 @@ def test_workload_forward(name):
         _check_full(w, x, o, lse)
 
 
-@pytest.mark.parametrize("D,causal", [(128, True), (64, False), (256, True), (96, True), (160, False)])
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False), (256, True), (96, True), (160, False), (32, True)])
 def test_forward_long_sequence(D, causal):
     """N = 65536 (twice c4's length: 1024 key tiles per row, 32-bit tile
     offsets within a head up to 32 MiB), checked on sampled rows."""
@@ -95,7 +95,7 @@ def test_forward_long_sequence(D, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("D", [64, 96, 128, 160, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 256])
 @pytest.mark.parametrize("N", [1, 5, 64, 65, 130, 256, 300, 520])
 def test_forward_bf16_shapes(N, D, causal):
     w = WORKLOADS["c2"].with_(name="edge", B=1, H=2, N=N, D=D, causal=causal, seed=N * 7 + D)
@@ -114,7 +114,7 @@ def test_forward_f32_shapes(N, D, causal):
     _check_full(w, x, *_run(w, x))
 
 
-@pytest.mark.parametrize("D", [64, 96, 128, 160, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 256])
 def test_forward_peaked_rows(D):
     """Q scaled by 3 (and by 8): nearly one-hot rows stress the rescale path."""
     for mult in (3.0, 8.0):
@@ -125,7 +125,7 @@ def test_forward_peaked_rows(D):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("D", [64, 96, 128, 160, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 256])
 def test_forward_growing_scores(D, causal):
     """Scores that grow from key tile to key tile by G (exp2 units) along the
     processing order, so a later tile's exponentials against the running max
@@ -153,7 +153,7 @@ def test_forward_growing_scores(D, causal):
             _check_full(w, x, *_run(w, x))
 
 
-@pytest.mark.parametrize("D", [64, 96, 128, 160, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 256])
 def test_forward_invariants(D):
     import torch
 

@@ -86,6 +86,8 @@ CASES = [
     (1, 2, 130, 700, 160, True, 4),
     (2, 1, 1, 5000, 160, False, 0),
     (1, 2, 40, 3000, 160, False, 12),
+    (1, 2, 300, 1000, 32, True, 6),
+    (2, 2, 3, 2500, 32, False, 0),
 ]
 
 

@@ -80,6 +80,7 @@ CASES = [
     (1, 1, 300, 128, False, "rand0.0", False),  # nothing kept: O = 0, L = -inf everywhere
     (1, 2, 1000, 96, True, "rand0.5", True),
     (1, 2, 777, 96, False, "band", False),
+    (1, 2, 1000, 32, True, "holes", False),
 ]
 
 

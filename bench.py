@@ -320,6 +320,10 @@ def main() -> int:
         runs += [("p1", p1.with_(name="p1", causal=False)), ("p1_causal", p1.with_(name="p1_causal", causal=True))]
         # the causal backward at the c3 shape (timed only; the forward of c3 is the bench line)
         runs += [("c3", WORKLOADS["c3"].with_(backward=True))]
+        # head dims outside the five workloads, on their shapes: 32 and 96 on c2's and c3's,
+        # 160 on c5's
+        runs += [("d32", WORKLOADS["c2"].with_(name="d32", D=32)), ("d96", WORKLOADS["c3"].with_(name="d96", D=96)),
+                 ("d160", WORKLOADS["c5"].with_(name="d160", D=160, backward=False))]
         for name, wo in runs:
             xo = make_inputs(wo, with_do=False)
             qo, ko, vo = device_tensors(wo, xo)

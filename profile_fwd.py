@@ -240,7 +240,8 @@ def summarize_all_workloads(out: str, dest: str) -> None:
     bench.py runs c3, then c2, c4, c5 forward and c5 backward (whose setup
     runs one c5 forward), then the pages' shape B=2 H=4 N=2048 D=128 in both
     masking modes, the causal backward at the c3 shape (whose setup runs one
-    c3-shape forward), then fa_fwd_sparse at the c3 shape with a window of
+    c3-shape forward), the head dims 32, 96 and 160 on the c2, c3 and c5
+    shapes, then fa_fwd_sparse at the c3 shape with a window of
     16 key blocks and with a random half of the blocks (the same kernel
     instance: the first half of its launches is the window run), then
     fa_fwd_kv on the pages' shape in both masking
@@ -285,6 +286,8 @@ def summarize_all_workloads(out: str, dest: str) -> None:
                 label, seen_c5 = "c5 bwd", True
             else:
                 label, seen_c3_bwd = "c3 bwd", True
+        elif any(f"fwd_bf16_kernel<{d}," in family for d in (32, 96, 160)):
+            label = next(f"d{d} fwd" for d in (32, 96, 160) if f"fwd_bf16_kernel<{d}," in family)
         elif "fwd_bf16_kernel<64" in family:
             label, seen_c2 = "c2 fwd", True
         elif "fwd_bf16_kernel<256" in family:
@@ -305,6 +308,9 @@ def summarize_all_workloads(out: str, dest: str) -> None:
             "c4 fwd": WORKLOADS["c4"].fwd_flop(), "c5 fwd": WORKLOADS["c5"].fwd_flop(),
             "p1 fwd": p1.with_(causal=False).fwd_flop(), "p1 causal fwd": p1.with_(causal=True).fwd_flop()}
     flop["p1 fwd kv"], flop["p1 causal fwd kv"] = flop["p1 fwd"], flop["p1 causal fwd"]
+    flop["d32 fwd"] = WORKLOADS["c2"].with_(D=32).fwd_flop()
+    flop["d96 fwd"] = WORKLOADS["c3"].with_(D=96).fwd_flop()
+    flop["d160 fwd"] = WORKLOADS["c5"].with_(D=160).fwd_flop()
     import bench
     import numpy as np
 

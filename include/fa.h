@@ -44,7 +44,9 @@
  * Threads.  No global mutable state: calls from several host threads on
  *           different streams are safe.
  * Sizes.    B, H, N >= 1; B*H*N*D must fit in 2^31 - 1 elements per tensor.
- *           Head dims: D in {64, 128} for fa_fwd (also 256), see below.
+ *           Head dims: D in {32, 64, 96, 128, 160, 256} for the bf16
+ *           forward entry points, {64, 128, 256} for fa_fwd_f32 and the
+ *           backward; each entry point below states its own.
  *           scale must be finite and > 0 (the scores use scale = 1/sqrt(D)
  *           in every workload here; any positive scale is accepted).
  */
@@ -67,7 +69,7 @@ extern "C" {
  *   q, k, v : bf16 [B][H][N][D]        (read)
  *   o       : bf16 [B][H][N][D]        (written; O rounded to nearest-even)
  *   lse     : f32  [B][H][N]           (written; L = m + ln l, natural log)
- * D in {64, 128, 256}.  Any N >= 1.  causal: 0 or 1.
+ * D in {32, 64, 96, 128, 160, 256}.  Any N >= 1.  causal: 0 or 1.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
            float scale, int causal, void* stream);
@@ -106,7 +108,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
  *                     that size is 0).  Its contents on entry do not
  *                     matter; it is overwritten.  Two calls in flight at
  *                     once must not share it.
- * D in {64, 128, 256}; any Nq, Nk >= 1.  Errors: FA_ERR_INVALID_ARG also
+ * D in {32, 64, 96, 128, 160, 256} (the vector kernel for Nq <= 4 serves 64,
+ * 128 and 256; the others run on the matrix-core kernel); any Nq, Nk >= 1.
+ * Errors: FA_ERR_INVALID_ARG also
  * for causal with Nq > Nk, num_splits outside 0..256, or a missing, short
  * or misaligned workspace.
  */
@@ -146,9 +150,10 @@ size_t fa_fwd_kv_workspace_bytes(int B, int H, int Nq, int D, int num_splits);
  * any block pattern, the extension the metal-flash-attention README names.
  * A row that sees no key at all gets O = 0 and L = -inf (the pages do not
  * define it; -inf gives such a row weight 0 in any log-sum-exp merge).
- * D in {64, 128} (D = 256: FA_ERR_UNSUPPORTED; its forward kernel has no
- * LDS left for the tile list); 1 <= N <= 4096 * 64 (FA_ERR_UNSUPPORTED
- * above); FA_ERR_INVALID_ARG for a null mask or another mask_heads.
+ * D in {32, 64, 96, 128} (D = 160, 256: FA_ERR_UNSUPPORTED; their forward
+ * kernel has no LDS left for the tile list); 1 <= N <= 4096 * 64
+ * (FA_ERR_UNSUPPORTED above); FA_ERR_INVALID_ARG for a null mask or another
+ * mask_heads.
  */
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
                   float scale, int causal, const unsigned char* block_mask, int mask_heads, void* stream);

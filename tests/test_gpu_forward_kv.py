@@ -150,3 +150,18 @@ def test_forward_kv_long_decode_sampled_heads():
     """One decoded row per head over 32768 keys (the long-context key
     length), B=1 H=8, with the library's split count."""
     _run_and_check(1, 8, 1, 32768, 128, True, 0, seed=4, q_mult=3.0)
+
+
+@pytest.mark.parametrize("Nq,Nk,D,splits", [(1, 9000, 128, 0), (300, 2000, 64, 7), (3, 4000, 96, 0)])
+def test_forward_kv_deterministic(Nq, Nk, D, splits):
+    """Two runs on the same inputs give bitwise equal O and L (no atomics; the
+    merge sums the ranges in a fixed order)."""
+    import torch
+
+    scale, _, qb, _, kb, _, vb = _inputs(2, 3, Nq, Nk, D, 91)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o1, l1 = _fa().fwd_kv(q, k, v, scale, causal=True, num_splits=splits)
+    o2, l2 = _fa().fwd_kv(q, k, v, scale, causal=True, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)

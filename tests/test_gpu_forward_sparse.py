@@ -117,3 +117,18 @@ def test_forward_sparse_c3_shape_sampled_rows(kind):
                 el = max(el, abs(float(lh[b, h, i] - l_ref[0])))
     log(f"  c3 shape, mask {kind}: max|dO|={eo:.3e} max|dL|={el:.3e}")
     assert eo <= TOL_BF16_O and el <= TOL_BF16_L, (eo, el)
+
+
+def test_forward_sparse_deterministic():
+    """Two runs on the same inputs and mask give bitwise equal O and L."""
+    import torch
+
+    w = WORKLOADS["c3"].with_(B=1, H=4, N=3000, D=128, causal=True)
+    x = make_inputs(w, seed=93, with_do=False)
+    m = torch.from_numpy(_mask("rand0.5", -(-w.N // BLOCK), 94)).cuda()
+    q, k, v = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits)
+    o1, l1 = _fa().fwd_sparse(q, k, v, m, w.scale, True)
+    o2, l2 = _fa().fwd_sparse(q, k, v, m, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)

@@ -62,7 +62,10 @@ constexpr float kRescaleThreshold = 8.0f;  // exp2-domain growth allowed before 
 constexpr float kMaxFloor = 1.0e30f;       // the running max starts at -kMaxFloor
 constexpr float kTileSumLimit = 65536.0f;  // bound on a lane's share of a tile's row sum
 
-template <int D, int QB, int W>
+// QREG: keep the Q rows in registers even where the layout would put them in
+// LDS (the block-sparse instances of the 256-wide layout need that LDS for
+// their tile list).
+template <int D, int QB, int W, bool QREG = false>
 struct FwdCfg {
   static constexpr int kWaves = W;                       // waves per workgroup (4 or 8)
   static constexpr int kRowsPerWave = 32 * QB;
@@ -96,7 +99,7 @@ struct FwdCfg {
 #ifndef FA_FWD_QLDS
 #define FA_FWD_QLDS 1
 #endif
-  static constexpr bool kQInLds = kDP == 256 && FA_FWD_QLDS;
+  static constexpr bool kQInLds = kDP == 256 && !QREG && FA_FWD_QLDS;
   static constexpr int kQBytes = kQInLds ? kQBlocks * 32 * QB * kDP * 2 : 0;
   static constexpr int kLdsBytes = kRingBytes + kQBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
@@ -125,9 +128,9 @@ struct FwdCfg {
   static constexpr bool kLateRefill = kDP == 128;
 };
 
-template <int D, bool CAUSAL, int QB, int W>
+template <int D, bool CAUSAL, int QB, int W, bool QREG = false>
 struct FwdKernel {
-  using C = FwdCfg<D, QB, W>;
+  using C = FwdCfg<D, QB, W, QREG>;
   static constexpr int NB = C::kNB;
   static constexpr int KB = C::kKB;
 
@@ -388,14 +391,15 @@ __device__ __forceinline__ void unrolled(int i, int n, F& f, std::integer_sequen
 // SPARSE the kernel is the square forward.
 template <int D, bool CAUSAL, int QB, int W, bool SMALL, bool KV = false, bool SPARSE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W),
-                          amdgpu_waves_per_eu(FwdCfg<D, QB, W>::kWavesPerEU, FwdCfg<D, QB, W>::kWavesPerEU))) void
+                          amdgpu_waves_per_eu(FwdCfg<D, QB, W, SPARSE>::kWavesPerEU,
+                                              FwdCfg<D, QB, W, SPARSE>::kWavesPerEU))) void
 fwd_bf16_kernel(FwdArgs a, TileSched sched) {
-  using C = FwdCfg<D, QB, W>;
+  using C = FwdCfg<D, QB, W, SPARSE>;
   constexpr int NB = C::kNB;
   constexpr int LK = C::kLeadK, LV = C::kLeadV;
   constexpr int kWaves = C::kWaves;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLdsBytes];
-  FwdKernel<D, CAUSAL, QB, W> k;
+  FwdKernel<D, CAUSAL, QB, W, SPARSE> k;
   k.smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;

@@ -1,6 +1,8 @@
-// fa_fwd_sparse.hip -- block-sparse forward instances for D = 32, 64, 96
-// and 128.  (The D = 160 and D = 256 forward fills all 160 KB of LDS with its
-// K/V ring and Q rows, leaving no room for the tile list: not built.)
+// fa_fwd_sparse.hip -- block-sparse forward instances for D = 32, 64, 96,
+// 128, 160 and 256.  The 256-wide layout (D = 160, 256) fills all 160 KB of
+// LDS with its K/V ring and Q rows in the square kernel; its block-sparse
+// instances keep the Q rows in registers instead, which frees the LDS for
+// the tile list.
 //
 // The causal tile skip generalised: a block mask over (64-row query block,
 // 64-key block) pairs says which key tiles a query block reads, and each
@@ -16,7 +18,7 @@ namespace fwd {
 
 template <int D, bool CAUSAL, int QB, int W>
 int launch_sparse(const FwdArgs& a, hipStream_t stream) {
-  using C = FwdCfg<D, QB, W>;
+  using C = FwdCfg<D, QB, W, true>;
   const int n_qtiles = (a.N + C::kBlockM - 1) / C::kBlockM;
   const TileSched sched = make_sched(n_qtiles, a.B * a.H, CAUSAL);
   const long grid = (long)n_qtiles * a.B * a.H;
@@ -41,6 +43,10 @@ int launch_fwd_bf16_sparse(const FwdArgs& a, hipStream_t stream) {
     return a.causal ? fwd::launch_sparse<96, true, 1, 8>(a, stream) : fwd::launch_sparse<96, false, 1, 8>(a, stream);
   if (a.D == 32)
     return a.causal ? fwd::launch_sparse<32, true, 1, 4>(a, stream) : fwd::launch_sparse<32, false, 1, 4>(a, stream);
+  if (a.D == 256)
+    return a.causal ? fwd::launch_sparse<256, true, 1, 4>(a, stream) : fwd::launch_sparse<256, false, 1, 4>(a, stream);
+  if (a.D == 160)
+    return a.causal ? fwd::launch_sparse<160, true, 1, 4>(a, stream) : fwd::launch_sparse<160, false, 1, 4>(a, stream);
   return -2;
 }
 

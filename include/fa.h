@@ -150,10 +150,8 @@ size_t fa_fwd_kv_workspace_bytes(int B, int H, int Nq, int D, int num_splits);
  * any block pattern, the extension the metal-flash-attention README names.
  * A row that sees no key at all gets O = 0 and L = -inf (the pages do not
  * define it; -inf gives such a row weight 0 in any log-sum-exp merge).
- * D in {32, 64, 96, 128} (D = 160, 256: FA_ERR_UNSUPPORTED; their forward
- * kernel has no LDS left for the tile list); 1 <= N <= 4096 * 64
- * (FA_ERR_UNSUPPORTED above); FA_ERR_INVALID_ARG for a null mask or another
- * mask_heads.
+ * D in {32, 64, 96, 128, 160, 256}; 1 <= N <= 4096 * 64 (FA_ERR_UNSUPPORTED
+ * above); FA_ERR_INVALID_ARG for a null mask or another mask_heads.
  */
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
                   float scale, int causal, const unsigned char* block_mask, int mask_heads, void* stream);

@@ -81,6 +81,10 @@ CASES = [
     (1, 2, 1000, 96, True, "rand0.5", True),
     (1, 2, 777, 96, False, "band", False),
     (1, 2, 1000, 32, True, "holes", False),
+    (1, 2, 1000, 256, True, "rand0.5", True),
+    (1, 2, 777, 256, False, "holes", False),
+    (1, 2, 50, 256, True, "ones", False),
+    (1, 2, 900, 160, True, "band", False),
 ]
 
 

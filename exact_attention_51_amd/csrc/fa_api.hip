@@ -155,6 +155,9 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (rc != FA_OK) return rc;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
   const int splits = num_splits == 0 ? choose_splits(B, H, Nq, Nk, D) : num_splits;
+  // one workgroup per (query block, key range, head): the 1-D grid must fit
+  const int64_t qblocks = use_decode(Nq, D) ? 1 : (Nq + fa::fwd_rows_per_workgroup(D) - 1) / fa::fwd_rows_per_workgroup(D);
+  if (qblocks * splits * B * H > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
   const size_t need = kv_workspace_bytes(B, H, Nq, D, splits);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, D, scale, causal);

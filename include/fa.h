@@ -111,8 +111,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
  * D in {32, 64, 96, 128, 160, 256} (the vector kernel for Nq <= 4 serves 64,
  * 128 and 256; the others run on the matrix-core kernel); any Nq, Nk >= 1.
  * Errors: FA_ERR_INVALID_ARG also
- * for causal with Nq > Nk, num_splits outside 0..256, or a missing, short
- * or misaligned workspace.
+ * for causal with Nq > Nk, num_splits outside 0..256, a missing, short or
+ * misaligned workspace, or more than 2^31 - 1 workgroups (query blocks x
+ * key ranges x B x H).
  */
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
               float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes, void* stream);

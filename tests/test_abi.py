@@ -146,6 +146,9 @@ def test_forward_kv_argument_validation():
     assert _fwd_kv(lib, splits=4, ws=FAKE, ws_bytes=need - 1) == inv  # short workspace
     assert _fwd_kv(lib, splits=4, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == inv  # misaligned
     assert _fwd_kv(lib, B=1024, H=1024, Nq=16, Nk=4096, D=64, **ok) == inv  # K holds 2^38 elements
+    # 2^23 heads x 256 key ranges: more workgroups than a 1-D grid holds
+    huge = lib.fa_fwd_kv_workspace_bytes(4096, 2048, 1, 64, 256)
+    assert _fwd_kv(lib, B=4096, H=2048, Nq=1, Nk=2, D=64, splits=256, ws=FAKE, ws_bytes=huge) == inv
     for d in (48, 80):
         assert _fwd_kv(lib, D=d, **ok) == uns
     # sizes of the workspace

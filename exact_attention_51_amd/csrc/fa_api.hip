@@ -120,7 +120,8 @@ const char* fa_strerror(int code) {
       return "invalid argument (null pointer, non-positive size, bad scale or causal flag, or size overflow)";
     case FA_ERR_UNSUPPORTED:
       return "unsupported shape (head dimension: 32, 64, 96, 128, 160 or 256 for the bf16 forward, 64, 128 or "
-             "256 elsewhere) or block-sparse sequence length above 262144";
+             "256 for the float32 forward, 32, 64, 96, 128 or 256 for the backward) or block-sparse sequence length "
+             "above 262144";
     case FA_ERR_LAUNCH:
       return "kernel launch failed";
     default:

@@ -36,9 +36,17 @@ constexpr int kKeyTile = 64;  // dQ kernel: keys per streamed K/V tile
 // go to two waves that own the same 32 query rows (their dQ partial sums
 // are added at the end), so a workgroup covers 64 rows and the B*H*N/32
 // query blocks of a workload fill twice as many SIMDs.
+// LDS rows are DP wide: D = 32 and 96 use the layout of 64 and 128 with the
+// chunks past D unused (global rows stay D wide).
+template <int D>
+constexpr int lds_width() {
+  return D <= 64 ? 64 : D <= 128 ? 128 : 256;
+}
+
 template <int D>
 struct DqCfg {
-  static constexpr int kSplit = D == 256 ? 2 : 1;
+  static constexpr int kDP = lds_width<D>();
+  static constexpr int kSplit = kDP == 256 ? 2 : 1;
   static constexpr int kKB = 2 / kSplit;               // 32-key blocks a wave takes per tile
   static constexpr int kRows = 32 * kWavesQ / kSplit;  // query rows per workgroup
 };
@@ -54,7 +62,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     BwdArgs a, TileSched sched) {
   constexpr int kDSteps = D / 16, kDBlocks = D / 32;
   constexpr int KB = DqCfg<D>::kKB, kRowsQ = DqCfg<D>::kRows, kQBlocks = kWavesQ / DqCfg<D>::kSplit;
-  constexpr int kTileBytes = kKeyTile * D * 2;
+  constexpr int DP = DqCfg<D>::kDP;
+  constexpr int kTileBytes = kKeyTile * DP * 2;
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * kTileBytes];
   lds_char* smem = (lds_char*)smem_raw;
   lds_char* kbuf[2] = {smem, smem + kTileBytes};
@@ -86,7 +95,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
   // K/V tile t into ring slot b: scalar-base copies with loop-invariant
   // per-lane offsets, rows clamped onto N-1 only for a ragged last tile
-  RowTileCopier<D, D, kKeyTile, kWavesQ> cp;
+  RowTileCopier<D, DP, kKeyTile, kWavesQ> cp;
   cp.init(wave, lane);
   auto copy_tile = [&](int t, int b) {
     const int row0 = t * kKeyTile;
@@ -144,8 +153,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     for (int ds = 0; ds < kDSteps; ++ds)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = mfma32(read_row_operand<D>(kt, kr0 + kb * 32 + l32, ds, half), qf[ds], s[kb]);
-        dp[kb] = mfma32(read_row_operand<D>(vt, kr0 + kb * 32 + l32, ds, half), dof[ds], dp[kb]);
+        s[kb] = mfma32(read_row_operand<DP>(kt, kr0 + kb * 32 + l32, ds, half), qf[ds], s[kb]);
+        dp[kb] = mfma32(read_row_operand<DP>(vt, kr0 + kb * 32 + l32, ds, half), dof[ds], dp[kb]);
       }
 
     const bool masked = (CAUSAL && j == wave_last) || (j == n_ktiles_all - 1 && (N % kKeyTile) != 0);
@@ -183,7 +192,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
-          dq[db] = mfma32(read_tr_operand<D>(kt, kr0 + kb * 32 + cc * 16, db * 32, lane), dsk[kb][cc], dq[db]);
+          dq[db] = mfma32(read_tr_operand<DP>(kt, kr0 + kb * 32 + cc * 16, db * 32, lane), dsk[kb][cc], dq[db]);
   }
 
   if constexpr (DqCfg<D>::kSplit == 2) {
@@ -231,12 +240,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 template <int D>
 struct KvCfg {
   static_assert(D <= 128, "");
+  static constexpr int kDP = lds_width<D>();
   static constexpr int kWaves = 4;
   static constexpr int kKeys = 32 * kWaves;  // key rows per workgroup
   static constexpr int kQTile = 64;
   static constexpr int kQB = kQTile / 32;
-  static constexpr int kKvBytes = kKeys * D * 2;
-  static constexpr int kTileBytes = kQTile * D * 2;
+  static constexpr int kKvBytes = kKeys * kDP * 2;
+  static constexpr int kTileBytes = kQTile * kDP * 2;
   static constexpr int kStatBytes = 256;  // 64 floats of L or delta
   static constexpr int kLdsBytes = 2 * kKvBytes + 4 * kTileBytes + 4 * kStatBytes;
 };
@@ -245,7 +255,7 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 * KvCfg<D>::kWaves),
                           amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a, TileSched sched) {
   using C = KvCfg<D>;
-  constexpr int kDSteps = D / 16, kDBlocks = D / 32, QB = C::kQB, W = C::kWaves;
+  constexpr int kDSteps = D / 16, kDBlocks = D / 32, QB = C::kQB, W = C::kWaves, DP = C::kDP;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLdsBytes];
   lds_char* smem = (lds_char*)smem_raw;
   lds_char* kres = smem;
@@ -277,8 +287,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 
   const int t_begin = CAUSAL ? k0 / C::kQTile : 0;
 
   auto load_qtile = [&](int t, int b) {
-    copy_rows_lds<D, C::kQTile, W>(Q, N, t * C::kQTile, qbuf[b], wave, lane);
-    copy_rows_lds<D, C::kQTile, W>(dO, N, t * C::kQTile, obuf[b], wave, lane);
+    copy_rows_lds<D, DP, C::kQTile, W>(Q, N, t * C::kQTile, qbuf[b], wave, lane);
+    copy_rows_lds<D, DP, C::kQTile, W>(dO, N, t * C::kQTile, obuf[b], wave, lane);
     if (wave == 0) {
       int r = t * C::kQTile + lane;
       r = r < N ? r : N - 1;
@@ -286,8 +296,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 
       load_lds4(Dg + r, dbuf[b]);
     }
   };
-  copy_rows_lds<D, C::kKeys, W>(K, N, k0, kres, wave, lane);
-  copy_rows_lds<D, C::kKeys, W>(V, N, k0, vres, wave, lane);
+  copy_rows_lds<D, DP, C::kKeys, W>(K, N, k0, kres, wave, lane);
+  copy_rows_lds<D, DP, C::kKeys, W>(V, N, k0, vres, wave, lane);
   load_qtile(t_begin, 0);
 
   f32x16 dk[kDBlocks], dv[kDBlocks];
@@ -316,12 +326,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 
       for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < kDSteps; ++ds) {
-      const bf16x8 kf = read_row_operand<D>(kres, wave * 32 + l32, ds, half);
-      const bf16x8 vf = read_row_operand<D>(vres, wave * 32 + l32, ds, half);
+      const bf16x8 kf = read_row_operand<DP>(kres, wave * 32 + l32, ds, half);
+      const bf16x8 vf = read_row_operand<DP>(vres, wave * 32 + l32, ds, half);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        s[qb] = mfma32(read_row_operand<D>(qt, qb * 32 + l32, ds, half), kf, s[qb]);
-        dp[qb] = mfma32(read_row_operand<D>(ot, qb * 32 + l32, ds, half), vf, dp[qb]);
+        s[qb] = mfma32(read_row_operand<DP>(qt, qb * 32 + l32, ds, half), kf, s[qb]);
+        dp[qb] = mfma32(read_row_operand<DP>(ot, qb * 32 + l32, ds, half), vf, dp[qb]);
       }
     }
 
@@ -375,8 +385,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * KvCfg<D>::kWaves, 64 
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          dv[db] = mfma32(read_tr_operand<D>(ot, qb * 32 + cc * 16, db * 32, lane), ppk[qb][cc], dv[db]);
-          dk[db] = mfma32(read_tr_operand<D>(qt, qb * 32 + cc * 16, db * 32, lane), dspk[qb][cc], dk[db]);
+          dv[db] = mfma32(read_tr_operand<DP>(ot, qb * 32 + cc * 16, db * 32, lane), ppk[qb][cc], dv[db]);
+          dk[db] = mfma32(read_tr_operand<DP>(qt, qb * 32 + cc * 16, db * 32, lane), dspk[qb][cc], dk[db]);
         }
   }
 
@@ -422,8 +432,12 @@ int launch_dkdv(const BwdArgs& a, hipStream_t stream) {
 
 int launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   switch (a.D) {
+    case 32:
+      return a.causal ? launch_dq<32, true>(a, stream) : launch_dq<32, false>(a, stream);
     case 64:
       return a.causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+    case 96:
+      return a.causal ? launch_dq<96, true>(a, stream) : launch_dq<96, false>(a, stream);
     case 128:
       return a.causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
     case 256:
@@ -434,8 +448,12 @@ int launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 
 int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   switch (a.D) {
+    case 32:
+      return a.causal ? launch_dkdv<32, true>(a, stream) : launch_dkdv<32, false>(a, stream);
     case 64:
       return a.causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
+    case 96:
+      return a.causal ? launch_dkdv<96, true>(a, stream) : launch_dkdv<96, false>(a, stream);
     case 128:
       return a.causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
     case 256:

@@ -96,8 +96,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
   auto load_qtile = [&](int t) {
     const int sl = t % 3;
-    copy_rows_lds<D, C::kQTile, W>(Q, N, t * C::kQTile, qbuf(sl), wave, lane);
-    copy_rows_lds<D, C::kQTile, W>(dO, N, t * C::kQTile, obuf(sl), wave, lane);
+    copy_rows_lds<D, D, C::kQTile, W>(Q, N, t * C::kQTile, qbuf(sl), wave, lane);
+    copy_rows_lds<D, D, C::kQTile, W>(dO, N, t * C::kQTile, obuf(sl), wave, lane);
     if (wave == 0) {
       int r = t * C::kQTile + lane;
       r = r < N ? r : N - 1;

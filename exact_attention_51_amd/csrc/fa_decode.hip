@@ -127,7 +127,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(FwdArgs a) {
   int base = k_lo + wave * G;
   if (base < k_hi) load(base, kc, vc);
   for (; base < k_hi; base += U * STRIDE) {
-    if (base + U * STRIDE < k_hi) load(base + U * STRIDE, kn, vn);
+    const bool more = base + U * STRIDE < k_hi;  // wave-uniform
+    if (more) load(base + U * STRIDE, kn, vn);
     float s[NQ][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -178,10 +179,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[r][e] = __builtin_fmaf(p[r][u], vf[e], o[r][e]);
     }
+    if (more) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      kc[u] = kn[u];
-      vc[u] = vn[u];
+      for (int u = 0; u < U; ++u) {
+        kc[u] = kn[u];
+        vc[u] = vn[u];
+      }
     }
   }
 

@@ -189,12 +189,15 @@ __device__ __forceinline__ void load_lds4(const void* gptr, const void __attribu
 typedef char __attribute__((address_space(3))) lds_char;
 
 // Copy rows row0 .. row0+ROWS-1 (clamped to N-1) of a [N][D] bf16 matrix into
-// an LDS buffer of ROWS x D, in the swizzled layout above.  All WAVES waves of
-// the workgroup take part; each issues ROWS*D/8/WAVES/64 direct loads.
-template <int D, int ROWS, int WAVES>
+// an LDS buffer of ROWS x DP (DP >= D, in {64, 128, 256}), in the swizzled
+// layout above.  All WAVES waves of the workgroup take part; each issues
+// ROWS*DP/8/WAVES/64 direct loads.  A slot whose chunk lies past D copies the
+// row's first chunk again (into the unused part of the LDS row).
+template <int D, int DP, int ROWS, int WAVES>
 __device__ __forceinline__ void copy_rows_lds(const __bf16* __restrict__ src, int N, int row0, lds_char* buf, int wave,
                                               int lane) {
-  constexpr int kRowChunks = D / 8;
+  static_assert(D <= DP && D % 8 == 0, "row widths");
+  constexpr int kRowChunks = DP / 8;
   constexpr int kChunksPerWave = ROWS * kRowChunks / WAVES;
   static_assert(kChunksPerWave % 64 == 0, "tile must split into whole wave loads");
 #pragma unroll
@@ -202,7 +205,8 @@ __device__ __forceinline__ void copy_rows_lds(const __bf16* __restrict__ src, in
     const int slot0 = wave * kChunksPerWave + i * 64;  // wave-uniform
     const int slot = slot0 + lane;
     const int r = slot / kRowChunks;
-    const int c = (slot % kRowChunks) ^ swz<D>(r);
+    int c = (slot % kRowChunks) ^ swz<DP>(r);
+    c = c < D / 8 ? c : 0;
     int grow = row0 + r;
     grow = grow < N ? grow : N - 1;
     load_lds16(src + (size_t)grow * D + c * 8, buf + slot0 * 16);

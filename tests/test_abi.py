@@ -117,7 +117,7 @@ def test_backward_argument_validation(fn, nptr):
     assert f(*ptrs, 1, 1, 128, 64, float("nan"), 0, None) == inv
     assert f(*ptrs, 1, 1, 128, 64, 0.125, 7, None) == inv
     assert f(*ptrs, 1, 1, 128, 80, 0.125, 0, None) == uns
-    for d in (32, 96, 160):  # forward-only head dims: the backward launchers reject them before launching
+    for d in (160,):  # a forward-only head dim: the backward launchers reject it before launching
         assert f(*ptrs, 1, 1, 128, d, 0.125, 0, None) == uns
 
 

@@ -39,10 +39,15 @@ def _run_bwd(w, x):
 
 
 def _check(w, x, got, rel_tol=TOL_BF16_GRAD):
-    """Gradients: max abs error <= 2e-2 and, unless the oracle's gradient is
-    exactly zero, max abs error / max |reference| <= 2e-2."""
+    """Gradients: max abs error <= 2e-2 * max(1, max |reference|) and, unless
+    the oracle's gradient is exactly zero, max abs error / max |reference|
+    <= 2e-2.  bf16 rounding errors scale with the magnitude of what is
+    rounded; the absolute 2e-2 is the bound for entries up to 1 (the
+    D = 256 workload's are about 0.03), and where a gradient's largest entry
+    exceeds 1 (small head dims, scale 1/sqrt(32)) it scales with it."""
     dq, dk, dv, delta = got
     errs = {}
+    refmax = {}
     zero = set()
     for b in range(w.B):
         for h in range(w.H):
@@ -54,6 +59,7 @@ def _check(w, x, got, rel_tol=TOL_BF16_GRAD):
                 er = ea / max(float(np.abs(ref[name]).max()), 1e-30)
                 pa, pr = errs.get(name, (0.0, 0.0))
                 errs[name] = (max(pa, ea), max(pr, er))
+                refmax[name] = max(refmax.get(name, 0.0), float(np.abs(ref[name]).max()))
             ed = float(np.abs(host(delta)[b, h] - ref["delta"]).max())
             edr = ed / max(float(np.abs(ref["delta"]).max()), TINY)
             pa, pr = errs.get("delta", (0.0, 0.0))
@@ -64,7 +70,7 @@ def _check(w, x, got, rel_tol=TOL_BF16_GRAD):
     log(f"  {w.name} B={w.B} H={w.H} N={w.N} D={w.D} causal={w.causal}: " + ", ".join(f"{k}: abs {a:.2e} rel {r:.2e}" for k, (a, r) in errs.items()))
     for name in ("dq", "dk", "dv"):
         a, r = errs[name]
-        assert a <= TOL_BF16_GRAD, (name, a)
+        assert a <= TOL_BF16_GRAD * max(1.0, refmax[name]), (name, a, refmax[name])
         assert name in zero or r <= rel_tol, (name, r)
     assert errs["delta"][1] <= TOL_DELTA_REL, errs["delta"]
 
@@ -77,7 +83,7 @@ def test_workload_backward_c5():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("N", [1, 40, 64, 100, 256, 333])
 def test_backward_shapes(N, D, causal):
     w = WORKLOADS["c5"].with_(name="edge", B=1, H=2, N=N, D=D, causal=causal, seed=3 * N + D)
@@ -86,7 +92,7 @@ def test_backward_shapes(N, D, causal):
     _check(w, x, _run_bwd(w, x))
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [96, 128, 256])
 def test_backward_causal_long(D):
     w = WORKLOADS["c5"].with_(name="causal_long", B=1, H=2, N=1024, D=D, causal=True, seed=D + 1)
     log(f"test_backward_causal_long D={D}")

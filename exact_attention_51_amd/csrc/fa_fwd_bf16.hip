@@ -23,13 +23,37 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 
 int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
 
+// CUs of the current device (256 if the query fails).
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
 // Query blocks of 32 rows per wave, and waves per workgroup by head
 // dimension: at D = 128 one 8-wave workgroup per CU (two waves per SIMD;
 // the K/V ring takes 128 KB of LDS), at D = 64 three 4-wave workgroups per
 // CU, which do not share barriers and so drift into complementary phases
-// (the D = 64 step is bound by its VALU work).
+// (the D = 64 step is bound by its VALU work).  At D = 128 (and 96) a grid
+// of fewer 256-row workgroups than CUs takes 4-wave, 128-row workgroups
+// instead: twice the workgroups, one wave on each SIMD of twice the CUs.
+// Under causal masking (uneven blocks) this pays up to twice as many
+// 256-row blocks as CUs; measured on one MI355X: B=2 H=4 N=2048, 54 -> 39 us
+// with and without the mask, B=1 H=8 N=8192 causal 210 -> 182 us, while
+// non-causal grids of 256..511 blocks lose (B=1 H=8 N=8192: 263 -> 310 us).
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   constexpr int QB = 1, W64 = 4, W128 = 8;
+  if (a.D == 128 || a.D == 96) {
+    const long blocks = (long)((a.N + 255) / 256) * a.B * a.H;
+    const int cus = device_cus();
+    if (blocks < cus || (a.causal && blocks < 2 * cus)) {
+      if (a.D == 128)
+        return a.causal ? fwd::launch<128, true, QB, 4>(a, stream) : fwd::launch<128, false, QB, 4>(a, stream);
+      return a.causal ? fwd::launch<96, true, QB, 4>(a, stream) : fwd::launch<96, false, QB, 4>(a, stream);
+    }
+  }
   if (a.D == 64) return a.causal ? fwd::launch<64, true, QB, W64>(a, stream) : fwd::launch<64, false, QB, W64>(a, stream);
   if (a.D == 32)  // the D = 64 workgroup shape and LDS layout, 32 columns unused
     return a.causal ? fwd::launch<32, true, QB, W64>(a, stream) : fwd::launch<32, false, QB, W64>(a, stream);

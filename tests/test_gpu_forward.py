@@ -105,6 +105,19 @@ def test_forward_bf16_shapes(N, D, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [96, 128])
+def test_forward_bf16_many_heads(D, causal):
+    """B*H = 512 heads of N = 300: enough 256-row blocks that D = 96 and 128
+    run their 8-wave workgroups (the small shapes above run the 4-wave,
+    128-row workgroups the forward picks for grids smaller than the GPU)."""
+    w = WORKLOADS["c3"].with_(name="heads", B=4, H=128, N=300, D=D, causal=causal, seed=300 + D)
+    log(f"test_forward_bf16_many_heads D={D} causal={causal}")
+    x = make_inputs(w, with_do=False)
+    o, lse = _run(w, x)
+    _check_full(w, x, o, lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 33, 256, 300])
 def test_forward_f32_shapes(N, D, causal):

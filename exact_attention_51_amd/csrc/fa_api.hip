@@ -82,7 +82,7 @@ int choose_splits(int B, int H, int Nq, int Nk, int D) {
     return s < 1 ? 1 : (int)s;
   }
   const int64_t slots = (int64_t)cus * fa::fwd_workgroups_per_cu(D);
-  const int rows = fa::fwd_rows_per_workgroup(D);
+  const int rows = fa::fwd_rows_per_workgroup(D, Nq);
   const int64_t blocks = (int64_t)((Nq + rows - 1) / rows) * B * H;
   if (blocks >= slots) return 1;
   int64_t s = (slots + blocks - 1) / blocks;
@@ -157,7 +157,7 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
   const int splits = num_splits == 0 ? choose_splits(B, H, Nq, Nk, D) : num_splits;
   // one workgroup per (query block, key range, head): the 1-D grid must fit
-  const int64_t qblocks = use_decode(Nq, D) ? 1 : (Nq + fa::fwd_rows_per_workgroup(D) - 1) / fa::fwd_rows_per_workgroup(D);
+  const int64_t qblocks = use_decode(Nq, D) ? 1 : (Nq + fa::fwd_rows_per_workgroup(D, Nq) - 1) / fa::fwd_rows_per_workgroup(D, Nq);
   if (qblocks * splits * B * H > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
   const size_t need = kv_workspace_bytes(B, H, Nq, D, splits);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)) return FA_ERR_INVALID_ARG;

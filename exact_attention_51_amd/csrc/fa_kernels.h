@@ -70,7 +70,7 @@ int launch_fwd_bf16_sparse(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_decode(const FwdArgs& a, hipStream_t stream);
 // Workgroups of the forward kernel one CU runs at a time, by head dimension.
 int fwd_workgroups_per_cu(int D);
-int fwd_rows_per_workgroup(int D);
+int fwd_rows_per_workgroup(int D, int Nq);  // query rows per workgroup of the fa_fwd_kv matrix-core path
 int launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 int launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);

@@ -80,64 +80,81 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_kernel(FwdArgs a) {
 }
 
 // The same merge for many key ranges: one workgroup per row, the ranges
-// divided among kP groups of D/4 threads (range s goes to group s % kP), so
-// the loads of different ranges are in flight together; the groups' partial
-// max, sums and O combine through LDS.
+// divided among kP groups of D/4 threads (range s goes to group s % kP).
+// Each thread merges its ranges in chunks of kChunk, issuing a chunk's loads
+// together, as a running (max M, sum l, weighted O) in the exp2 domain; the
+// groups' running sums combine through LDS.  The running max starts at a
+// finite floor, so ranges with L_s = -inf (O_s = 0) add exactly nothing.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
   constexpr int kThreadsPerRow = D / 4;
   constexpr int kP = 256 / kThreadsPerRow;
-  __shared__ float red[kP];
+  constexpr int kChunk = 8;
+  constexpr float kFloor = -1.0e30f;
+  __shared__ float red_m[kP], red_l[kP];
   __shared__ f32x4 ored[kP][kThreadsPerRow];
   const long rows = (long)a.B * a.H * a.N;
   const long r = blockIdx.x;
   // threads past kP whole groups (D/4 need not divide 256) take no range
   const bool in_group = threadIdx.x < kP * kThreadsPerRow;
   const int t = threadIdx.x % kThreadsPerRow, p = threadIdx.x / kThreadsPerRow;
-  const int S = in_group ? a.n_split : 0;  // no range for threads outside the groups
+  const int S = in_group ? a.n_split : 0;
   const float* __restrict__ Lp = a.part_l + r;
   const float* __restrict__ Op = a.part_o + r * D + t * 4;
-  float mx = -__builtin_inff();
-  for (int s = p; s < S; s += kP) mx = __builtin_fmaxf(mx, Lp[(size_t)s * rows]);
-  if (t == 0 && in_group) red[p] = mx;
-  __syncthreads();
-  mx = red[0];
-#pragma unroll
-  for (int i = 1; i < kP; ++i) mx = __builtin_fmaxf(mx, red[i]);
-  __syncthreads();
-  float sum = 0.f;
-  for (int s = p; s < S; s += kP) sum += fast_exp2((Lp[(size_t)s * rows] - mx) * kLog2e);
-  if (t == 0 && in_group) red[p] = sum;
-  __syncthreads();
-  sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < kP; ++i) sum += red[i];
-  const float L = mx + fast_log2(sum) * kLn2;
+  float M = kFloor, l = 0.f;  // exp2 domain
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = p; s < S; s += kP) {
-    const float w = fast_exp2((Lp[(size_t)s * rows] - L) * kLog2e);
-    if (w > 0.f) {
-      const f32x4 x = *(const f32x4*)(Op + (size_t)s * rows * D);
-      acc[0] = __builtin_fmaf(w, x[0], acc[0]);
-      acc[1] = __builtin_fmaf(w, x[1], acc[1]);
-      acc[2] = __builtin_fmaf(w, x[2], acc[2]);
-      acc[3] = __builtin_fmaf(w, x[3], acc[3]);
+  for (int s0 = p; s0 < S; s0 += kP * kChunk) {
+    float ls[kChunk];
+    f32x4 xs[kChunk];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int s = s0 + c * kP;
+      ls[c] = s < S ? Lp[(size_t)s * rows] * kLog2e : -__builtin_inff();
+      xs[c] = s < S ? *(const f32x4*)(Op + (size_t)s * rows * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mc = M;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) mc = __builtin_fmaxf(mc, ls[c]);
+    const float alpha = fast_exp2(M - mc);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const float w = fast_exp2(ls[c] - mc);
+      l += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, xs[c][e], acc[e]);
+    }
+    M = mc;
+  }
+  if (in_group) {
+    ored[p][t] = acc;
+    if (t == 0) {
+      red_m[p] = M;
+      red_l[p] = l;
     }
   }
-  if (in_group) ored[p][t] = acc;
   __syncthreads();
   if (p != 0) return;
+  float Mt = red_m[0];
 #pragma unroll
-  for (int i = 1; i < kP; ++i) {
+  for (int i = 1; i < kP; ++i) Mt = __builtin_fmaxf(Mt, red_m[i]);
+  float lt = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kP; ++i) {
+    const float w = fast_exp2(red_m[i] - Mt);
+    lt = __builtin_fmaf(w, red_l[i], lt);
     const f32x4 x = ored[i][t];
-    acc[0] += x[0];
-    acc[1] += x[1];
-    acc[2] += x[2];
-    acc[3] += x[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(w, x[e], o[e]);
   }
-  const u32x2 packed = {pack_bf16_u32(acc[0], acc[1]), pack_bf16_u32(acc[2], acc[3])};
+  // every row sees some key, so lt > 0
+  const float inv = 1.0f / lt;
+  const u32x2 packed = {pack_bf16_u32(o[0] * inv, o[1] * inv), pack_bf16_u32(o[2] * inv, o[3] * inv)};
   *(u32x2*)((__bf16*)a.o + r * D + t * 4) = packed;
-  if (t == 0) a.lse[r] = L;
+  if (t == 0) a.lse[r] = (Mt + fast_log2(lt)) * kLn2;
 }
 
 }  // namespace fwd

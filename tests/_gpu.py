@@ -1,7 +1,9 @@
 """Helpers for the GPU parity tests: move seeded inputs to the device, run
 the library through its C ABI and compare with the float64 oracle."""
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -54,3 +56,30 @@ def sample_rows(n, count, seed):
     rows = [r for r in fixed if 0 <= r < n]
     rows += list(rng.integers(0, n, size=count))
     return np.unique(np.array(rows, dtype=np.int64))
+
+
+def pool_workers(cap=16):
+    """Worker threads for the CPU oracle: the host cores this process may use,
+    at most ``cap`` (one GPU's share of a shared host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(n, cap))
+
+
+def forward_errors_all_rows(w, x, o_host, l_host, row_block=256):
+    """Max |O - O_ref| and max |L - L_ref| over EVERY row of every (batch,
+    head), the oracle run on (batch, head, row block) units over a thread
+    pool (one BLAS thread per worker).  o_host, l_host: the GPU results as
+    float64 host arrays [B, H, N, D] and [B, H, N]."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    def unit(args):
+        b, h, r0 = args
+        rows = np.arange(r0, min(w.N, r0 + row_block))
+        o_ref, l_ref = oracle.forward_rows(x.q[b, h], x.k[b, h], x.v[b, h], rows, w.scale, w.causal)
+        return (float(np.abs(o_host[b, h, rows] - o_ref).max()), float(np.abs(l_host[b, h, rows] - l_ref).max()))
+
+    units = [(b, h, r0) for b in range(w.B) for h in range(w.H) for r0 in range(0, w.N, row_block)]
+    with threadpool_limits(1), ThreadPoolExecutor(pool_workers()) as ex:
+        res = list(ex.map(unit, units))
+    return max(r[0] for r in res), max(r[1] for r in res)

@@ -38,35 +38,39 @@ def _run_bwd(w, x):
     return dq, dk, dv, delta
 
 
-def _check(w, x, got, rel_tol=TOL_BF16_GRAD):
+def _check(w, x, got, rel_tol=TOL_BF16_GRAD, heads=None):
     """Gradients: max abs error <= 2e-2 * max(1, max |reference|) and, unless
     the oracle's gradient is exactly zero, max abs error / max |reference|
     <= 2e-2.  bf16 rounding errors scale with the magnitude of what is
     rounded; the absolute 2e-2 is the bound for entries up to 1 (the
     D = 256 workload's are about 0.03), and where a gradient's largest entry
-    exceeds 1 (small head dims, scale 1/sqrt(32)) it scales with it."""
+    exceeds 1 (small head dims, scale 1/sqrt(32)) it scales with it.
+    heads: the (batch, head) pairs to compare (default: all)."""
     dq, dk, dv, delta = got
+    gh = {"dq": host(dq), "dk": host(dk), "dv": host(dv)}
+    delta_h = host(delta)
     errs = {}
     refmax = {}
     zero = set()
-    for b in range(w.B):
-        for h in range(w.H):
-            ref = oracle.backward(x.q[b, h], x.k[b, h], x.v[b, h], x.do[b, h], w.scale, w.causal)
-            for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-                g = host(t)[b, h]
-                assert np.isfinite(g).all(), name
-                ea = float(np.abs(g - ref[name]).max())
-                er = ea / max(float(np.abs(ref[name]).max()), 1e-30)
-                pa, pr = errs.get(name, (0.0, 0.0))
-                errs[name] = (max(pa, ea), max(pr, er))
-                refmax[name] = max(refmax.get(name, 0.0), float(np.abs(ref[name]).max()))
-            ed = float(np.abs(host(delta)[b, h] - ref["delta"]).max())
-            edr = ed / max(float(np.abs(ref["delta"]).max()), TINY)
-            pa, pr = errs.get("delta", (0.0, 0.0))
-            errs["delta"] = (max(pa, ed), max(pr, edr))
-            for name in ("dq", "dk", "dv"):
-                if float(np.abs(ref[name]).max()) < TINY:
-                    zero.add(name)
+    if heads is None:
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in heads:
+        ref = oracle.backward(x.q[b, h], x.k[b, h], x.v[b, h], x.do[b, h], w.scale, w.causal)
+        for name in ("dq", "dk", "dv"):
+            g = gh[name][b, h]
+            assert np.isfinite(g).all(), name
+            ea = float(np.abs(g - ref[name]).max())
+            er = ea / max(float(np.abs(ref[name]).max()), 1e-30)
+            pa, pr = errs.get(name, (0.0, 0.0))
+            errs[name] = (max(pa, ea), max(pr, er))
+            refmax[name] = max(refmax.get(name, 0.0), float(np.abs(ref[name]).max()))
+        ed = float(np.abs(delta_h[b, h] - ref["delta"]).max())
+        edr = ed / max(float(np.abs(ref["delta"]).max()), TINY)
+        pa, pr = errs.get("delta", (0.0, 0.0))
+        errs["delta"] = (max(pa, ed), max(pr, edr))
+        for name in ("dq", "dk", "dv"):
+            if float(np.abs(ref[name]).max()) < TINY:
+                zero.add(name)
     log(f"  {w.name} B={w.B} H={w.H} N={w.N} D={w.D} causal={w.causal}: " + ", ".join(f"{k}: abs {a:.2e} rel {r:.2e}" for k, (a, r) in errs.items()))
     for name in ("dq", "dk", "dv"):
         a, r = errs[name]
@@ -101,13 +105,18 @@ def test_backward_causal_long(D):
 
 
 def test_backward_c3_shape():
-    """The causal backward at the c3 sequence length and head dimension
-    (N = 8192, D = 128) for one head against the dense oracle: heads are
-    independent, so the 32 heads of c3 only repeat this."""
-    w = WORKLOADS["c3"].with_(name="c3_bwd_head", B=1, H=1, backward=True, seed=13)
-    log(f"test_backward_c3_shape N={w.N} D={w.D} causal={w.causal}")
+    """The causal backward on the whole c3 grid (B = 2, H = 16, N = 8192,
+    D = 128): both kernels run over all 32 heads, and eight of them are
+    compared with the dense oracle.  The tile scheduler gives each of the
+    eight XCDs a contiguous group of B*H/8 = 4 heads, so the heads checked,
+    bh = 0, 5, 10, 15, 16, 21, 26, 31, are one per XCD group and each
+    position within a group."""
+    w = WORKLOADS["c3"].with_(name="c3_bwd", backward=True, seed=13)
+    log(f"test_backward_c3_shape B={w.B} H={w.H} N={w.N} D={w.D} causal={w.causal}")
     x = make_inputs(w, with_do=True)
-    _check(w, x, _run_bwd(w, x))
+    got = _run_bwd(w, x)
+    heads = [divmod(bh, w.H) for bh in (0, 5, 10, 15, 16, 21, 26, 31)]
+    _check(w, x, got, heads=heads)
 
 
 def test_backward_deterministic():

@@ -215,8 +215,23 @@ def time_backward(w, q, k, v, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps
 
 
+def cgroup_cpu_quota():
+    """CPUs the cgroup v2 quota grants this process (cpu.max), or None when
+    there is no quota."""
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+    except (OSError, ValueError):
+        return None
+    if quota == "max":
+        return None
+    return max(1, int(int(quota) // int(period)))
+
+
 def cpu_baseline(w, x, budget_s: float = 12.0):
-    """Time the float64 oracle on whole heads of the workload, on all host cores.
+    """Time the float64 oracle on whole heads of the workload, on all host
+    cores this process may use (its CPU affinity, capped by a cgroup CPU
+    quota if one is set); the record gives the worker count and both limits.
 
     Heads are added until about ``budget_s`` of wall time is spent (at most
     all of them).  Work is split into (head, 256-row block) units over a
@@ -229,8 +244,11 @@ def cpu_baseline(w, x, budget_s: float = 12.0):
 
     import oracle
 
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    cores = max(1, min(cores, 16))
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    quota = cgroup_cpu_quota()
+    # one worker per core this process may run on; a cgroup CPU quota below
+    # the affinity count caps it (more threads than the quota only time-slice)
+    cores = max(1, min(affinity, quota) if quota else affinity)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     rb = 256
 
@@ -257,6 +275,8 @@ def cpu_baseline(w, x, budget_s: float = 12.0):
         "value": flop / dt / 1e12,
         "unit": "TFLOPS",
         "cores": cores,
+        "affinity_cores": affinity,
+        "cgroup_cpu_quota": quota,
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name}, all {w.N} rows each, float64 numpy, {dt:.1f} s",
     }

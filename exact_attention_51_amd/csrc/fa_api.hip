@@ -4,8 +4,33 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa.h"
 #include "fa_kernels.h"
+
+namespace fa {
+
+constexpr int kMaxDevices = 64;
+
+namespace {
+std::atomic<int> g_device_cus[kMaxDevices];  // 0 until the device's count is read
+}  // namespace
+
+// Racing first calls on one device both read the same count and store it;
+// every later call on that device reads the cached value.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int cached = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (cached > 0) return cached;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace fa
 
 namespace {
 
@@ -67,10 +92,7 @@ bool use_decode(int Nq, int D) { return Nq <= fa::kDecodeMaxRows && (D == 64 || 
 // for three or four rows), at least two ranges, each over at least 256 keys
 // (measured: 256 to 512 decode workgroups beat both fewer and more).
 int choose_splits(int B, int H, int Nq, int Nk, int D) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = fa::device_cus();
   if (use_decode(Nq, D)) {
     const int64_t heads = (int64_t)B * H;
     int64_t s = (cus + heads - 1) / heads;
@@ -104,6 +126,54 @@ int check_kv(int B, int H, int Nq, int Nk, int D, float scale, int causal) {
   if ((int64_t)B * H * Nk * D > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
   if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
   return FA_OK;
+}
+
+// Checks of fa_fwd_kv, and the range count.
+// HIP's launch limit is on work-items (workgroups x threads per workgroup
+// below 2^32), for the range kernel and for the merge: both are checked
+// here, before anything is launched.
+int kv_prepare(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
+               float scale, int causal, int num_splits, int* splits_out) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  const int rc = check_kv(B, H, Nq, Nk, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  const int splits = num_splits == 0 ? choose_splits(B, H, Nq, Nk, D) : num_splits;
+  const int64_t rows = (int64_t)B * H * Nq;
+  int64_t workgroups, threads;
+  if (use_decode(Nq, D)) {
+    workgroups = (int64_t)B * H * splits;
+    threads = fa::kDecodeThreads;
+  } else {
+    const int rows_wg = fa::fwd_rows_per_workgroup(D, Nq);
+    workgroups = (int64_t)((Nq + rows_wg - 1) / rows_wg) * splits * B * H;
+    threads = fa::fwd_threads_per_workgroup(D, Nq);
+  }
+  if (workgroups * threads > (int64_t)UINT32_MAX) return FA_ERR_INVALID_ARG;
+  // the merge: one 256-thread workgroup per row for many ranges, else
+  // 256-thread workgroups of 256 / (D/4) rows
+  if (splits > 1) {
+    const int64_t rows_per_wg = 256 / (D / 4);
+    const int64_t merge_wgs = splits > fa::kMaxNarrowMerge ? rows : (rows + rows_per_wg - 1) / rows_per_wg;
+    if (merge_wgs * 256 > (int64_t)UINT32_MAX) return FA_ERR_INVALID_ARG;
+  }
+  *splits_out = splits;
+  return FA_OK;
+}
+
+int kv_run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
+           float scale, int causal, int splits, void* workspace, void* stream) {
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, D, scale, causal);
+  a.Nk = Nk;
+  a.n_split = splits;
+  if (splits > 1) {
+    a.part_o = (float*)workspace;
+    a.part_l = (float*)workspace + (size_t)splits * B * H * Nq * D;
+  }
+  int lrc = use_decode(Nq, D) ? fa::launch_fwd_decode(a, (hipStream_t)stream)
+                              : fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
+  if (lrc == 0 && splits > 1) lrc = fa::launch_fwd_kv_merge(a, (hipStream_t)stream);
+  return map_launch(lrc);
 }
 
 }  // namespace
@@ -151,27 +221,12 @@ size_t fa_fwd_kv_workspace_bytes(int B, int H, int Nq, int D, int num_splits) {
 
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
               float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  const int rc = check_kv(B, H, Nq, Nk, D, scale, causal);
+  int splits = 0;
+  const int rc = kv_prepare(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, num_splits, &splits);
   if (rc != FA_OK) return rc;
-  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
-  const int splits = num_splits == 0 ? choose_splits(B, H, Nq, Nk, D) : num_splits;
-  // one workgroup per (query block, key range, head): the 1-D grid must fit
-  const int64_t qblocks = use_decode(Nq, D) ? 1 : (Nq + fa::fwd_rows_per_workgroup(D, Nq) - 1) / fa::fwd_rows_per_workgroup(D, Nq);
-  if (qblocks * splits * B * H > (int64_t)INT32_MAX) return FA_ERR_INVALID_ARG;
   const size_t need = kv_workspace_bytes(B, H, Nq, D, splits);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)) return FA_ERR_INVALID_ARG;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, D, scale, causal);
-  a.Nk = Nk;
-  a.n_split = splits;
-  if (splits > 1) {
-    a.part_o = (float*)workspace;
-    a.part_l = (float*)workspace + (size_t)splits * B * H * Nq * D;
-  }
-  int lrc = use_decode(Nq, D) ? fa::launch_fwd_decode(a, (hipStream_t)stream)
-                              : fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
-  if (lrc == 0 && splits > 1) lrc = fa::launch_fwd_kv_merge(a, (hipStream_t)stream);
-  return map_launch(lrc);
+  return kv_run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, splits, workspace, stream);
 }
 
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,

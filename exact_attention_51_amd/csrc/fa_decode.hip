@@ -30,7 +30,7 @@
 namespace fa {
 namespace dec {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kDecodeThreads / 64;
 constexpr int kUnroll = 4;                 // key rows per lane group in flight per buffer
 constexpr float kMaxFloor = 1.0e30f;       // running max starts at -kMaxFloor (masked keys give p = 0)
 

@@ -96,10 +96,7 @@ struct FwdCfg {
   // Q rows in LDS (D = 256) instead of registers: with them in registers
   // the O accumulators no longer fit beside the rest and the compiler
   // copies them between VGPRs and AGPRs around every P V MFMA.
-#ifndef FA_FWD_QLDS
-#define FA_FWD_QLDS 1
-#endif
-  static constexpr bool kQInLds = kDP == 256 && !QREG && FA_FWD_QLDS;
+  static constexpr bool kQInLds = kDP == 256 && !QREG;
   static constexpr int kQBytes = kQInLds ? kQBlocks * 32 * QB * kDP * 2 : 0;
   static constexpr int kLdsBytes = kRingBytes + kQBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");

@@ -23,15 +23,6 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 
 int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
 
-// CUs of the current device (256 if the query fails).
-static int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  return cus;
-}
-
 // Query blocks of 32 rows per wave, and waves per workgroup by head
 // dimension: at D = 128 one 8-wave workgroup per CU (two waves per SIMD;
 // the K/V ring takes 128 KB of LDS), at D = 64 three 4-wave workgroups per

@@ -36,7 +36,7 @@ int launch_kv(const FwdArgs& a, hipStream_t stream) {
 // the row's L_s of every range give L, then O = sum_s e^{L_s - L} O_s,
 // rounded to bf16.  Every range's loads are issued together; a range a row
 // does not reach holds O_s = 0 and L_s = -inf, so its term is exactly 0.
-constexpr int kMaxNarrow = 8;
+constexpr int kMaxNarrow = kMaxNarrowMerge;
 template <int D>
 __global__ __launch_bounds__(256) void fwd_kv_merge_kernel(FwdArgs a) {
   constexpr int kThreadsPerRow = D / 4;
@@ -168,6 +168,12 @@ __global__ __launch_bounds__(256) void fwd_kv_merge_wide_kernel(FwdArgs a) {
 static bool kv_small_block(int D, int Nq) { return (D == 128 || D == 96) && Nq <= 128; }
 
 int fwd_workgroups_per_cu(int D) { return D <= 64 ? 3 : 1; }
+int fwd_threads_per_workgroup(int D, int Nq) {
+  if (D <= 64) return 64 * fwd::FwdCfg<64, 1, 4>::kWaves;
+  if (kv_small_block(D, Nq)) return 64 * fwd::FwdCfg<128, 1, 4>::kWaves;
+  if (D == 96 || D == 128) return 64 * fwd::FwdCfg<128, 1, 8>::kWaves;
+  return 64 * fwd::FwdCfg<256, 1, 4>::kWaves;
+}
 int fwd_rows_per_workgroup(int D, int Nq) {
   if (D <= 64) return fwd::FwdCfg<64, 1, 4>::kBlockM;
   if (kv_small_block(D, Nq)) return fwd::FwdCfg<128, 1, 4>::kBlockM;

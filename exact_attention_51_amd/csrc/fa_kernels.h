@@ -50,6 +50,10 @@ struct BwdArgs {
   int causal;
 };
 
+// CUs of the current device, read from the device once and cached per
+// device (256 if the query fails); safe to call from several host threads.
+int device_cus();
+
 // Each returns 0 on a successful launch, -1 when the launch failed and -2
 // when no kernel instance exists for the shape.
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
@@ -57,6 +61,9 @@ int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // n_split workgroups per query block, then the merge of the key ranges.
 int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream);
 int launch_fwd_bf16_kv_d256(const FwdArgs& a, hipStream_t stream);  // fa_fwd_kv_d256.hip
+// Merge: up to kMaxNarrowMerge ranges with D/4 threads per row in 256-thread
+// workgroups, more ranges with one 256-thread workgroup per row.
+constexpr int kMaxNarrowMerge = 8;
 int launch_fwd_kv_merge(const FwdArgs& a, hipStream_t stream);
 // fa_decode.hip: a.N <= kDecodeMaxRows query rows per head on the vector
 // ALUs, keys split over a.n_split workgroups (same partial-result layout and
@@ -71,6 +78,8 @@ int launch_fwd_decode(const FwdArgs& a, hipStream_t stream);
 // Workgroups of the forward kernel one CU runs at a time, by head dimension.
 int fwd_workgroups_per_cu(int D);
 int fwd_rows_per_workgroup(int D, int Nq);  // query rows per workgroup of the fa_fwd_kv matrix-core path
+int fwd_threads_per_workgroup(int D, int Nq);  // threads per workgroup of the same
+constexpr int kDecodeThreads = 256;            // threads per workgroup of the decode kernel
 int launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 int launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);

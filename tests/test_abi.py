@@ -159,6 +159,31 @@ def test_forward_kv_argument_validation():
     assert lib.fa_fwd_kv_splits(1, 1, 10, 5, 64, 1) == inv
 
 
+def _no_gpu_visible():
+    """The two tests below pass sizes that only a host-side check stops; on a
+    machine with a GPU a missing check would launch on fake pointers, so they
+    run only where no GPU is visible (device_count does not initialise one)."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-side size checks are exercised on machines without a GPU")
+
+
+def test_forward_kv_work_items_checked_before_launch():
+    """HIP's grid limit is on work-items (workgroups x threads < 2^32): 2^24
+    query rows merged from 16 ranges need one 256-thread merge workgroup per
+    row, 2^32 work-items, which fa_fwd_kv rejects before the range kernel
+    runs."""
+    _no_gpu_visible()
+    lib = _lib.load()
+    nq = 1 << 24
+    need = lib.fa_fwd_kv_workspace_bytes(1, 1, nq, 32, 16)
+    assert _fwd_kv(lib, Nq=nq, Nk=nq, D=32, splits=16, ws=FAKE, ws_bytes=need) == _lib.FA_ERR_INVALID_ARG
+    # 8 ranges take the narrow merge (D/4 threads per row): it fits
+    need8 = lib.fa_fwd_kv_workspace_bytes(1, 1, nq, 32, 8)
+    assert need8 > 0
+
+
 def test_forward_sparse_argument_validation():
     lib = _lib.load()
     inv, uns = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED

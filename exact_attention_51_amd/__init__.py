@@ -18,7 +18,7 @@ import math
 from . import _lib
 from ._lib import FAError  # noqa: F401
 
-__all__ = ["fwd", "fwd_kv", "kv_splits", "fwd_sparse", "SPARSE_BLOCK", "bwd_dq", "bwd_dkdv", "bwd", "FAError", "library_path", "version"]
+__all__ = ["fwd", "fwd_kv", "fwd_kv_noalloc", "kv_splits", "fwd_sparse", "SPARSE_BLOCK", "bwd_dq", "bwd_dkdv", "bwd", "FAError", "library_path", "version"]
 
 
 def library_path() -> str:
@@ -156,6 +156,33 @@ def fwd_kv(q, k, v, scale: float | None = None, causal: bool = False, num_splits
         ws_ptr, ws_bytes, _stream_ptr(q, stream),
     )
     _lib.check("fa_fwd_kv", rc)
+    return out, lse
+
+
+def fwd_kv_noalloc(q, k, v, out, lse, scale: float | None = None, causal: bool = False, num_splits: int = 0,
+                   stream=None):
+    """``fa_fwd_kv_noalloc``: ``fwd_kv`` with the key-range partials in the
+    library's per-device scratch array instead of a workspace.  The caller
+    passes the outputs (o [B, H, Nq, D] bf16, lse [B, H, Nq] float32); the
+    call allocates nothing.  Calls that overlap on one device race on the
+    scratch.  Returns (out, lse)."""
+    torch = _torch()
+    _check_bhnd("q", q, torch.bfloat16)
+    B, H, Nq, D = q.shape
+    _check_bhnd("k", k, torch.bfloat16)
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected ({B}, {H}, Nk, {D})")
+    _check_bhnd("v", v, torch.bfloat16, k.shape)
+    _check_bhnd("out", out, torch.bfloat16, q.shape)
+    _check_rows("lse", lse, (B, H, Nq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = _lib.load().fa_fwd_kv_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+        int(num_splits), _stream_ptr(q, stream),
+    )
+    _lib.check("fa_fwd_kv_noalloc", rc)
     return out, lse
 
 

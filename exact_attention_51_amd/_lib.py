@@ -11,6 +11,7 @@ FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_LAUNCH = -3
+FA_FWD_KV_NOALLOC_MAX_BYTES = 64 << 20  # include/fa.h
 
 # name -> (restype, argtypes); must match include/fa.h exactly.
 _P = ctypes.c_void_p
@@ -20,6 +21,7 @@ SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, ctypes.c_size_t, _P]),
+    "fa_fwd_kv_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_fwd_kv_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fa_fwd_sparse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P]),
     "fa_fwd_kv_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),

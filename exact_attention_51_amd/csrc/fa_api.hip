@@ -128,7 +128,7 @@ int check_kv(int B, int H, int Nq, int Nk, int D, float scale, int causal) {
   return FA_OK;
 }
 
-// Checks of fa_fwd_kv, and the range count.
+// Checks shared by fa_fwd_kv and fa_fwd_kv_noalloc, and the range count.
 // HIP's launch limit is on work-items (workgroups x threads per workgroup
 // below 2^32), for the range kernel and for the merge: both are checked
 // here, before anything is launched.
@@ -174,6 +174,31 @@ int kv_run(const void* q, const void* k, const void* v, void* o, float* lse, int
                               : fa::launch_fwd_bf16_kv(a, (hipStream_t)stream);
   if (lrc == 0 && splits > 1) lrc = fa::launch_fwd_kv_merge(a, (hipStream_t)stream);
   return map_launch(lrc);
+}
+
+// Scratch of fa_fwd_kv_noalloc: the key-range partials of one call, in a
+// fixed array that each device holds from the library's first use on it
+// until the process ends.  In host code `scratch` only names the symbol;
+// its device address is looked up once per device (with that device
+// current) and kept in g_scratch.  Every call on one device shares the
+// array, so calls that overlap on one device race.  Nothing in it has to
+// start at zero: every range writes all of its partial rows.
+std::atomic<void*> g_scratch[fa::kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[FA_FWD_KV_NOALLOC_MAX_BYTES];
+
+namespace {
+
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= fa::kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace
@@ -227,6 +252,21 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   const size_t need = kv_workspace_bytes(B, H, Nq, D, splits);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)) return FA_ERR_INVALID_ARG;
   return kv_run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, splits, workspace, stream);
+}
+
+int fa_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                      int D, float scale, int causal, int num_splits, void* stream) {
+  int splits = 0;
+  const int rc = kv_prepare(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, num_splits, &splits);
+  if (rc != FA_OK) return rc;
+  const size_t need = kv_workspace_bytes(B, H, Nq, D, splits);
+  if (need > FA_FWD_KV_NOALLOC_MAX_BYTES) return FA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_ptr();
+    if (!ws) return FA_ERR_LAUNCH;
+  }
+  return kv_run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, splits, ws, stream);
 }
 
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,

@@ -120,6 +120,27 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
               float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_kv for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, semantics, kernels and results as fa_fwd_kv, except that
+ * the key-range partials go to a scratch array of
+ * FA_FWD_KV_NOALLOC_MAX_BYTES the library holds on each device (set up on
+ * the first call on that device, kept until the process ends) instead of
+ * a caller workspace.  The call allocates nothing.
+ *   Errors: FA_ERR_INVALID_ARG as fa_fwd_kv, and also when the partials
+ *   need more than FA_FWD_KV_NOALLOC_MAX_BYTES, i.e. when
+ *   fa_fwd_kv_workspace_bytes(B, H, Nq, D, splits) exceeds it for the
+ *   range count used (pass a smaller num_splits, or use fa_fwd_kv);
+ *   FA_ERR_LAUNCH if the scratch array's device address cannot be read.
+ * Every call on one device shares that device's scratch array: calls
+ * that overlap on one device (other streams, other host threads) race and
+ * must be ordered by the caller.  A call with one key range uses no scratch.
+ */
+#define FA_FWD_KV_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int fa_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                      int D, float scale, int causal, int num_splits, void* stream);
+
+/*
  * The key-range count fa_fwd_kv uses for num_splits = 0, at most 256.  For
  * Nq > 4 (matrix-core kernel): enough workgroups to occupy every CU of the
  * current device, at least two key tiles of 64 per range.  For Nq <= 4

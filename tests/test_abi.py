@@ -27,6 +27,7 @@ def test_header_declares_expected_entry_points():
             "fa_fwd",
             "fa_fwd_f32",
             "fa_fwd_kv",
+            "fa_fwd_kv_noalloc",
             "fa_fwd_kv_splits",
             "fa_fwd_kv_workspace_bytes",
             "fa_fwd_sparse",
@@ -182,6 +183,28 @@ def test_forward_kv_work_items_checked_before_launch():
     # 8 ranges take the narrow merge (D/4 threads per row): it fits
     need8 = lib.fa_fwd_kv_workspace_bytes(1, 1, nq, 32, 8)
     assert need8 > 0
+
+
+def test_forward_kv_noalloc_validation():
+    """The no-allocation variant rejects what fa_fwd_kv rejects and any range
+    count whose partials exceed its scratch array, before any HIP call."""
+    _no_gpu_visible()
+    lib = _lib.load()
+    inv = _lib.FA_ERR_INVALID_ARG
+
+    def call(ptrs=None, B=1, H=64, Nq=4096, Nk=8192, D=128, scale=0.125, causal=0, splits=8):
+        ptrs = ptrs or [FAKE] * 5
+        return lib.fa_fwd_kv_noalloc(*ptrs, B, H, Nq, Nk, D, scale, causal, splits, None)
+
+    assert lib.fa_fwd_kv_workspace_bytes(1, 64, 4096, 128, 8) > _lib.FA_FWD_KV_NOALLOC_MAX_BYTES
+    assert call() == inv  # partials of 8 ranges: 1.08 GB
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert call(ptrs=ptrs, H=1, Nq=16, splits=4) == inv
+    assert call(H=1, Nq=16, splits=257) == inv
+    assert call(H=1, Nq=16, splits=-1) == inv
+    assert call(H=1, Nq=8193, causal=1) == inv
 
 
 def test_forward_sparse_argument_validation():

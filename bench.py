@@ -37,8 +37,9 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd attention TFLOPS (4N²D·B·H, causal halved) + % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
-KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_bf16.h", "fa_device.h", "fa_sched.h"]
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fwd_d128_c3_traffic.json")
+# the sources of the kernel the bench workload runs (square forward, D = 128)
+KERNEL_SOURCES = ["fa_fwd_d128.hip", "fa_device.h", "fa_sched.h", "fa_kernels.h"]
 
 
 def kernel_source_hash() -> str:

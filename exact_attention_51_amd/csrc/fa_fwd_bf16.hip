@@ -48,8 +48,10 @@ int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.D == 64) return a.causal ? fwd::launch<64, true, QB, W64>(a, stream) : fwd::launch<64, false, QB, W64>(a, stream);
   if (a.D == 32)  // the D = 64 workgroup shape and LDS layout, 32 columns unused
     return a.causal ? fwd::launch<32, true, QB, W64>(a, stream) : fwd::launch<32, false, QB, W64>(a, stream);
-  if (a.D == 128)
+  if (a.D == 128) {
+    if (a.N >= 64) return launch_fwd_d128(a, stream);  // 64 rows per wave, assembly key loop
     return a.causal ? fwd::launch<128, true, QB, W128>(a, stream) : fwd::launch<128, false, QB, W128>(a, stream);
+  }
   if (a.D == 96)  // the D = 128 workgroup shape and LDS layout, 32 columns unused
     return a.causal ? fwd::launch<96, true, QB, W128>(a, stream) : fwd::launch<96, false, QB, W128>(a, stream);
   if (a.D == 256 || a.D == 160) return launch_fwd_bf16_d256(a, stream);

@@ -57,6 +57,9 @@ int device_cus();
 // Each returns 0 on a successful launch, -1 when the launch failed and -2
 // when no kernel instance exists for the shape.
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// fa_fwd_d128.hip: the square forward at D = 128 for N >= 64 (64 query rows
+// per wave, key loop in assembly).
+int launch_fwd_d128(const FwdArgs& a, hipStream_t stream);
 // fa_fwd_kv.hip: query and key lengths apart, keys optionally split over
 // n_split workgroups per query block, then the merge of the key ranges.
 int launch_fwd_bf16_kv(const FwdArgs& a, hipStream_t stream);

@@ -7,12 +7,12 @@ Run on a GPU machine from the repository root:
 Writes its summaries under gpurun_out/profile_fwd/profiles/ (the GPU machine
 keeps only gpurun_out/); `python3 profile_fwd.py --summarize` rebuilds them
 from the returned CSVs, under profiles/:
-  fwd_bf16_c3_kernel_trace.md  per-kernel durations of `bench.py --no-cpu --no-others`
-  fwd_bf16_c3_traffic.md       HBM bytes per launch of the forward kernel
-  fwd_bf16_c3_traffic.json     the same figure, keyed by a hash of the kernel
+  fwd_d128_c3_kernel_trace.md  per-kernel durations of `bench.py --no-cpu --no-others`
+  fwd_d128_c3_traffic.md       HBM bytes per launch of the forward kernel
+  fwd_d128_c3_traffic.json     the same figure, keyed by a hash of the kernel
                                sources (bench.py reports it only while the
                                hash still matches)
-  fwd_bf16_c3_counters.md      shader clock, MFMA busy, VALU/LDS activity, LDS
+  fwd_d128_c3_counters.md      shader clock, MFMA busy, VALU/LDS activity, LDS
                                bank conflicts and the instruction mix
   kernels_all_workloads.md     kernel durations of the full `bench.py --no-cpu`
                                (every workload: c2, c3, c4, c5 forward and c5
@@ -41,7 +41,7 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(ROOT, "gpurun_out", "profile_fwd")
 PROFILES = os.path.join(ROOT, "profiles")
-FWD_KERNEL = "fwd_bf16_kernel"
+FWD_KERNEL = "fwd_d128_kernel"
 COPY_BYTES = 1 << 30
 BENCH = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "30", "--warmup", "5", "--no-cpu", "--no-others"]
 # SQ counter passes (at most 8 SQ and 2 GRBM counters each)
@@ -199,7 +199,7 @@ def summarize(out: str, dest: str) -> None:
         "raw": counters,
         "command": "python3 profile_fwd.py",
     }
-    with open(os.path.join(dest, "fwd_bf16_c3_traffic.json"), "w") as f:
+    with open(os.path.join(dest, "fwd_d128_c3_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
 
     lines = ["# Forward kernel, causal B=2 H=16 N=8192 D=128 bf16: kernel trace", "",
@@ -208,7 +208,7 @@ def summarize(out: str, dest: str) -> None:
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in krows:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
-    with open(os.path.join(dest, "fwd_bf16_c3_kernel_trace.md"), "w") as f:
+    with open(os.path.join(dest, "fwd_d128_c3_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     algo = 2 * 16 * 8192 * 128 * 2 * 4 + 2 * 16 * 8192 * 4  # Q, K, V read + O written, L written
@@ -221,7 +221,7 @@ def summarize(out: str, dest: str) -> None:
              f"- algorithmic bytes (Q, K, V read once; O, L written once): {algo / 2**20:.1f} MiB",
              f"- ratio measured / algorithmic: {total / algo:.2f}",
              f"- kernel source hash: {rec['kernel_source_hash']}"]
-    with open(os.path.join(dest, "fwd_bf16_c3_traffic.md"), "w") as f:
+    with open(os.path.join(dest, "fwd_d128_c3_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     if all(os.path.isdir(os.path.join(out, n)) for n in ("sq1", "sq2")):
         summarize_counters(out, dest)
@@ -303,9 +303,11 @@ def summarize_all_workloads(out: str, dest: str) -> None:
             label, seen_c2 = "c2 fwd", True
         elif "fwd_bf16_kernel<256" in family:
             label, seen_c5 = "c5 fwd", True
-        elif "fwd_bf16_kernel<128" in family:  # bench order: c3, c2, c4, c5, the pages' shape, c3-shape bwd
+        elif "fwd_d128_kernel" in family or "fwd_bf16_kernel<128" in family:
+            # bench order: c3, c2, c4, c5, the pages' shape, c3-shape bwd
+            causal = "<true>" in family or "<128, true" in family
             if seen_c5:
-                label = "p1 causal fwd" if "<128, true" in family else "p1 fwd"
+                label = "p1 causal fwd" if causal else "p1 fwd"
                 if i + 1 < len(families) and "bwd_dq" in families[i + 1]:
                     label = "c3 bwd setup fwd"
             else:
@@ -376,8 +378,8 @@ def build_metadata_lines() -> list[str]:
     sys.path.insert(0, ROOT)
     from exact_attention_51_amd import build
 
-    src = os.path.join(ROOT, "exact_attention_51_amd", "csrc", "fa_fwd_bf16.hip")
-    cmd = [build.hipcc(), *build.COMMON_FLAGS, *build.source_flags("fa_fwd_bf16.hip"), "--offload-device-only",
+    src = os.path.join(ROOT, "exact_attention_51_amd", "csrc", "fa_fwd_d128.hip")
+    cmd = [build.hipcc(), *build.COMMON_FLAGS, *build.source_flags("fa_fwd_d128.hip"), "--offload-device-only",
            "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", os.devnull]
     try:
         err = subprocess.run(cmd, capture_output=True, text=True, timeout=600).stderr.splitlines()
@@ -385,7 +387,7 @@ def build_metadata_lines() -> list[str]:
         return []
     want = ("VGPRs:", "AGPRs:", "ScratchSize [bytes/lane]:", "Occupancy [waves/SIMD]:", "LDS Size [bytes/block]:")
     for i, line in enumerate(err):
-        if "Function Name:" in line and "fwd_bf16_kernelILi128ELb1ELi1ELi8ELb0E" in line:
+        if "Function Name:" in line and "fwd_d128_kernelILb1EE" in line:
             got = []
             for rest in err[i + 1:i + 16]:
                 if "Function Name:" in rest:
@@ -393,7 +395,7 @@ def build_metadata_lines() -> list[str]:
                 body = rest.split("remark: ")[-1].split(" [-Rpass")[0].strip()
                 if body.startswith(want):
                     got.append(body)
-            return ["- compiler resource usage of this instance (D=128, causal, 8 waves; hipcc"
+            return ["- compiler resource usage of this instance (D=128, causal, 4 waves of 64 rows; hipcc"
                     " -Rpass-analysis=kernel-resource-usage): " + "; ".join(got)]
     return []
 
@@ -455,7 +457,7 @@ def summarize_counters(out: str, dest: str) -> None:
               *tcc_lines(med),
               *build_metadata_lines(),
               f"- kernel source hash: {collected_source_hash(out)}"]
-    with open(os.path.join(dest, "fwd_bf16_c3_counters.md"), "w") as f:
+    with open(os.path.join(dest, "fwd_d128_c3_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
 

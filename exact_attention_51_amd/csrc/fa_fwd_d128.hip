@@ -201,7 +201,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
       .elseif ((\k)>>1) == 14
         s_waitcnt lgkmcnt(1)
       .else
-        s_waitcnt lgkmcnt(0)
+        s_waitcnt lgkmcnt(2)
       .endif
     .endif
     FA_SMFMA \k, ((\j)&1)
@@ -245,20 +245,20 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_lshl_b32 s83, s82, 6
     s_sub_u32 s84, s81, 64
     s_min_u32 s84, s83, s84
-    v_add_u32 v176, s84, v222
-    v_sub_u32 v177, s83, v176
-    v_sub_u32 v178, v220, v176
-    v_sub_u32 v179, v221, v176
-    v_sub_u32 v178, v178, v177
-    v_max_i32 v178, 0, v178
-    v_sub_u32 v179, v179, v177
-    v_max_i32 v179, 0, v179
+    v_add_u32 v228, s84, v222
+    v_sub_u32 v229, s83, v228
+    v_sub_u32 v230, v220, v228
+    v_sub_u32 v231, v221, v228
+    v_sub_u32 v230, v230, v229
+    v_max_i32 v230, 0, v230
+    v_sub_u32 v231, v231, v229
+    v_max_i32 v231, 0, v231
     .irp kb, 0, 1
       .irp r, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15
-        v_sub_u32 v180, (\kb)*32+((\r)>>2)*8+((\r)&3), v177
-        v_cmp_gt_u32 vcc, v178, v180
+        v_sub_u32 v232, (\kb)*32+((\r)>>2)*8+((\r)&3), v229
+        v_cmp_gt_u32 vcc, v230, v232
         v_cndmask_b32 v[(\c)*64+(\kb)*32+(\r)], v223, v[(\c)*64+(\kb)*32+(\r)], vcc
-        v_cmp_gt_u32 vcc, v179, v180
+        v_cmp_gt_u32 vcc, v231, v232
         v_cndmask_b32 v[(\c)*64+(\kb)*32+16+(\r)], v223, v[(\c)*64+(\kb)*32+16+(\r)], vcc
       .endr
     .endr
@@ -275,9 +275,6 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_barrier
     v_mul_f32_e64 v198, -v192, s79
     v_mul_f32_e64 v199, -v193, s79
-    FA_VREAD 0, (\j)
-    FA_VREAD 1, (\j)
-    FA_VREAD 2, (\j)
     // P V half: positions 0..31
     .irp t, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
       .if ((\t)&1) == 0
@@ -304,6 +301,9 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
       FA_VPOS \t, (((\j)+1)&1)
       .if (\t) >= 62
         FA_REFILL ((\t)-62), \j
+      .endif
+      .if (\t) >= 69
+        FA_VREAD ((\t)-69), (((\j)+1)&3)
       .endif
     .endr
     v_accvgpr_read_b32 v196, a192
@@ -353,47 +353,47 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_nop 7
     s_nop 7
     .irp qb, 0, 1
-      v_max3_f32 v176, v[(((\j)+1)&1)*64+(\qb)*16], v[(((\j)+1)&1)*64+(\qb)*16+1], v[(((\j)+1)&1)*64+(\qb)*16+2]
+      v_max3_f32 v228, v[(((\j)+1)&1)*64+(\qb)*16], v[(((\j)+1)&1)*64+(\qb)*16+1], v[(((\j)+1)&1)*64+(\qb)*16+2]
       .irp r, 3, 5, 7, 9, 11, 13
-        v_max3_f32 v176, v176, v[(((\j)+1)&1)*64+(\qb)*16+(\r)], v[(((\j)+1)&1)*64+(\qb)*16+(\r)+1]
+        v_max3_f32 v228, v228, v[(((\j)+1)&1)*64+(\qb)*16+(\r)], v[(((\j)+1)&1)*64+(\qb)*16+(\r)+1]
       .endr
-      v_max_f32 v176, v176, v[(((\j)+1)&1)*64+(\qb)*16+15]
+      v_max_f32 v228, v228, v[(((\j)+1)&1)*64+(\qb)*16+15]
       .irp r, 0, 2, 4, 6, 8, 10, 12, 14
-        v_max3_f32 v176, v176, v[(((\j)+1)&1)*64+32+(\qb)*16+(\r)], v[(((\j)+1)&1)*64+32+(\qb)*16+(\r)+1]
+        v_max3_f32 v228, v228, v[(((\j)+1)&1)*64+32+(\qb)*16+(\r)], v[(((\j)+1)&1)*64+32+(\qb)*16+(\r)+1]
       .endr
-      v_mov_b32 v177, v176
+      v_mov_b32 v229, v228
       s_nop 1
-      v_permlane32_swap_b32 v176, v177
+      v_permlane32_swap_b32 v228, v229
       s_nop 1
-      v_max_f32 v[186+(\qb)], v176, v177
+      v_max_f32 v[233+(\qb)], v228, v229
     .endr
     .irp qb, 0, 1
-      v_max_f32 v188, v[192+(\qb)], v[186+(\qb)]
-      v_sub_f32 v189, v188, v[192+(\qb)]
-      v_mul_f32 v189, s79, v189
-      v_cmp_lt_f32 vcc, 0x41000000, v189
+      v_max_f32 v235, v[192+(\qb)], v[233+(\qb)]
+      v_sub_f32 v236, v235, v[192+(\qb)]
+      v_mul_f32 v236, s79, v236
+      v_cmp_lt_f32 vcc, 0x41000000, v236
       s_and_b64 vcc, exec, vcc
       s_cbranch_vccz L_keep_\j\()_\uid\()_\qb
-      v_sub_f32 v189, v[192+(\qb)], v188
-      v_mul_f32 v189, s79, v189
-      v_exp_f32 v189, v189
+      v_sub_f32 v236, v[192+(\qb)], v235
+      v_mul_f32 v236, s79, v236
+      v_exp_f32 v236, v236
       s_nop 1
       .irp r, 0,4,8,12,16,20,24,28,32,36,40,44,48,52,56,60
-        v_accvgpr_read_b32 v176, a[(\qb)*64+(\r)]
-        v_accvgpr_read_b32 v177, a[(\qb)*64+(\r)+1]
-        v_accvgpr_read_b32 v178, a[(\qb)*64+(\r)+2]
-        v_accvgpr_read_b32 v179, a[(\qb)*64+(\r)+3]
-        v_mul_f32 v176, v176, v189
-        v_mul_f32 v177, v177, v189
-        v_mul_f32 v178, v178, v189
-        v_mul_f32 v179, v179, v189
-        v_accvgpr_write_b32 a[(\qb)*64+(\r)], v176
-        v_accvgpr_write_b32 a[(\qb)*64+(\r)+1], v177
-        v_accvgpr_write_b32 a[(\qb)*64+(\r)+2], v178
-        v_accvgpr_write_b32 a[(\qb)*64+(\r)+3], v179
+        v_accvgpr_read_b32 v228, a[(\qb)*64+(\r)]
+        v_accvgpr_read_b32 v229, a[(\qb)*64+(\r)+1]
+        v_accvgpr_read_b32 v230, a[(\qb)*64+(\r)+2]
+        v_accvgpr_read_b32 v231, a[(\qb)*64+(\r)+3]
+        v_mul_f32 v228, v228, v236
+        v_mul_f32 v229, v229, v236
+        v_mul_f32 v230, v230, v236
+        v_mul_f32 v231, v231, v236
+        v_accvgpr_write_b32 a[(\qb)*64+(\r)], v228
+        v_accvgpr_write_b32 a[(\qb)*64+(\r)+1], v229
+        v_accvgpr_write_b32 a[(\qb)*64+(\r)+2], v230
+        v_accvgpr_write_b32 a[(\qb)*64+(\r)+3], v231
       .endr
-      v_mul_f32 v[194+(\qb)], v[194+(\qb)], v189
-      v_mov_b32 v[192+(\qb)], v188
+      v_mul_f32 v[194+(\qb)], v[194+(\qb)], v236
+      v_mov_b32 v[192+(\qb)], v235
     L_keep_\j\()_\uid\()_\qb:
     .endr
     v_mul_f32_e64 v198, -v192, s79
@@ -438,7 +438,11 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     v_accvgpr_write_b32 a[\r], 0
     v_accvgpr_write_b32 a[64+(\r)], 0
   .endr
-  s_nop 2
+  s_waitcnt vmcnt(16)
+  s_barrier
+  FA_VREAD 0, 0
+  FA_VREAD 1, 0
+  FA_VREAD 2, 0
 L_loop_%=:
   FA_STEP 0, %=
   FA_STEP 1, %=
@@ -458,6 +462,7 @@ L_loop_%=:
   FA_WALL 2, %=
   FA_WALL 3, %=
 L_done_%=:
+  s_waitcnt lgkmcnt(0)
   s_nop 7
   s_nop 7
   s_nop 7
@@ -667,31 +672,44 @@ fwd_d128_kernel(FwdArgs a, TileSched sched) {
                  "{v[200:207]}"(koff), "{v[208:215]}"(voff), "{v[216:219]}"(cpoff), "{v220}"(bound0), "{v221}"(bound1),
                  "{v222}"(half4), "{v[224:227]}"(rsel), "{s[70:71]}"(Ks), "{s[72:73]}"(Vs), "{s75}"(nt_s), "{s76}"(R_s), "{s77}"(fm_s),
                  "{s78}"(ltb_s), "{s79}"(cs), "{s80}"(ring_wave), "{s81}"(N_s)
-               : "v223", "s82", "s83", "s84", "s85", "s86", "s87", "s88", "s89", "m0", "vcc", "exec", "scc",
+               : "v223", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "s82", "s83", "s84", "s85", "s86", "s87", "s88", "s89", "m0", "vcc", "exec", "scc",
                  "memory");
   wait_vmcnt<0>();  // no direct-to-LDS copy may outlive the workgroup
 
-  // ---- epilogue: O = acc / l, L = m*scale + ln l
+  // ---- epilogue: O = acc / l, L = m*scale + ln l.  Each wave stages its
+  // 64 x 128 bf16 block of O in its own 16 KB of the (now idle) ring, rows of
+  // 256 bytes with the 16-byte chunks XOR-swizzled by row, and stores it back
+  // in whole rows: a lane's fragment holds 8 bytes of 32 different rows,
+  // which stored directly would split every store into 32 row pieces.
+  __syncthreads();  // every wave is past its last read of the ring
   __bf16* __restrict__ O = (__bf16*)a.o + head_off;
   float* __restrict__ Lse = a.lse + (size_t)bh * N;
+  lds_char* ostage = smem + wave * (64 * D * 2);
   const f32x32 ob[2][2] = {{o0, o1}, {o2, o3}};
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = l[qb];
     const float inv = 1.0f / lt;
-    const int row = wq0 + qb * 32 + l32;
-    if (row < N) {
+    const int r = qb * 32 + l32;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x32& x = ob[qb][db >> 1];
-          const int e = (db & 1) * 16 + g4 * 4;
-          u32x2 w = {pack_bf16_u32(x[e + 0] * inv, x[e + 1] * inv), pack_bf16_u32(x[e + 2] * inv, x[e + 3] * inv)};
-          *(u32x2*)(O + (size_t)row * D + db * 32 + g4 * 8 + half * 4) = w;
-        }
-      if (half == 0) Lse[row] = m[qb] * a.scale + fast_log2(lt) * kLn2;
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x32& x = ob[qb][db >> 1];
+        const int e = (db & 1) * 16 + g4 * 4;
+        const u32x2 w = {pack_bf16_u32(x[e + 0] * inv, x[e + 1] * inv), pack_bf16_u32(x[e + 2] * inv, x[e + 3] * inv)};
+        const int chunk = db * 4 + g4;
+        *(u32x2 __attribute__((address_space(3)))*)(ostage + r * (D * 2) + ((chunk ^ (r & 15)) << 4) + half * 8) = w;
+      }
+    const int row = wq0 + r;
+    if (row < N && half == 0) Lse[row] = m[qb] * a.scale + fast_log2(lt) * kLn2;
+  }
+  // the block back in rows: lanes 16k .. 16k+15 hold one 256-byte row
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = k * 4 + (lane >> 4), c = lane & 15;
+    const u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(ostage + r * (D * 2) + ((c ^ (r & 15)) << 4));
+    if (wq0 + r < N) *(u32x4*)(O + (size_t)(wq0 + r) * D + c * 8) = v;
   }
 }
 

@@ -75,6 +75,7 @@ constexpr int kBlockN = 64;              // keys per tile
 constexpr int kTileBytes = kBlockN * D * 2;
 constexpr int kNB = 4;                   // ring slots per tensor
 constexpr int kRingBytes = 2 * kNB * kTileBytes;
+constexpr int kStageBytes = kWaves * 32 * D * 2;  // epilogue staging, 32 rows per wave
 constexpr float kMaxFloor = 1.0e30f;     // the running max starts at -kMaxFloor
 
 typedef __attribute__((ext_vector_type(32))) float f32x32;
@@ -162,16 +163,19 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   .endm
   // ring refill piece r of step p (slot j = p mod 4): 0 = address of K(p+4),
   // 1..4 = its four copies into slot j, 5 = address of V(p+3), 6..9 = its
-  // copies into V slot (j+3) mod 4.  A copy of a position past the block's
-  // last tile runs with no lane active (s[88:89] = 0), so it moves nothing.
-  .macro FA_REFILL r, j
+  // copies into V slot (j+3) mod 4.  A position past the block's last tile
+  // is the next block's tile (position minus nt) when the workgroup has one,
+  // computed out of line; else its copies run with no lane active.
+  .macro FA_REFILL r, j, uid
     .if (\r) == 0
       s_add_u32 s82, s74, 4
       s_cmp_lt_u32 s82, s75
-      s_cselect_b64 s[88:89], -1, 0
+      s_cbranch_scc0 L_kn_\j\()_\uid
       FA_TILE_BYTES
       s_add_u32 s86, s70, s82
       s_addc_u32 s87, s71, 0
+      s_mov_b64 s[88:89], -1
+    L_kr_\j\()_\uid:
     .elseif (\r) <= 4
       s_add_u32 m0, s80, (\j)*16384+((\r)-1)*1024
       s_mov_b64 exec, s[88:89]
@@ -180,15 +184,48 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     .elseif (\r) == 5
       s_add_u32 s82, s74, 3
       s_cmp_lt_u32 s82, s75
-      s_cselect_b64 s[88:89], -1, 0
+      s_cbranch_scc0 L_vn_\j\()_\uid
       FA_TILE_BYTES
       s_add_u32 s86, s72, s82
       s_addc_u32 s87, s73, 0
+      s_mov_b64 s[88:89], -1
+    L_vr_\j\()_\uid:
     .else
       s_add_u32 m0, s80, 65536+((((\j)+3)&3)*16384)+((\r)-6)*1024
       s_mov_b64 exec, s[88:89]
       global_load_lds_dwordx4 v[216+(\r)-6], s[86:87]
       s_mov_b64 exec, -1
+    .endif
+  .endm
+  // out of line: the byte offset of the next block's tile at position
+  // s82 - nt (its masked tiles first, as for every block), on the next
+  // block's K (kv = 0) or V (kv = 1); no lane active without a next block
+  .macro FA_RNEXT kv, j, uid
+    .if (\kv) == 0
+    L_kn_\j\()_\uid:
+    .else
+    L_vn_\j\()_\uid:
+    .endif
+    s_sub_u32 s82, s82, s75
+    s_add_u32 s83, s82, s95
+    s_sub_u32 s84, s82, s94
+    s_cmp_lt_u32 s82, s94
+    s_cselect_b32 s82, s83, s84
+    s_lshl_b32 s82, s82, 14
+    s_min_u32 s82, s82, s78
+    .if (\kv) == 0
+      s_add_u32 s86, s90, s82
+      s_addc_u32 s87, s91, 0
+    .else
+      s_add_u32 s86, s92, s82
+      s_addc_u32 s87, s93, 0
+    .endif
+    s_cmp_lg_u32 s96, 0
+    s_cselect_b64 s[88:89], -1, 0
+    .if (\kv) == 0
+      s_branch L_kr_\j\()_\uid
+    .else
+      s_branch L_vr_\j\()_\uid
     .endif
   .endm
   // the score-half MFMA at step position t (32..71): row-sum MFMAs at 32..35,
@@ -300,7 +337,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
       FA_SPOS \t, \j
       FA_VPOS \t, (((\j)+1)&1)
       .if (\t) >= 62
-        FA_REFILL ((\t)-62), \j
+        FA_REFILL ((\t)-62), \j, \uid
       .endif
       .if (\t) >= 69
         FA_VREAD ((\t)-69), (((\j)+1)&3)
@@ -426,11 +463,24 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_branch L_mret_\j\()_\uid
   .endm
 
-  // ---- out of line: the last two steps wait for every copy in flight
+  // ---- out of line: the last two steps of the workgroup's last block wait
+  // for every copy in flight (copies with no lane active may not count)
   .macro FA_WALL j, uid
   L_wall_\j\()_\uid:
+    s_cmp_lg_u32 s96, 0
+    s_cbranch_scc1 L_wnext_\j\()_\uid
     s_waitcnt vmcnt(0)
     s_branch L_wret_\j\()_\uid
+  L_wnext_\j\()_\uid:
+    s_waitcnt vmcnt(8)
+    s_branch L_wret_\j\()_\uid
+  .endm
+  // score sets swapped on entry at an odd ring slot: tile 1's scores belong
+  // in set 0
+  .macro FA_SWAPSETS
+    .irp r, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31,32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63
+      v_mov_b32 v[\r], v[64+(\r)]
+    .endr
   .endm
 
   s_waitcnt lgkmcnt(0)
@@ -440,15 +490,43 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   .endr
   s_waitcnt vmcnt(16)
   s_barrier
+  // enter the unrolled ring at the block's first slot (s97)
+  s_cmp_eq_u32 s97, 1
+  s_cbranch_scc1 L_e1_%=
+  s_cmp_eq_u32 s97, 2
+  s_cbranch_scc1 L_e2_%=
+  s_cmp_eq_u32 s97, 3
+  s_cbranch_scc1 L_e3_%=
   FA_VREAD 0, 0
   FA_VREAD 1, 0
   FA_VREAD 2, 0
-L_loop_%=:
+  s_branch L_s0_%=
+L_e1_%=:
+  FA_SWAPSETS
+  FA_VREAD 0, 1
+  FA_VREAD 1, 1
+  FA_VREAD 2, 1
+  s_branch L_s1_%=
+L_e2_%=:
+  FA_VREAD 0, 2
+  FA_VREAD 1, 2
+  FA_VREAD 2, 2
+  s_branch L_s2_%=
+L_e3_%=:
+  FA_SWAPSETS
+  FA_VREAD 0, 3
+  FA_VREAD 1, 3
+  FA_VREAD 2, 3
+  s_branch L_s3_%=
+L_s0_%=:
   FA_STEP 0, %=
+L_s1_%=:
   FA_STEP 1, %=
+L_s2_%=:
   FA_STEP 2, %=
+L_s3_%=:
   FA_STEP 3, %=
-  s_branch L_loop_%=
+  s_branch L_s0_%=
   FA_RARE 0, %=
   FA_RARE 1, %=
   FA_RARE 2, %=
@@ -461,6 +539,10 @@ L_loop_%=:
   FA_WALL 1, %=
   FA_WALL 2, %=
   FA_WALL 3, %=
+  .irp jj, 0, 1, 2, 3
+    FA_RNEXT 0, \jj, %=
+    FA_RNEXT 1, \jj, %=
+  .endr
 L_done_%=:
   s_waitcnt lgkmcnt(0)
   s_nop 7
@@ -483,64 +565,64 @@ L_done_%=:
   .purgem FA_RARE
   .purgem FA_MASK
   .purgem FA_WALL
+  .purgem FA_SWAPSETS
+  .purgem FA_RNEXT
 )ASM"
+
+// One work item: a block of kRows query rows of one (batch, head), its key
+// tiles in processing order -- the R tiles that need the elementwise mask
+// (the causal diagonal region, or a ragged last tile) first, then tiles 0..
+struct Block {
+  int qtile, bh;
+  int nt;  // key tiles visited
+  int fm;  // first masked tile
+  int R;   // masked tiles
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ Block make_block(const TileSched& sched, int hw, int N) {
+  Block k;
+  sched_item(sched, hw, k.qtile, k.bh);
+  const int q0 = k.qtile * kRows;
+  const int n_ktiles = (N + kBlockN - 1) / kBlockN;
+  k.nt = n_ktiles;
+  if constexpr (CAUSAL) k.nt = min(q0 + kRows - 1, N - 1) / kBlockN + 1;
+  k.fm = k.nt;
+  if (CAUSAL) k.fm = q0 / kBlockN;
+  else if (N % kBlockN != 0) k.fm = n_ktiles - 1;
+  k.R = k.nt - k.fm;
+  return k;
+}
+
+// The blocks of workgroup w.  With one block per workgroup (cont == 0) that
+// is block w.  Persistent (cont != 0, gridDim.x a multiple of 8): round r
+// gives workgroup w = 8u + x the block 8 * (u, or U-1-u in odd rounds) + x of
+// the r-th run of gridDim.x blocks in scheduler order (U = gridDim.x / 8), so
+// a workgroup keeps to the heads of its XCD (x = w mod 8, where the
+// dispatcher places it) and, since the scheduler orders a causal grid
+// heaviest first, alternate rounds pair heavy blocks with light ones.
+__device__ __forceinline__ int block_of(int w, int round, int n_blocks, int cont) {
+  if (!cont) return round == 0 ? w : -1;
+  const int G = (int)gridDim.x, U = G >> 3, x = w & 7, u = w >> 3;
+  const int hw = round * G + 8 * ((round & 1) ? U - 1 - u : u) + x;
+  return hw < n_blocks ? hw : -1;
+}
 
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves), amdgpu_waves_per_eu(1, 1))) void
-fwd_d128_kernel(FwdArgs a, TileSched sched) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kRingBytes];
+fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRingBytes + kStageBytes];
   lds_char* smem = (lds_char*)smem_raw;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-
-  int qtile, bh;
-  sched_item(sched, blockIdx.x, qtile, bh);
   const int N = a.N;
-  const size_t head_off = (size_t)bh * N * D;
-  const __bf16* __restrict__ Q = (const __bf16*)a.q + head_off;
-  const __bf16* __restrict__ K = (const __bf16*)a.k + head_off;
-  const __bf16* __restrict__ V = (const __bf16*)a.v + head_off;
-  const int q0 = qtile * kRows;
-  const int wq0 = q0 + wave * 64;
-
-  // key tiles the block sees, and the processing order: the R tiles that
-  // need the elementwise mask (the causal diagonal region, or a ragged last
-  // tile) first, then tiles 0.. in order
-  const int n_ktiles = (N + kBlockN - 1) / kBlockN;
-  int nt = n_ktiles;
-  if constexpr (CAUSAL) nt = min(q0 + kRows - 1, N - 1) / kBlockN + 1;
-  int first_masked = nt;
-  if (CAUSAL) first_masked = q0 / kBlockN;
-  else if (N % kBlockN != 0) first_masked = n_ktiles - 1;
-  const int R = nt - first_masked;
   const uint32_t last_tile_bytes = (uint32_t)(N - kBlockN) * (D * 2);
-  auto seq_tile = [&](int p) { return p < R ? first_masked + p : p - R; };
-  auto tile_bytes = [&](int p) { return min((uint32_t)seq_tile(p) * (uint32_t)kTileBytes, last_tile_bytes); };
+  const int w = (int)blockIdx.x;
 
   // ring copies: K slots at [0, 64 KB), V slots at [64 KB, 128 KB)
   RowTileCopier<D, D, kBlockN, kWaves> cp;
   cp.init(wave, lane);
-  auto issue_k = [&](int p, int b) { cp.copy_at(K, tile_bytes(p), smem + b * kTileBytes); };
-  auto issue_v = [&](int p, int b) { cp.copy_at(V, tile_bytes(p), smem + (kNB + b) * kTileBytes); };
-  // Q^T fragments: query column l32 of each block, d = ds*16 + half*8 .. +7
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = min(wq0 + qb * 32 + l32, N - 1);
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds) qf[qb][ds] = *(const bf16x8*)(Q + (size_t)row * D + ds * 16 + half * 8);
-  }
-  // then every prologue copy, in the order the first steps need them: K0
-  // K1 V0 K2 V1 K3 V2 (positions past the last tile load a valid tile that
-  // is never read)
-  issue_k(0, 0);
-  issue_k(1, 1);
-  issue_v(0, 0);
-  issue_k(2, 2);
-  issue_v(1, 1);
-  issue_k(3, 3);
-  issue_v(2, 2);
   // per-lane LDS addresses of the K and V fragments (ring base included)
   const uint32_t ring = (uint32_t)(uintptr_t)smem;
   i32x8 koff, voff;
@@ -557,13 +639,7 @@ fwd_d128_kernel(FwdArgs a, TileSched sched) {
         voff[db * 2 + t] = (int)ring + kNB * kTileBytes + lds_off_bytes<D>(r1 + 8 * t, dcol >> 3) + (dcol & 7) * 2;
     }
   }
-  i32x4 cpoff = {(int)cp.off[0], (int)cp.off[1], (int)cp.off[2], (int)cp.off[3]};
-  // causal bound of each query block: keys < bound are visible
-  int bound0 = N, bound1 = N;
-  if constexpr (CAUSAL) {
-    bound0 = min(N, wq0 + l32 + 1);
-    bound1 = min(N, wq0 + 32 + l32 + 1);
-  }
+  const i32x4 cpoff = {(int)cp.off[0], (int)cp.off[1], (int)cp.off[2], (int)cp.off[3]};
   const int half4 = half * 4;
   // A operand of the row-sum MFMAs: bf16 ones where ((lane mod 16) / 4) mod 2
   // equals (lane / 16) mod 2, zeros elsewhere
@@ -571,161 +647,244 @@ fwd_d128_kernel(FwdArgs a, TileSched sched) {
   const i32x4 rsel = {rsel1, rsel1, rsel1, rsel1};
   const float c = a.scale_log2;
 
-  // scores of the tile at position p from K ring slot b, masked when p < R
-  auto scores = [&](int b, int p, f32x16 (&s)[2][2]) {
+  auto head = [&](const __bf16* t, int bh) { return t + (size_t)bh * N * D; };
+  auto tile_bytes = [&](const Block& k, int p) {
+    const int t = p < k.R ? k.fm + p : p - k.R;
+    return min((uint32_t)t * (uint32_t)kTileBytes, last_tile_bytes);
+  };
+  // Q^T fragments of a block: query column l32 of each 32-row group, d = ds*16 + half*8 .. +7
+  bf16x8 qf[2][8];
+  auto load_q = [&](const Block& k) {
+    const __bf16* __restrict__ Q = head((const __bf16*)a.q, k.bh);
+    const int wq0 = k.qtile * kRows + wave * 64;
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds)
+    for (int qb = 0; qb < 2; ++qb) {
+      const int row = min(wq0 + qb * 32 + l32, N - 1);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf =
-            *(const bf16x8 __attribute__((address_space(3)))*)(smem + b * kTileBytes + koff[ds] - ring + kb * 32 * D * 2);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(kf, qf[qb][ds], ds == 0 ? f32x16{} : s[kb][qb]);
-      }
-    if (p < R) {
-      // -inf where a key is invisible (the loop's mask rule)
-      const int t = seq_tile(p);
-      const int row0 = min(t * kBlockN, N - kBlockN);
-      const int base = row0 + half4, lo = t * kBlockN - base;
-      const int hi[2] = {bound0 - base, bound1 - base};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
-            s[kb][qb][r] = (off >= lo && off < hi[qb]) ? s[kb][qb][r] : -__builtin_inff();
-          }
+      for (int ds = 0; ds < 8; ++ds) qf[qb][ds] = *(const bf16x8*)(Q + (size_t)row * D + ds * 16 + half * 8);
     }
   };
 
-  // tile 0: scores, the running max (its row max; a finite floor where a
-  // row sees none of its keys), P and the row sums over the rounded P
+  int round = 0;
+  Block cur = make_block<CAUSAL>(sched, block_of(w, 0, n_blocks, cont), N);
+  // the first block: its Q rows, then its prologue copies in the order the
+  // first steps need them, K0 K1 V0 K2 V1 K3 V2 (positions past its last
+  // tile load a valid tile that is never read).  Later blocks find theirs
+  // in the ring, copied by the steps of the block before.
+  load_q(cur);
+  {
+    const __bf16* K = head((const __bf16*)a.k, cur.bh);
+    const __bf16* V = head((const __bf16*)a.v, cur.bh);
+    auto issue_k = [&](int p) { cp.copy_at(K, tile_bytes(cur, p), smem + p * kTileBytes); };
+    auto issue_v = [&](int p) { cp.copy_at(V, tile_bytes(cur, p), smem + (kNB + p) * kTileBytes); };
+    issue_k(0);
+    issue_k(1);
+    issue_v(0);
+    issue_k(2);
+    issue_v(1);
+    issue_k(3);
+    issue_v(2);
+  }
   wait_vmcnt<5 * RowTileCopier<D, D, kBlockN, kWaves>::kLoads>();  // Q, K0 and K1 landed
-  __syncthreads();
-  f32x16 s0[2][2], s1[2][2];
-  scores(0, 0, s0);
-  float m[2], l[2];
-  bf16x8 p0[2][2][2];  // [qb][kb][cc]
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  int r0 = 0;  // ring slot of the block's first tile
+
+  for (;;) {
+    const int hw_next = block_of(w, round + 1, n_blocks, cont);
+    const bool has_next = hw_next >= 0;
+    const Block nxt = has_next ? make_block<CAUSAL>(sched, hw_next, N) : cur;
+    const int wq0 = cur.qtile * kRows + wave * 64;
+    // causal bound of each query block: keys < bound are visible
+    int bound0 = N, bound1 = N;
+    if constexpr (CAUSAL) {
+      bound0 = min(N, wq0 + l32 + 1);
+      bound1 = min(N, wq0 + 32 + l32 + 1);
+    }
+
+    // scores of the tile at position p from K ring slot b, masked when p < R
+    auto scores = [&](int b, int p, f32x16 (&s)[2][2]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float t = -kMaxFloor;
+      for (int ds = 0; ds < 8; ++ds)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf =
+              *(const bf16x8 __attribute__((address_space(3)))*)(smem + b * kTileBytes + koff[ds] - ring + kb * 32 * D * 2);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t = __builtin_fmaxf(t, s0[kb][qb][r]);
-    m[qb] = max_halves(t);
-    const float nmc = -m[qb] * c;
-    float lt = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        bf16x2 pr[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pr[w] = pack_bf16(fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w], c, nmc)),
-                            fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w + 1], c, nmc)));
-          lt = __builtin_amdgcn_fdot2_f32_bf16(pr[w], ones, lt, false);
+          for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(kf, qf[qb][ds], ds == 0 ? f32x16{} : s[kb][qb]);
         }
-        p0[qb][kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
+      if (p < cur.R) {
+        // -inf where a key is invisible (the loop's mask rule)
+        const int t = cur.fm + p;
+        const int row0 = min(t * kBlockN, N - kBlockN);
+        int base = row0 + half4;
+        // (kept opaque: hoisted out of the block loop, the 64 comparisons
+        // would each hold an SGPR pair for the kernel's whole life)
+        asm volatile("" : "+v"(base));
+        const int lo = t * kBlockN - base;
+        const int hi[2] = {bound0 - base, bound1 - base};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+              s[kb][qb][r] = (off >= lo && off < hi[qb]) ? s[kb][qb][r] : -__builtin_inff();
+            }
       }
-    l[qb] = sum_halves(lt);  // every lane holds its row's whole sum, as the row-sum MFMAs give it
-  }
-  // the scores of tile 1
-  scores(1, 1, s1);
+    };
 
-  f32x32 o0, o1, o2, o3;                 // O^T: a[0:31] (qb 0, db 0-1) .. a[96:127] (qb 1, db 2-3)
-  f32x32 junk0, junk1;                   // registers the loop uses internally
-  f32x16 junk2, junk3;
-  f32x4 junk4;
-  f32x8 junk5;
-  // scalar operands of the loop, pinned to SGPRs (all are wave-uniform)
-  auto sgpr = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
-  auto sgpr_ptr = [](const __bf16* x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)x);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)x >> 32));
-    return (const __bf16*)(((uint64_t)hi << 32) | (uint64_t)lo);
-  };
-  int p = sgpr(0);
-  const int ring_wave = sgpr((int)ring + (int)cp.lds_wave);
-  const float cs = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, c)));
-  const __bf16* Ks = sgpr_ptr(K);
-  const __bf16* Vs = sgpr_ptr(V);
-  const int nt_s = sgpr(nt), R_s = sgpr(R), fm_s = sgpr(first_masked), N_s = sgpr(N);
-  const int ltb_s = sgpr((int)last_tile_bytes);
-  asm volatile(FA_D128_LOOP_ASM
-               : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
-                 "=&{v[0:31]}"(junk0), "+{v[64:79]}"(s1[0][0]), "+{v[80:95]}"(s1[0][1]), "+{v[96:111]}"(s1[1][0]),
-                 "+{v[112:127]}"(s1[1][1]), "+{v[128:131]}"(p0[0][0][0]), "+{v[132:135]}"(p0[0][0][1]),
-                 "+{v[136:139]}"(p0[0][1][0]), "+{v[140:143]}"(p0[0][1][1]), "+{v[144:147]}"(p0[1][0][0]),
-                 "+{v[148:151]}"(p0[1][0][1]), "+{v[152:155]}"(p0[1][1][0]), "+{v[156:159]}"(p0[1][1][1]),
-                 "+{v192}"(m[0]), "+{v193}"(m[1]), "+{v194}"(l[0]), "+{v195}"(l[1]), "+{s74}"(p),
-                 "=&{v[32:63]}"(junk1), "=&{v[160:175]}"(junk2), "=&{v[176:191]}"(junk3), "=&{v[196:199]}"(junk4),
-                 "=&{a[192:199]}"(junk5)
-               : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]), "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
-                 "{a[144:147]}"(qf[0][4]), "{a[148:151]}"(qf[0][5]), "{a[152:155]}"(qf[0][6]), "{a[156:159]}"(qf[0][7]),
-                 "{a[160:163]}"(qf[1][0]), "{a[164:167]}"(qf[1][1]), "{a[168:171]}"(qf[1][2]), "{a[172:175]}"(qf[1][3]),
-                 "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]), "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
-                 "{v[200:207]}"(koff), "{v[208:215]}"(voff), "{v[216:219]}"(cpoff), "{v220}"(bound0), "{v221}"(bound1),
-                 "{v222}"(half4), "{v[224:227]}"(rsel), "{s[70:71]}"(Ks), "{s[72:73]}"(Vs), "{s75}"(nt_s), "{s76}"(R_s), "{s77}"(fm_s),
-                 "{s78}"(ltb_s), "{s79}"(cs), "{s80}"(ring_wave), "{s81}"(N_s)
-               : "v223", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "s82", "s83", "s84", "s85", "s86", "s87", "s88", "s89", "m0", "vcc", "exec", "scc",
-                 "memory");
+    // tile 0: scores, the running max (its row max; a finite floor where a
+    // row sees none of its keys), P and the row sums over the rounded P.
+    // Every wave's copies of tiles 0 and 1 have landed (waited for above,
+    // or at the start of the previous block's last step).
+    __syncthreads();
+    f32x16 s0[2][2], s1[2][2];
+    scores(r0, 0, s0);
+    float m[2], l[2];
+    bf16x8 p0[2][2][2];  // [qb][kb][cc]
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float t = -kMaxFloor;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t = __builtin_fmaxf(t, s0[kb][qb][r]);
+      m[qb] = max_halves(t);
+      const float nmc = -m[qb] * c;
+      float lt = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x2 pr[4];
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) {
+            pr[w4] = pack_bf16(fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w4], c, nmc)),
+                               fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w4 + 1], c, nmc)));
+            lt = __builtin_amdgcn_fdot2_f32_bf16(pr[w4], ones, lt, false);
+          }
+          p0[qb][kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
+        }
+      l[qb] = sum_halves(lt);  // every lane holds its row's whole sum, as the row-sum MFMAs give it
+    }
+    // the scores of tile 1
+    scores((r0 + 1) & 3, 1, s1);
+
+    f32x32 o0, o1, o2, o3;  // O^T: a[0:31] (qb 0, db 0-1) .. a[96:127] (qb 1, db 2-3)
+    f32x32 junk0, junk1;    // registers the loop uses internally
+    f32x16 junk2, junk3;
+    f32x4 junk4;
+    f32x8 junk5;
+    // scalar operands of the loop, pinned to SGPRs (all are wave-uniform)
+    auto sgpr = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    auto sgpr_ptr = [](const __bf16* x) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)x);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)x >> 32));
+      return (const __bf16*)(((uint64_t)hi << 32) | (uint64_t)lo);
+    };
+    int p = sgpr(0);
+    const int ring_wave = sgpr((int)ring + (int)cp.lds_wave);
+    const float cs = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, c)));
+    const __bf16* Ks = sgpr_ptr(head((const __bf16*)a.k, cur.bh));
+    const __bf16* Vs = sgpr_ptr(head((const __bf16*)a.v, cur.bh));
+    const __bf16* Kn = sgpr_ptr(head((const __bf16*)a.k, nxt.bh));
+    const __bf16* Vn = sgpr_ptr(head((const __bf16*)a.v, nxt.bh));
+    const int nt_s = sgpr(cur.nt), R_s = sgpr(cur.R), fm_s = sgpr(cur.fm), N_s = sgpr(N);
+    const int ltb_s = sgpr((int)last_tile_bytes);
+    const int Rn_s = sgpr(nxt.R), fmn_s = sgpr(nxt.fm), next_s = sgpr(has_next ? 1 : 0), r0_s = sgpr(r0);
+    asm volatile(FA_D128_LOOP_ASM
+                 : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
+                   "=&{v[0:31]}"(junk0), "+{v[64:79]}"(s1[0][0]), "+{v[80:95]}"(s1[0][1]), "+{v[96:111]}"(s1[1][0]),
+                   "+{v[112:127]}"(s1[1][1]), "+{v[128:131]}"(p0[0][0][0]), "+{v[132:135]}"(p0[0][0][1]),
+                   "+{v[136:139]}"(p0[0][1][0]), "+{v[140:143]}"(p0[0][1][1]), "+{v[144:147]}"(p0[1][0][0]),
+                   "+{v[148:151]}"(p0[1][0][1]), "+{v[152:155]}"(p0[1][1][0]), "+{v[156:159]}"(p0[1][1][1]),
+                   "+{v192}"(m[0]), "+{v193}"(m[1]), "+{v194}"(l[0]), "+{v195}"(l[1]), "+{s74}"(p),
+                   "=&{v[32:63]}"(junk1), "=&{v[160:175]}"(junk2), "=&{v[176:191]}"(junk3), "=&{v[196:199]}"(junk4),
+                   "=&{a[192:199]}"(junk5)
+                 : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]), "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
+                   "{a[144:147]}"(qf[0][4]), "{a[148:151]}"(qf[0][5]), "{a[152:155]}"(qf[0][6]), "{a[156:159]}"(qf[0][7]),
+                   "{a[160:163]}"(qf[1][0]), "{a[164:167]}"(qf[1][1]), "{a[168:171]}"(qf[1][2]), "{a[172:175]}"(qf[1][3]),
+                   "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]), "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
+                   "{v[200:207]}"(koff), "{v[208:215]}"(voff), "{v[216:219]}"(cpoff), "{v220}"(bound0), "{v221}"(bound1),
+                   "{v222}"(half4), "{v[224:227]}"(rsel), "{s[70:71]}"(Ks), "{s[72:73]}"(Vs), "{s75}"(nt_s), "{s76}"(R_s),
+                   "{s77}"(fm_s), "{s78}"(ltb_s), "{s79}"(cs), "{s80}"(ring_wave), "{s81}"(N_s), "{s[90:91]}"(Kn),
+                   "{s[92:93]}"(Vn), "{s94}"(Rn_s), "{s95}"(fmn_s), "{s96}"(next_s), "{s97}"(r0_s)
+                 : "v223", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "s82", "s83", "s84",
+                   "s85", "s86", "s87", "s88", "s89", "m0", "vcc", "exec", "scc", "memory");
+    // The next block's tiles 0 and 1 have landed (its ring copies were issued
+    // from four and three steps before the end); its Q rows load during this
+    // block's epilogue.
+    const Block done = cur;
+    if (has_next) load_q(nxt);
+
+    // ---- epilogue: O = acc / l, L = m*scale + ln l.  Each wave stages its
+    // 64 x 128 bf16 block of O, 32 rows at a time, in its own 8 KB past the
+    // ring (256-byte rows, 16-byte chunks XOR-swizzled by row) and stores it
+    // in whole rows: a lane's fragment holds 8 bytes of 32 different rows,
+    // which stored directly would split every store into 32 row pieces.
+    __bf16* __restrict__ O = (__bf16*)a.o + (size_t)done.bh * N * D;
+    float* __restrict__ Lse = a.lse + (size_t)done.bh * N;
+    lds_char* ostage = smem + kRingBytes + wave * (32 * D * 2);
+    const f32x32 ob[2][2] = {{o0, o1}, {o2, o3}};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float lt = l[qb];
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x32& x = ob[qb][db >> 1];
+          const int e = (db & 1) * 16 + g4 * 4;
+          const u32x2 v2 = {pack_bf16_u32(x[e + 0] * inv, x[e + 1] * inv), pack_bf16_u32(x[e + 2] * inv, x[e + 3] * inv)};
+          const int chunk = db * 4 + g4;
+          *(u32x2 __attribute__((address_space(3)))*)(ostage + l32 * (D * 2) + ((chunk ^ (l32 & 15)) << 4) + half * 8) = v2;
+        }
+      const int row = wq0 + qb * 32 + l32;
+      if (row < N && half == 0) Lse[row] = m[qb] * a.scale + fast_log2(lt) * kLn2;
+      // back in rows: lanes 16k .. 16k+15 hold one 256-byte row
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = k * 4 + (lane >> 4), ch = lane & 15;
+        const u32x4 v4 = *(const u32x4 __attribute__((address_space(3)))*)(ostage + r * (D * 2) + ((ch ^ (r & 15)) << 4));
+        const int orow = wq0 + qb * 32 + r;
+        if (orow < N) *(u32x4*)(O + (size_t)orow * D + ch * 8) = v4;
+      }
+    }
+    if (!has_next) break;
+    r0 = (r0 + done.nt) & 3;
+    cur = nxt;
+    ++round;
+  }
   wait_vmcnt<0>();  // no direct-to-LDS copy may outlive the workgroup
-
-  // ---- epilogue: O = acc / l, L = m*scale + ln l.  Each wave stages its
-  // 64 x 128 bf16 block of O in its own 16 KB of the (now idle) ring, rows of
-  // 256 bytes with the 16-byte chunks XOR-swizzled by row, and stores it back
-  // in whole rows: a lane's fragment holds 8 bytes of 32 different rows,
-  // which stored directly would split every store into 32 row pieces.
-  __syncthreads();  // every wave is past its last read of the ring
-  __bf16* __restrict__ O = (__bf16*)a.o + head_off;
-  float* __restrict__ Lse = a.lse + (size_t)bh * N;
-  lds_char* ostage = smem + wave * (64 * D * 2);
-  const f32x32 ob[2][2] = {{o0, o1}, {o2, o3}};
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = l[qb];
-    const float inv = 1.0f / lt;
-    const int r = qb * 32 + l32;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x32& x = ob[qb][db >> 1];
-        const int e = (db & 1) * 16 + g4 * 4;
-        const u32x2 w = {pack_bf16_u32(x[e + 0] * inv, x[e + 1] * inv), pack_bf16_u32(x[e + 2] * inv, x[e + 3] * inv)};
-        const int chunk = db * 4 + g4;
-        *(u32x2 __attribute__((address_space(3)))*)(ostage + r * (D * 2) + ((chunk ^ (r & 15)) << 4) + half * 8) = w;
-      }
-    const int row = wq0 + r;
-    if (row < N && half == 0) Lse[row] = m[qb] * a.scale + fast_log2(lt) * kLn2;
-  }
-  // the block back in rows: lanes 16k .. 16k+15 hold one 256-byte row
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int r = k * 4 + (lane >> 4), c = lane & 15;
-    const u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(ostage + r * (D * 2) + ((c ^ (r & 15)) << 4));
-    if (wq0 + r < N) *(u32x4*)(O + (size_t)(wq0 + r) * D + c * 8) = v;
-  }
 }
 
 }  // namespace d128
 
 // Square forward at D = 128 for N >= 64 (callers route shorter tensors to
-// the generic kernel).
+// the generic kernel).  From N = 256 on (every block then visits at least
+// four key tiles) a grid larger than the device runs persistently: one
+// workgroup per compute unit, each working through its blocks with the ring
+// carried from one block into the next.
 int launch_fwd_d128(const FwdArgs& a, hipStream_t stream) {
   if (a.D != 128 || a.N < d128::kBlockN) return -2;
   const int n_qtiles = (a.N + d128::kRows - 1) / d128::kRows;
   const TileSched sched = make_sched(n_qtiles, a.B * a.H, a.causal != 0);
-  const long grid = (long)n_qtiles * a.B * a.H;
+  const long n_blocks = (long)n_qtiles * a.B * a.H;
+  long grid = n_blocks;
+  int cont = 0;
+  const int cus = device_cus();
+  if (a.N >= 4 * d128::kBlockN && cus >= 8 && n_blocks > cus) {
+    grid = cus & ~7;
+    cont = 1;
+  }
   if (a.causal)
-    hipLaunchKernelGGL(d128::fwd_d128_kernel<true>, dim3((unsigned)grid), dim3(64 * d128::kWaves), 0, stream, a, sched);
+    hipLaunchKernelGGL(d128::fwd_d128_kernel<true>, dim3((unsigned)grid), dim3(64 * d128::kWaves), 0, stream, a, sched,
+                       (int)n_blocks, cont);
   else
-    hipLaunchKernelGGL(d128::fwd_d128_kernel<false>, dim3((unsigned)grid), dim3(64 * d128::kWaves), 0, stream, a, sched);
+    hipLaunchKernelGGL(d128::fwd_d128_kernel<false>, dim3((unsigned)grid), dim3(64 * d128::kWaves), 0, stream, a, sched,
+                       (int)n_blocks, cont);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -129,6 +129,22 @@ def test_forward_bf16_many_heads(D, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(3, 37, 1000), (2, 20, 3000)])
+def test_forward_d128_persistent_rounds(B, H, N, causal):
+    """D = 128 grids larger than the GPU run one persistent workgroup per
+    compute unit, which carries its K/V ring from one 256-row block into the
+    next.  Both shapes take a full round of blocks and a partial one, with a
+    ragged last key tile: 111 heads of N = 1000 (444 blocks; heads not a
+    multiple of the eight XCDs, so no per-XCD head groups) and 40 heads of
+    N = 3000 (480 blocks, 5 heads per XCD, blocks of 4 to 47 key tiles)."""
+    w = WORKLOADS["c3"].with_(name="rounds", B=B, H=H, N=N, D=128, causal=causal, seed=N + H)
+    log(f"test_forward_d128_persistent_rounds B={B} H={H} N={N} causal={causal}")
+    x = make_inputs(w, with_do=False)
+    o, lse = _run(w, x)
+    _check_full(w, x, o, lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 33, 256, 300])
 def test_forward_f32_shapes(N, D, causal):

@@ -312,7 +312,8 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_barrier
     v_mul_f32_e64 v198, -v192, s79
     v_mul_f32_e64 v199, -v193, s79
-    // P V half: positions 0..31
+    // P V half: positions 0..31 (each position's LDS reads go out before its
+    // vector work, which then covers part of their latency)
     .irp t, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
       .if ((\t)&1) == 0
         .if ((\t)>>1) <= 13
@@ -324,15 +325,19 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
         .endif
       .endif
       FA_PMFMA ((\t)>>1), ((\t)&1)
-      FA_VPOS \t, (((\j)+1)&1)
       .if (((\t)&1) == 1) && (((\t)>>1) <= 12)
         FA_VREAD (((\t)>>1)+3), (\j)
       .endif
+      FA_VPOS \t, (((\j)+1)&1)
       .if ((\t) == 27) || ((\t) == 29) || ((\t) == 31)
         FA_KREAD (((\t)-27)>>1), (((\j)+2)&3)
       .endif
     .endr
-    // score half: positions 32..71 (32 score MFMAs of tile p+2, 8 row sums)
+    // score half: positions 32..71 (32 score MFMAs of tile p+2, 8 row sums);
+    // past the block's last tile (p+2 >= nt) the variant without scores
+    s_add_u32 s82, s74, 2
+    s_cmp_ge_u32 s82, s75
+    s_cbranch_scc1 L_ns_\j\()_\uid
     .irp t, 32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63,64,65,66,67,68,69,70,71
       FA_SPOS \t, \j
       FA_VPOS \t, (((\j)+1)&1)
@@ -343,6 +348,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
         FA_VREAD ((\t)-69), (((\j)+1)&3)
       .endif
     .endr
+  L_nsret_\j\()_\uid:
     v_accvgpr_read_b32 v196, a192
     v_accvgpr_read_b32 v197, a196
     // tile p+1 exists: check its exponentials, add its row sums
@@ -463,6 +469,31 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_branch L_mret_\j\()_\uid
   .endm
 
+  // ---- out of line: the score half of the block's last two steps, whose
+  // score tiles p+2 lie past its end: the same row sums, softmax, ring
+  // refills and V reads, without the score MFMAs (nops keep the hazard
+  // distances the score MFMAs gave)
+  .macro FA_NS j, uid
+  L_ns_\j\()_\uid:
+    .irp t, 32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63,64,65,66,67,68,69,70,71
+      .if ((\t) <= 35) || ((\t) == 42) || ((\t) == 50) || ((\t) == 58) || ((\t) == 66)
+        s_nop 4
+        FA_SPOS \t, \j
+      .endif
+      FA_VPOS \t, (((\j)+1)&1)
+      .if (\t) >= 62
+        FA_REFILL ((\t)-62), \j, \uid\()n
+      .endif
+      .if (\t) >= 69
+        FA_VREAD ((\t)-69), (((\j)+1)&3)
+      .endif
+    .endr
+    s_nop 7
+    s_nop 7
+    s_nop 7
+    s_branch L_nsret_\j\()_\uid
+  .endm
+
   // ---- out of line: the last two steps of the workgroup's last block wait
   // for every copy in flight (copies with no lane active may not count)
   .macro FA_WALL j, uid
@@ -540,8 +571,11 @@ L_s3_%=:
   FA_WALL 2, %=
   FA_WALL 3, %=
   .irp jj, 0, 1, 2, 3
+    FA_NS \jj, %=
     FA_RNEXT 0, \jj, %=
     FA_RNEXT 1, \jj, %=
+    FA_RNEXT 0, \jj, %=n
+    FA_RNEXT 1, \jj, %=n
   .endr
 L_done_%=:
   s_waitcnt lgkmcnt(0)
@@ -567,6 +601,7 @@ L_done_%=:
   .purgem FA_WALL
   .purgem FA_SWAPSETS
   .purgem FA_RNEXT
+  .purgem FA_NS
 )ASM"
 
 // One work item: a block of kRows query rows of one (batch, head), its key

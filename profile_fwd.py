@@ -196,7 +196,8 @@ def summarize(out: str, dest: str) -> None:
         "write_bytes": round(write_b),
         "copy_scale_fetch": fetch_f,
         "copy_scale_write": write_f,
-        "raw": counters,
+        "raw": {ctr: {k: {"n": len(v), "median": statistics.median(v), "min": min(v), "max": max(v)} for k, v in d.items()}
+                for ctr, d in counters.items()},  # KiB per dispatch (forward) and per copy
         "command": "python3 profile_fwd.py",
     }
     with open(os.path.join(dest, "fwd_d128_c3_traffic.json"), "w") as f:

@@ -36,7 +36,7 @@ constexpr int kKeyTile = 64;  // dQ kernel: keys per streamed K/V tile
 // go to two waves that own the same 32 query rows (their dQ partial sums
 // are added at the end), so a workgroup covers 64 rows and the B*H*N/32
 // query blocks of a workload fill twice as many SIMDs.
-// LDS rows are DP wide: D = 32 and 96 use the layout of 64 and 128 with the
+// LDS rows are DP wide: D = 32, 96 and 160 use the layout of 64, 128 and 256 with the
 // chunks past D unused (global rows stay D wide).
 template <int D>
 constexpr int lds_width() {
@@ -236,7 +236,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 // and 16 queries in its registers; P and dS packed to bf16 are then the
 // k-operands of dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read
 // transposed from the query tile.
-// (D = 256 has its own kernel, fa_bwd_dkdv_d256.hip.)
+// (D = 160 and 256 have their own kernel, fa_bwd_dkdv_d256.hip.)
 template <int D>
 struct KvCfg {
   static_assert(D <= 128, "");
@@ -440,6 +440,8 @@ int launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
       return a.causal ? launch_dq<96, true>(a, stream) : launch_dq<96, false>(a, stream);
     case 128:
       return a.causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
+    case 160:  // the D = 256 layout and key split, 96 columns unused
+      return a.causal ? launch_dq<160, true>(a, stream) : launch_dq<160, false>(a, stream);
     case 256:
       return a.causal ? launch_dq<256, true>(a, stream) : launch_dq<256, false>(a, stream);
   }
@@ -456,6 +458,7 @@ int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
       return a.causal ? launch_dkdv<96, true>(a, stream) : launch_dkdv<96, false>(a, stream);
     case 128:
       return a.causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
+    case 160:
     case 256:
       return launch_bwd_dkdv_d256(a, stream);
   }

@@ -1,4 +1,5 @@
-// fa_bwd_dkdv_d256.hip -- dK/dV kernel of the split backward at D = 256 (gfx950).
+// fa_bwd_dkdv_d256.hip -- dK/dV kernel of the split backward at D = 256 and
+// D = 160 (gfx950).
 //
 // The operation is the key/value side of the metal-flash-attention README's
 // backward ("Quantifying performance", backward-key-value pseudocode): a
@@ -15,7 +16,9 @@
 // through LDS, and each accumulates dK and dV for its half of the 256
 // output columns.  The work per key group is unchanged and a wave holds 128
 // accumulator registers.  The K (or V) rows of a wave's keys stay in
-// registers as MFMA operands.
+// registers as MFMA operands.  D = 160 runs the same kernel on the 256-wide
+// LDS rows of D = 256 (the chunks past 160 unused, global rows 160 wide);
+// its five 32-column output blocks split 3 + 2 over the two waves.
 //
 // The loop is skewed by one query tile so that a step has one barrier and
 // two independent halves of MFMA work: step i forms S (or dP) of tile i and
@@ -35,12 +38,16 @@ namespace fa {
 
 namespace {
 
+template <int D_>
 struct KvDsplitCfg {
-  static constexpr int D = 256;
+  static constexpr int D = D_;
+  static constexpr int DP = 256;     // LDS row pitch (elements)
+  static constexpr int kDBlocks = D / 32;                 // 32-column output blocks
+  static constexpr int kHalfBlocks = (kDBlocks + 1) / 2;  // blocks of output half 0 (half 1: the rest)
   static constexpr int kWaves = 4;   // 2 key groups x 2 output halves
   static constexpr int kKeys = 64;   // key rows per workgroup
   static constexpr int kQTile = 32;  // query rows per streamed tile
-  static constexpr int kTileBytes = kQTile * D * 2;
+  static constexpr int kTileBytes = kQTile * DP * 2;
   static constexpr int kStatBytes = 256;       // 64 floats of L or delta (rows past the tile are spare)
   static constexpr int kXpBytes = 2 * 64 * 16;  // P: two bf16x8 operands per lane
   static constexpr int kXdBytes = 16 * 64 * 4;  // dP: a 32x32 fp32 accumulator, [r/4][lane] x 4
@@ -50,11 +57,11 @@ struct KvDsplitCfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 };
 
-template <bool CAUSAL>
+template <int D_, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_d256_kernel(
     BwdArgs a, TileSched sched) {
-  using C = KvDsplitCfg;
-  constexpr int D = C::D, kDSteps = D / 16, kHalfBlocks = D / 64, W = C::kWaves;
+  using C = KvDsplitCfg<D_>;
+  constexpr int D = C::D, DP = C::DP, kDSteps = D / 16, kHalfBlocks = C::kHalfBlocks, W = C::kWaves;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLdsBytes];
   lds_char* smem = (lds_char*)smem_raw;
   // query-tile ring: tile t in slot t % 3 (Q, dO, L, delta)
@@ -96,8 +103,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
   auto load_qtile = [&](int t) {
     const int sl = t % 3;
-    copy_rows_lds<D, D, C::kQTile, W>(Q, N, t * C::kQTile, qbuf(sl), wave, lane);
-    copy_rows_lds<D, D, C::kQTile, W>(dO, N, t * C::kQTile, obuf(sl), wave, lane);
+    copy_rows_lds<D, DP, C::kQTile, W>(Q, N, t * C::kQTile, qbuf(sl), wave, lane);
+    copy_rows_lds<D, DP, C::kQTile, W>(dO, N, t * C::kQTile, obuf(sl), wave, lane);
     if (wave == 0) {
       int r = t * C::kQTile + lane;
       r = r < N ? r : N - 1;
@@ -107,7 +114,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   };
   load_qtile(t_begin);
 
-  // this wave's half of dK^T and dV^T: d blocks dh*4 .. dh*4+3
+  // this wave's half of dK^T and dV^T: d blocks dh*kHalfBlocks .. (those below kDBlocks)
   f32x16 dk[kHalfBlocks], dv[kHalfBlocks];
 #pragma unroll
   for (int i = 0; i < kHalfBlocks; ++i)
@@ -140,7 +147,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       f32x16 mine;
 #pragma unroll
       for (int ds = 0; ds < kDSteps; ++ds)
-        mine = mfma32(read_row_operand<D>(at, l32, ds, half), kvf[ds], ds == 0 ? f32x16{} : mine);
+        mine = mfma32(read_row_operand<DP>(at, l32, ds, half), kvf[ds], ds == 0 ? f32x16{} : mine);
       if (dh == 0) {  // P = exp(S - L), masked; queries of register r: (r/4)*8 + half*4 + r%4
         const bool masked = (CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N);
         // L of the lane's 16 queries: four runs of four consecutive rows
@@ -221,15 +228,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         }
         dspk[cc] = join8(dd[0], dd[1], dd[2], dd[3]);
       }
-      // dV^T += dO^T P,  dK^T += Q^T dS over d blocks dh*4 ..
+      // dV^T += dO^T P,  dK^T += Q^T dS over d blocks dh*kHalfBlocks ..
 #pragma unroll
-      for (int i = 0; i < kHalfBlocks; ++i)
+      for (int i = 0; i < kHalfBlocks; ++i) {
+        if (dh * kHalfBlocks + i >= C::kDBlocks) break;  // D = 160: half 1 has one block fewer
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const int d0 = (dh * kHalfBlocks + i) * 32;
-          dv[i] = mfma32(read_tr_operand<D>(obuf(sl), cc * 16, d0, lane), ppk[cc], dv[i]);
-          dk[i] = mfma32(read_tr_operand<D>(qbuf(sl), cc * 16, d0, lane), dspk[cc], dk[i]);
+          dv[i] = mfma32(read_tr_operand<DP>(obuf(sl), cc * 16, d0, lane), ppk[cc], dv[i]);
+          dk[i] = mfma32(read_tr_operand<DP>(qbuf(sl), cc * 16, d0, lane), dspk[cc], dk[i]);
         }
+      }
     }
   }
 
@@ -238,7 +247,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   __bf16* __restrict__ dK = (__bf16*)a.dk + head_off;
   __bf16* __restrict__ dV = (__bf16*)a.dv + head_off;
 #pragma unroll
-  for (int i = 0; i < kHalfBlocks; ++i)
+  for (int i = 0; i < kHalfBlocks; ++i) {
+    if (dh * kHalfBlocks + i >= C::kDBlocks) break;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const size_t off = (size_t)key * D + (dh * kHalfBlocks + i) * 32 + g4 * 8 + half * 4;
@@ -249,22 +259,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       *(u32x2*)(dK + off) = wk;
       *(u32x2*)(dV + off) = wv;
     }
+  }
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 int launch(const BwdArgs& a, hipStream_t stream) {
-  const int n_tiles = (a.N + KvDsplitCfg::kKeys - 1) / KvDsplitCfg::kKeys;
+  const int n_tiles = (a.N + KvDsplitCfg<D>::kKeys - 1) / KvDsplitCfg<D>::kKeys;
   // causal: the first key blocks see the most query tiles, so ascending order is heaviest first
   const TileSched sched = make_sched(n_tiles, a.B * a.H, false);
   const long grid = (long)n_tiles * a.B * a.H;
-  hipLaunchKernelGGL((bwd_dkdv_d256_kernel<CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, a, sched);
+  hipLaunchKernelGGL((bwd_dkdv_d256_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, a, sched);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
 int launch_bwd_dkdv_d256(const BwdArgs& a, hipStream_t stream) {
-  return a.causal ? launch<true>(a, stream) : launch<false>(a, stream);
+  if (a.D == 160) return a.causal ? launch<160, true>(a, stream) : launch<160, false>(a, stream);
+  if (a.D == 256) return a.causal ? launch<256, true>(a, stream) : launch<256, false>(a, stream);
+  return -2;
 }
 
 }  // namespace fa

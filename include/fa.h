@@ -194,7 +194,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  * from q, k, v, o (the forward output), dO (bf16) and lse (the forward's
  * L).  Each workgroup owns a block of query rows and loops over key blocks,
  * so no two workgroups write the same element: no atomics, no workspace.
- * D in {32, 64, 96, 128, 256}; any N >= 1.
+ * D in {32, 64, 96, 128, 160, 256}; any N >= 1.
  */
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
               float* delta, void* dq, int B, int H, int N, int D, float scale, int causal, void* stream);
@@ -206,7 +206,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const 
  * from q, k, v, dO, lse and delta.  delta must be the one fa_bwd_dq wrote:
  * enqueue this call after fa_bwd_dq on the same stream (or otherwise order
  * it after).  Each workgroup owns a block of key rows and loops over query
- * blocks: no atomics, no workspace.  D in {32, 64, 96, 128, 256}; any N >= 1.
+ * blocks: no atomics, no workspace.  D in {32, 64, 96, 128, 160, 256}; any N >= 1.
  */
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
                 void* dk, void* dv, int B, int H, int N, int D, float scale, int causal, void* stream);

@@ -25,6 +25,14 @@ collected in its own rocprofv3 pass (counter-block limits).
 
 `python3 profile_fwd.py --copy BYTES` is the calibration workload: it copies a
 BYTES-long device buffer three times (run under rocprofv3 by the main mode).
+
+`python3 profile_fwd.py --kernels` takes the same two SQ passes for the other
+kernels on their workloads (`--run NAME` is the workload each pass profiles:
+c2 and c5 forward, the c5 backward's two kernels, the causal backward at the
+c3 shape) and the HBM traffic of the c4 forward, and writes
+  kernel_counters.md            one section per kernel: clock, MFMA busy, VALU
+                                and transcendental issue, LDS, scratch/registers
+  fwd_d128_c4_traffic.md        FETCH_SIZE / WRITE_SIZE of the c4 forward
 """
 
 from __future__ import annotations
@@ -57,6 +65,64 @@ BENCH_ALL = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "10", "-
 FLOP_C3 = 4 * 8192 * 8192 * 128 * 2 * 16 // 2
 # 256-row query block t (of 32 per head) visits key tiles 0 .. 4t+3 of 64 keys
 EXP_C3 = 2 * 16 * sum(256 * 64 * (4 * t + 4) for t in range(8192 // 256))
+
+
+# --kernels: (name, workload run, kernel-name regex, source, instance, flop per launch)
+def _flop(name):
+    sys.path.insert(0, ROOT)
+    from fa_inputs import WORKLOADS
+
+    w = WORKLOADS[name]
+    return w
+
+
+# (the kernel regex is a plain name: each workload runs one instance of it)
+KERNEL_SETS = [
+    ("c2 forward, D=64 (B=4 H=16 N=2048)", "c2_fwd", "fwd_bf16_kernel", "fa_fwd_bf16.hip",
+     "fwd_bf16_kernelILi64ELb0ELi1ELi4ELb0ELb0ELb0E", lambda: _flop("c2").fwd_flop()),
+    ("c5 forward, D=256 (B=1 H=4 N=4096)", "c5_fwd", "fwd_bf16_kernel", "fa_fwd_bf16_d256.hip",
+     "fwd_bf16_kernelILi256ELb0ELi1ELi4ELb0ELb0ELb0E", lambda: _flop("c5").fwd_flop()),
+    ("c5 backward dQ, D=256", "c5_bwd", "bwd_dq_kernel", "fa_bwd.hip", "bwd_dq_kernelILi256ELb0E",
+     lambda: 6 * 4096 * 4096 * 256 * 4),
+    ("c5 backward dK/dV, D=256", "c5_bwd", "bwd_dkdv_d256_kernel", "fa_bwd_dkdv_d256.hip",
+     "bwd_dkdv_d256_kernelILi256ELb0E", lambda: 8 * 4096 * 4096 * 256 * 4),
+    ("causal backward dQ at the c3 shape, D=128 (B=2 H=16 N=8192)", "c3_bwd", "bwd_dq_kernel", "fa_bwd.hip",
+     "bwd_dq_kernelILi128ELb1E", lambda: 3 * 8192 * 8192 * 128 * 32),
+    ("causal backward dK/dV at the c3 shape, D=128", "c3_bwd", "bwd_dkdv_kernel", "fa_bwd.hip",
+     "bwd_dkdv_kernelILi128ELb1E", lambda: 4 * 8192 * 8192 * 128 * 32),
+]
+RUN_REPS = 12
+
+
+def run_workload(name: str, reps: int) -> None:
+    """One workload, `reps` launches (the profiled program of --kernels)."""
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import exact_attention_51_amd as fa
+    from fa_inputs import WORKLOADS, make_inputs
+
+    key, kind = name.split("_")
+    w = WORKLOADS[key]
+    if key == "c3" and kind == "bwd":
+        w = w.with_(backward=True, seed=13)
+    x = make_inputs(w, with_do=kind == "bwd")
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, k, v = bf(x.q_bits), bf(x.k_bits), bf(x.v_bits)
+    o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+    if kind == "bwd":
+        do = bf(x.do_bits)
+        for _ in range(reps):
+            fa.bwd(q, k, v, o, do, lse, w.scale, w.causal)
+    else:
+        for _ in range(reps):
+            fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    print(f"copied {name} x{reps}", flush=True)  # the line run() looks for
 
 
 def copy_workload(nbytes: int) -> None:
@@ -131,10 +197,33 @@ def main() -> int:
     ap.add_argument("--summarize", action="store_true",
                     help="only rebuild profiles/ from the CSVs already under gpurun_out/profile_fwd")
     ap.add_argument("--passes", default=",".join(PASSES), help=f"comma-separated subset of {','.join(PASSES)}")
+    ap.add_argument("--kernels", action="store_true", help="SQ passes of the other kernels, c4 traffic")
+    ap.add_argument("--run", default="", help="profiled workload of --kernels (c2_fwd, c5_fwd, c5_bwd, c3_bwd, c4_fwd)")
     args = ap.parse_args()
     passes = args.passes.split(",")
     if args.copy:
         copy_workload(args.copy)
+        return 0
+    if args.run:
+        run_workload(args.run, RUN_REPS)
+        return 0
+    if args.kernels:
+        out = os.path.join(ROOT, "gpurun_out", "profile_kernels")
+        if not args.summarize:
+            os.makedirs(out, exist_ok=True)
+            me = [sys.executable, os.path.abspath(__file__)]
+            for i, (label, run_name, regex, _, _, _) in enumerate(KERNEL_SETS):
+                for pname, ctrs in SQ_PASSES.items():
+                    if pname == "tcc":
+                        continue
+                    run(["rocprofv3", "--pmc", *ctrs, "--kernel-include-regex", regex, "--output-format", "csv", "-d",
+                         os.path.join(out, f"k{i}_{pname}"), "-o", "run", "--", *me, "--run", run_name], 300)
+            for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                run(["rocprofv3", "--pmc", ctr, "--kernel-include-regex", FWD_KERNEL, "--output-format", "csv", "-d",
+                     os.path.join(out, f"c4_{ctr}"), "-o", "run", "--", *me, "--run", "c4_fwd"], 300)
+                run(["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", os.path.join(out, f"copy_{ctr}"), "-o",
+                     "run", "--", *me, "--copy", str(COPY_BYTES)], 300)
+        summarize_kernels(out, PROFILES if args.summarize else os.path.join(out, "profiles"))
         return 0
 
     if not args.summarize:
@@ -461,6 +550,123 @@ def summarize_counters(out: str, dest: str) -> None:
     with open(os.path.join(dest, "fwd_d128_c3_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
+
+
+def resource_usage(src_name: str, instance: str) -> str:
+    """Register, scratch and LDS use of one kernel instance from the
+    compiler's resource-usage remarks on our own build."""
+    sys.path.insert(0, ROOT)
+    from exact_attention_51_amd import build
+
+    src = os.path.join(ROOT, "exact_attention_51_amd", "csrc", src_name)
+    cmd = [build.hipcc(), *build.COMMON_FLAGS, *build.source_flags(src_name), "--offload-device-only",
+           "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", os.devnull]
+    try:
+        err = subprocess.run(cmd, capture_output=True, text=True, timeout=600).stderr.splitlines()
+    except (OSError, subprocess.TimeoutExpired):
+        return ""
+    want = ("VGPRs:", "AGPRs:", "ScratchSize [bytes/lane]:", "Occupancy [waves/SIMD]:", "LDS Size [bytes/block]:")
+    for i, line in enumerate(err):
+        if "Function Name:" in line and instance in line:
+            got = []
+            for rest in err[i + 1:i + 16]:
+                if "Function Name:" in rest:
+                    break
+                body = rest.split("remark: ")[-1].split(" [-Rpass")[0].strip()
+                if body.startswith(want):
+                    got.append(body)
+            return "; ".join(got)
+    return ""
+
+
+def kernel_medians(outdir: str, regex_plain: str) -> tuple[dict, list]:
+    vals: dict[int, dict] = {}
+    span: dict[int, tuple] = {}
+    for r in counter_rows(outdir):
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+        if regex_plain not in name:
+            continue
+        d = int(r["Dispatch_Id"])
+        v = vals.setdefault(d, {})
+        v[r["Counter_Name"]] = v.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            span[d] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    ids = sorted(vals)[1:] or sorted(vals)
+    med = {k: statistics.median(vals[d][k] for d in ids if k in vals[d]) for k in {k for d in ids for k in vals[d]}}
+    spans = [(vals[d]["GRBM_GUI_ACTIVE"] / 8 / (span[d][1] - span[d][0]), span[d][1] - span[d][0]) for d in ids
+             if d in span and span[d][1] > span[d][0]]
+    return med, spans
+
+
+def summarize_kernels(out: str, dest: str) -> None:
+    """kernel_counters.md and fwd_d128_c4_traffic.md from the --kernels CSVs."""
+    os.makedirs(dest, exist_ok=True)
+    lines = ["# SQ counters of the other kernels", "",
+             "Command (repository root, GPU box): `python3 profile_fwd.py --kernels`: per kernel, two",
+             "`rocprofv3 --pmc` passes (the counter sets below) over `python3 profile_fwd.py --run WORKLOAD`",
+             f"({RUN_REPS} launches of the workload on seeded synthetic inputs), kernel filtered by name, medians",
+             "over the dispatches after the first.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024",
+             "SIMDs); TFLOPS from the median dispatch duration and the workload's FLOP count (4N²D per head",
+             "for the forward, 6N²D for dQ, 8N²D for dK/dV, halved under causal masking).", ""]
+    for name, ctrs in SQ_PASSES.items():
+        if name != "tcc":
+            lines.append(f"- pass {name}: `{' '.join(ctrs)}`")
+    for i, (label, run_name, regex, src, instance, flop) in enumerate(KERNEL_SETS):
+        plain = regex
+        if not all(os.path.isdir(os.path.join(out, f"k{i}_{p}")) for p in ("sq1", "sq2")):
+            continue
+        m1, sp = kernel_medians(os.path.join(out, f"k{i}_sq1"), plain)
+        m2, _ = kernel_medians(os.path.join(out, f"k{i}_sq2"), plain)
+        if not m1 or not m2:
+            continue
+        gui = m1["GRBM_GUI_ACTIVE"] / 8
+        ghz = statistics.median(c for c, _ in sp) if sp else float("nan")
+        ns = statistics.median(t for _, t in sp) if sp else float("nan")
+        tf = flop() / (ns * 1e-9) / 1e12 if sp else float("nan")
+        n_mfma = max(m2["SQ_INSTS_MFMA"], 1)
+        lines += ["", f"## {label}: `{regex}`", "",
+                  f"- dispatch duration (median): {ns / 1e3:.1f} us -> {tf:.0f} TFLOPS ({100 * tf / 2500:.1f}% of the"
+                  f" bf16 dense peak); shader clock {ghz:.2f} GHz",
+                  f"- MFMA busy: {100 * m1['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * 1024):.1f}%; MFMA cycles co-executing"
+                  f" VALU: {100 * m1['SQ_VALU_MFMA_COEXEC_CYCLES'] / max(m1['SQ_VALU_MFMA_BUSY_CYCLES'], 1):.1f}%",
+                  f"- VALU issue (x 4 / (cycles x 1024 SIMDs), MFMA issue included):"
+                  f" {100 * 4 * m1['SQ_ACTIVE_INST_VALU'] / (gui * 1024):.1f}%; LDS instruction wait / wave cycles:"
+                  f" {100 * m1['SQ_WAIT_INST_LDS'] / max(m1['SQ_WAVE_CYCLES'], 1):.1f}%",
+                  f"- instructions per MFMA: VALU (MFMA included) {m2['SQ_INSTS_VALU'] / n_mfma:.2f}, of them"
+                  f" transcendental {m2['SQ_INSTS_VALU_TRANS_F32'] / n_mfma:.2f}; LDS {m2['SQ_INSTS_LDS'] / n_mfma:.2f};"
+                  f" SALU {m2['SQ_INSTS_SALU'] / n_mfma:.2f}",
+                  f"- LDS: SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs) = {100 * m2['SQ_LDS_IDX_ACTIVE'] / (gui * 256):.1f}%;"
+                  f" bank-conflict cycles / LDS active = {100 * m2['SQ_LDS_BANK_CONFLICT'] / max(m2['SQ_LDS_IDX_ACTIVE'], 1):.2f}%",
+                  f"- waves per dispatch: {m2['SQ_WAVES']:.0f}",
+                  f"- compiler resource usage (`{instance}`): {resource_usage(src, instance)}"]
+    with open(os.path.join(dest, "kernel_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+    # c4 traffic
+    try:
+        fwd = {c: per_dispatch(counter_rows(os.path.join(out, f"c4_{c}")), lambda n: FWD_KERNEL in n)
+               for c in ("FETCH_SIZE", "WRITE_SIZE")}
+        cp = {c: sorted(per_dispatch(counter_rows(os.path.join(out, f"copy_{c}")), lambda n: True))[-3:]
+              for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    except (ValueError, OSError):
+        return
+    fetch_f = (COPY_BYTES / 1024) / statistics.median(cp["FETCH_SIZE"])
+    write_f = (COPY_BYTES / 1024) / statistics.median(cp["WRITE_SIZE"])
+    fetch_b = statistics.median(fwd["FETCH_SIZE"][1:]) * 1024 * fetch_f
+    write_b = statistics.median(fwd["WRITE_SIZE"][1:]) * 1024 * write_f
+    algo = 1 * 8 * 32768 * 128 * 2 * 4 + 1 * 8 * 32768 * 4
+    tl = ["# Forward kernel, causal B=1 H=8 N=32768 D=128 bf16 (Q x3): HBM traffic per launch", "",
+          "Command (repository root, GPU box): `python3 profile_fwd.py --kernels` (one rocprofv3 `--pmc` pass per",
+          "counter over `python3 profile_fwd.py --run c4_fwd`, forward kernel filtered by name; calibration = 1 GiB",
+          "device copy).", "",
+          f"- FETCH_SIZE scale (copy bytes / counter bytes): {fetch_f:.4f}; WRITE_SIZE scale: {write_f:.4f}",
+          f"- forward fetch: {fetch_b / 2**20:.1f} MiB, write: {write_b / 2**20:.1f} MiB, total"
+          f" {(fetch_b + write_b) / 2**20:.1f} MiB per launch",
+          f"- algorithmic bytes (Q, K, V read once; O, L written once): {algo / 2**20:.1f} MiB",
+          f"- ratio measured / algorithmic: {(fetch_b + write_b) / algo:.2f}"]
+    with open(os.path.join(dest, "fwd_d128_c4_traffic.md"), "w") as f:
+        f.write("\n".join(tl) + "\n")
+    print("\n".join(tl), flush=True)
 
 
 if __name__ == "__main__":

@@ -87,7 +87,7 @@ def test_workload_backward_c5():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 256])
 @pytest.mark.parametrize("N", [1, 40, 64, 100, 256, 333])
 def test_backward_shapes(N, D, causal):
     w = WORKLOADS["c5"].with_(name="edge", B=1, H=2, N=N, D=D, causal=causal, seed=3 * N + D)
@@ -96,7 +96,7 @@ def test_backward_shapes(N, D, causal):
     _check(w, x, _run_bwd(w, x))
 
 
-@pytest.mark.parametrize("D", [96, 128, 256])
+@pytest.mark.parametrize("D", [96, 128, 160, 256])
 def test_backward_causal_long(D):
     w = WORKLOADS["c5"].with_(name="causal_long", B=1, H=2, N=1024, D=D, causal=True, seed=D + 1)
     log(f"test_backward_causal_long D={D}")

@@ -59,7 +59,7 @@
 //   a[192:199]           row-sum accumulators, block qb at 192 + qb*4
 //   s[70:71], s[72:73]   K and V of the head;  s74 position p;  s75 tiles;
 //   s76 masked tiles R;  s77 first masked tile;  s78 last tile byte offset;
-//   s79 scale*log2(e);  s80 LDS ring base + this wave's copy offset;  s81 N;
+//   s79 scale*log2(e);  s80 LDS ring base + this wave's copy offset;  s81 wave;
 //   s82..s89 scalar temporaries
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -280,7 +280,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_add_u32 s82, s74, s77
     s_add_u32 s82, s82, \q
     s_lshl_b32 s83, s82, 6
-    s_sub_u32 s84, s81, 64
+    s_lshr_b32 s84, s78, 8
     s_min_u32 s84, s83, s84
     v_add_u32 v228, s84, v222
     v_sub_u32 v229, s83, v228
@@ -338,6 +338,9 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_add_u32 s82, s74, 2
     s_cmp_ge_u32 s82, s75
     s_cbranch_scc1 L_ns_\j\()_\uid
+    s_cmp_lt_u32 s82, s76
+    s_cbranch_scc1 L_diag_\j\()_\uid
+  L_sfull_\j\()_\uid:
     .irp t, 32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63,64,65,66,67,68,69,70,71
       FA_SPOS \t, \j
       FA_VPOS \t, (((\j)+1)&1)
@@ -474,6 +477,12 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   // refills and V reads, without the score MFMAs (nops keep the hazard
   // distances the score MFMAs gave)
   .macro FA_NS j, uid
+    // a masked tile p+2: without the causal mask's diagonal tiles past
+    // this wave's rows (position > wave), whose scores the mask turns
+    // into -inf whatever they hold
+  L_diag_\j\()_\uid:
+    s_cmp_gt_u32 s82, s81
+    s_cbranch_scc0 L_sfull_\j\()_\uid
   L_ns_\j\()_\uid:
     .irp t, 32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63,64,65,66,67,68,69,70,71
       .if ((\t) <= 35) || ((\t) == 42) || ((\t) == 50) || ((\t) == 58) || ((\t) == 66)
@@ -737,6 +746,15 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
 
     // scores of the tile at position p from K ring slot b, masked when p < R
     auto scores = [&](int b, int p, f32x16 (&s)[2][2]) {
+      if (CAUSAL && p < cur.R && p > wave) {  // a diagonal tile past this wave's rows
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][qb][r] = -__builtin_inff();
+        return;
+      }
 #pragma unroll
       for (int ds = 0; ds < 8; ++ds)
 #pragma unroll
@@ -825,7 +843,10 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
     const __bf16* Vs = sgpr_ptr(head((const __bf16*)a.v, cur.bh));
     const __bf16* Kn = sgpr_ptr(head((const __bf16*)a.k, nxt.bh));
     const __bf16* Vn = sgpr_ptr(head((const __bf16*)a.v, nxt.bh));
-    const int nt_s = sgpr(cur.nt), R_s = sgpr(cur.R), fm_s = sgpr(cur.fm), N_s = sgpr(N);
+    const int nt_s = sgpr(cur.nt), R_s = sgpr(cur.R), fm_s = sgpr(cur.fm);
+    // the diagonal tile at position i (i < R under causal masking) is fully
+    // masked for the rows of waves below i
+    const int wave_s = sgpr(CAUSAL ? wave : 1 << 30);
     const int ltb_s = sgpr((int)last_tile_bytes);
     const int Rn_s = sgpr(nxt.R), fmn_s = sgpr(nxt.fm), next_s = sgpr(has_next ? 1 : 0), r0_s = sgpr(r0);
     asm volatile(FA_D128_LOOP_ASM
@@ -843,7 +864,7 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
                    "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]), "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
                    "{v[200:207]}"(koff), "{v[208:215]}"(voff), "{v[216:219]}"(cpoff), "{v220}"(bound0), "{v221}"(bound1),
                    "{v222}"(half4), "{v[224:227]}"(rsel), "{s[70:71]}"(Ks), "{s[72:73]}"(Vs), "{s75}"(nt_s), "{s76}"(R_s),
-                   "{s77}"(fm_s), "{s78}"(ltb_s), "{s79}"(cs), "{s80}"(ring_wave), "{s81}"(N_s), "{s[90:91]}"(Kn),
+                   "{s77}"(fm_s), "{s78}"(ltb_s), "{s79}"(cs), "{s80}"(ring_wave), "{s81}"(wave_s), "{s[90:91]}"(Kn),
                    "{s[92:93]}"(Vn), "{s94}"(Rn_s), "{s95}"(fmn_s), "{s96}"(next_s), "{s97}"(r0_s)
                  : "v223", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "s82", "s83", "s84",
                    "s85", "s86", "s87", "s88", "s89", "m0", "vcc", "exec", "scc", "memory");

@@ -193,6 +193,32 @@ def test_forward_growing_scores(D, causal):
             _check_full(w, x, *_run(w, x))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_d128_persistent_growing_scores(causal):
+    """The growing-score inputs above on a D = 128 grid large enough to run
+    persistently (260 heads of N = 512: 520 blocks), so the out-of-line
+    rescale path runs in blocks that took their first K/V tiles from the
+    ring of the block before."""
+    from fa_inputs import Inputs, bf16_round
+
+    n, h, D = 512, 260, 128
+    rng = np.random.default_rng(97)
+    scale = 1.0 / np.sqrt(D)
+    for growth in (30.0, 200.0):
+        for rising in (True, False):
+            log(f"test_forward_d128_persistent_growing_scores causal={causal} growth={growth} rising={rising}")
+            q = 0.1 * rng.standard_normal((1, h, n, D)).astype(np.float32)
+            q[..., 0] = 1.0
+            k = 0.1 * rng.standard_normal((1, h, n, D)).astype(np.float32)
+            j = np.arange(n) if rising else np.arange(n)[::-1]
+            k[0, :, :, 0] = j * growth / (64 * scale * np.log2(np.e))
+            v = rng.standard_normal((1, h, n, D)).astype(np.float32)
+            (qv, qb), (kv, kb), (vv, vb) = bf16_round(q), bf16_round(k), bf16_round(v)
+            x = Inputs(q=qv, k=kv, v=vv, do=None, q_bits=qb, k_bits=kb, v_bits=vb)
+            w = WORKLOADS["c3"].with_(name="growing_persistent", B=1, H=h, N=n, D=D, causal=causal)
+            _check_full(w, x, *_run(w, x))
+
+
 @pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 256])
 def test_forward_invariants(D):
     import torch

@@ -17,7 +17,9 @@ oracle timed on a bounded sample of the same workload) and ``others``
 (TFLOPS of the other workloads, measured the same way, and ``fa_fwd_kv``
 with split key ranges on the pages' shape and on decoding one row per head,
 where the K/V read rate against the 8 TB/s HBM peak is the figure, and
-``fa_fwd_sparse`` at the c3 shape with two block masks).
+``fa_fwd_sparse`` at the c3 shape with two block masks).  The backward entries
+carry the dQ and dK/dV kernels timed alone, and c5 the pages' three-kernel
+figure: the mean utilisation of the forward, dQ and dK/dV kernels times 7/9.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
 """
@@ -210,7 +212,8 @@ def time_forward_sparse(w, q, k, v, mask, steps: int, warmup: int):
 
 
 def time_backward(w, q, k, v, steps: int, warmup: int):
-    """Mean event ms per (fa_bwd_dq + fa_bwd_dkdv) pair."""
+    """Mean event ms per (fa_bwd_dq + fa_bwd_dkdv) pair, then per dQ call and
+    per dK/dV call timed alone."""
     import numpy as np
     import torch
 
@@ -230,7 +233,20 @@ def time_backward(w, q, k, v, steps: int, warmup: int):
         fa.bwd(q, k, v, o, do, lse, w.scale, w.causal, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    pair = e0.elapsed_time(e1) / steps
+    dq, delta = fa.bwd_dq(q, k, v, o, do, lse, w.scale, w.causal, stream=stream)
+    dk, dv = fa.bwd_dkdv(q, k, v, do, lse, delta, w.scale, w.causal, stream=stream)
+    alone = []
+    for call in (lambda: fa.bwd_dq(q, k, v, o, do, lse, w.scale, w.causal, dq=dq, delta=delta, stream=stream),
+                 lambda: fa.bwd_dkdv(q, k, v, do, lse, delta, w.scale, w.causal, dk=dk, dv=dv, stream=stream)):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        alone.append(e0.elapsed_time(e1) / steps)
+    return pair, alone[0], alone[1]
 
 
 def cgroup_cpu_quota():
@@ -377,7 +393,7 @@ def main() -> int:
                     others[f"{name}_fwd"] = {"error": str(e)}
             if wo.backward:
                 try:
-                    ms = time_backward(wo, qo, ko, vo, steps, 2)
+                    ms, ms_dq, ms_kv = time_backward(wo, qo, ko, vo, steps, 2)
                     tf = wo.bwd_flop() / (ms * 1e-3) / 1e12
                     others[f"{name}_bwd"] = {
                         "ms": round(ms, 5),
@@ -385,7 +401,26 @@ def main() -> int:
                         "flop_convention": "14 N^2 D per head (dQ: 3 products, dK/dV: 4 products), halved if causal",
                         # the five-product count (2 N^2 D each) other backward figures are quoted in
                         "tflops_5_products": round(tf * 5 / 7, 2),
+                        "dq_ms": round(ms_dq, 5),
+                        "dkdv_ms": round(ms_kv, 5),
                     }
+                    fwd_rec = others.get(f"{name}_fwd", {})
+                    if "ms" in fwd_rec:
+                        # the pages' three-kernel figure: the mean MFMA utilisation of the
+                        # forward, dQ and dK/dV kernels (2, 3 and 4 products of 2 N^2 D
+                        # FLOP each) times 7/9, the split design's 9 products set against
+                        # the 7 of a backward with atomic dQ
+                        half = 2 if wo.causal else 1
+                        unit = 2 * wo.N * wo.N * wo.D * wo.B * wo.H / half
+                        util = [k * unit / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+                                for k, t in ((2, fwd_rec["ms"]), (3, ms_dq), (4, ms_kv))]
+                        others[f"{name}_three_kernel"] = {
+                            "fwd_pct": round(100 * util[0], 2),
+                            "dq_pct": round(100 * util[1], 2),
+                            "dkdv_pct": round(100 * util[2], 2),
+                            "mean_pct": round(100 * sum(util) / 3, 2),
+                            "mean_x7_9_pct": round(100 * sum(util) / 3 * 7 / 9, 2),
+                        }
                     log(f"bench: {name} bwd {ms:.4f} ms -> {tf:.1f} TFLOPS")
                 except fa.FAError as e:
                     others[f"{name}_bwd"] = {"error": str(e)}

@@ -57,6 +57,408 @@ struct KvDsplitCfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 };
 
+// S = A K^T over d as one accumulator chain of NS (6 <= NS <= 16) MFMAs,
+// the A fragments read from LDS 6 ahead of their MFMA (one buffer each).
+// The B operands (this wave's K or V rows) are held in a[0:63], fragment ds
+// in a[4ds : 4ds+3].  addr[ds] is the lane's LDS byte address of fragment
+// ds < 8; fragment ds >= 8 lies 256 bytes further (the swizzle permutes
+// chunks within each 16-chunk half of a 512-byte row).  Compiler-scheduled,
+// at 256 VGPRs this chain read one fragment at a time and waited for it.
+template <int NS>
+__device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& kv0, const f32x16& kv1,
+                                           const f32x16& kv2, const f32x16& kv3) {
+  static_assert(NS >= 6 && NS <= 16, "chain length");
+  f32x16 acc;
+  f32x4 b[6];  // fragment buffers: fragment ds in buffer ds mod 6
+  asm volatile(
+      "ds_read_b128 %[f0], %[a0]\n"
+      "ds_read_b128 %[f1], %[a1]\n"
+      "ds_read_b128 %[f2], %[a2]\n"
+      "ds_read_b128 %[f3], %[a3]\n"
+      "ds_read_b128 %[f4], %[a4]\n"
+      "ds_read_b128 %[f5], %[a5]\n"
+      ".if 0 < %[ns]\n"
+      "  .if 0 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 0 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 0 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 0 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 0 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[0:3], 0\n"
+      "  .if 6 < %[ns]\n    ds_read_b128 %[f0], %[a6]\n  .endif\n"
+      ".endif\n"
+      ".if 1 < %[ns]\n"
+      "  .if 1 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 1 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 1 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 1 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 1 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[4:7], %[acc]\n"
+      "  .if 7 < %[ns]\n    ds_read_b128 %[f1], %[a7]\n  .endif\n"
+      ".endif\n"
+      ".if 2 < %[ns]\n"
+      "  .if 2 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 2 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 2 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 2 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 2 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[8:11], %[acc]\n"
+      "  .if 8 < %[ns]\n    ds_read_b128 %[f2], %[a0] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 3 < %[ns]\n"
+      "  .if 3 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 3 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 3 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 3 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 3 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[12:15], %[acc]\n"
+      "  .if 9 < %[ns]\n    ds_read_b128 %[f3], %[a1] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 4 < %[ns]\n"
+      "  .if 4 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 4 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 4 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 4 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 4 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f4], a[16:19], %[acc]\n"
+      "  .if 10 < %[ns]\n    ds_read_b128 %[f4], %[a2] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 5 < %[ns]\n"
+      "  .if 5 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 5 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 5 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 5 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 5 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f5], a[20:23], %[acc]\n"
+      "  .if 11 < %[ns]\n    ds_read_b128 %[f5], %[a3] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 6 < %[ns]\n"
+      "  .if 6 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 6 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 6 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 6 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 6 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[24:27], %[acc]\n"
+      "  .if 12 < %[ns]\n    ds_read_b128 %[f0], %[a4] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 7 < %[ns]\n"
+      "  .if 7 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 7 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 7 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 7 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 7 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[28:31], %[acc]\n"
+      "  .if 13 < %[ns]\n    ds_read_b128 %[f1], %[a5] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 8 < %[ns]\n"
+      "  .if 8 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 8 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 8 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 8 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 8 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[32:35], %[acc]\n"
+      "  .if 14 < %[ns]\n    ds_read_b128 %[f2], %[a6] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 9 < %[ns]\n"
+      "  .if 9 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 9 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 9 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 9 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 9 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[36:39], %[acc]\n"
+      "  .if 15 < %[ns]\n    ds_read_b128 %[f3], %[a7] offset:256\n  .endif\n"
+      ".endif\n"
+      ".if 10 < %[ns]\n"
+      "  .if 10 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 10 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 10 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 10 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 10 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f4], a[40:43], %[acc]\n"
+      ".endif\n"
+      ".if 11 < %[ns]\n"
+      "  .if 11 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 11 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 11 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 11 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 11 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f5], a[44:47], %[acc]\n"
+      ".endif\n"
+      ".if 12 < %[ns]\n"
+      "  .if 12 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 12 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 12 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 12 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 12 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[48:51], %[acc]\n"
+      ".endif\n"
+      ".if 13 < %[ns]\n"
+      "  .if 13 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 13 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 13 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 13 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 13 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[52:55], %[acc]\n"
+      ".endif\n"
+      ".if 14 < %[ns]\n"
+      "  .if 14 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 14 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 14 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 14 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 14 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[56:59], %[acc]\n"
+      ".endif\n"
+      ".if 15 < %[ns]\n"
+      "  .if 15 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
+      "  .elseif 15 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 15 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
+      "  .elseif 15 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .elseif 15 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[60:63], %[acc]\n"
+      ".endif\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 7\n"  // the MFMA results may be read by vector instructions right after
+      : [acc] "=&v"(acc), [f0] "=&v"(b[0]), [f1] "=&v"(b[1]), [f2] "=&v"(b[2]), [f3] "=&v"(b[3]), [f4] "=&v"(b[4]), [f5] "=&v"(b[5])
+      : [a0] "v"(addr[0]), [a1] "v"(addr[1]), [a2] "v"(addr[2]), [a3] "v"(addr[3]), [a4] "v"(addr[4]),
+        [a5] "v"(addr[5]), [a6] "v"(addr[6]), [a7] "v"(addr[7]), [ns] "i"(NS), "{a[0:15]}"(kv0), "{a[16:31]}"(kv1),
+        "{a[32:47]}"(kv2), "{a[48:63]}"(kv3)
+      : "memory");
+  return acc;
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS over NB 32-column blocks, the Oᵀ and Qᵀ
+// operands read transposed from the query tile 3 fragments ahead of their
+// MFMA (fragment buffers v[240:255], second-read addresses in
+// v236..v239).  addr[i] is the lane's address of block i's first
+// transposed read in the Q tile (cc = 0); the dO tile lies 16384 bytes
+// further, the second 16 queries (cc = 1) 8192, the read 8 rows down d2.
+template <int NB>
+__device__ __forceinline__ void kv_tr_chain(const int (&addr)[4], int d2, const bf16x8& pp0, const bf16x8& pp1,
+                                            const bf16x8& ds0, const bf16x8& ds1, f32x16& dv0, f32x16& dv1,
+                                            f32x16& dv2, f32x16& dv3, f32x16& dk0, f32x16& dk1, f32x16& dk2,
+                                            f32x16& dk3) {
+  static_assert(NB >= 1 && NB <= 4, "blocks");
+  f32x16 junk;
+  f32x4 junk2;
+  asm volatile(
+      ".if 0 < 4 * %[nb]\n"
+      "  ds_read_b64_tr_b16 v[240:241], %[a0] offset:16384\n"
+      "  v_add_u32 v236, %[a0], %[d2]\n"
+      "  ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
+      ".endif\n"
+      ".if 1 < 4 * %[nb]\n"
+      "  ds_read_b64_tr_b16 v[244:245], %[a0] offset:0\n"
+      "  v_add_u32 v237, %[a0], %[d2]\n"
+      "  ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
+      ".endif\n"
+      ".if 2 < 4 * %[nb]\n"
+      "  ds_read_b64_tr_b16 v[248:249], %[a0] offset:24576\n"
+      "  v_add_u32 v238, %[a0], %[d2]\n"
+      "  ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
+      ".endif\n"
+      ".if 3 < 4 * %[nb]\n"
+      "  ds_read_b64_tr_b16 v[252:253], %[a0] offset:8192\n"
+      "  v_add_u32 v239, %[a0], %[d2]\n"
+      "  ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
+      ".endif\n"
+      ".if 0 < 4 * %[nb]\n"
+      "  .if 0 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 0 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 0 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv0], v[240:243], %[pp0], %[dv0]\n"
+      "  .if 4 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[240:241], %[a1] offset:16384\n"
+      "    v_add_u32 v236, %[a1], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 1 < 4 * %[nb]\n"
+      "  .if 1 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 1 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 1 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk0], v[244:247], %[ds0], %[dk0]\n"
+      "  .if 5 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[244:245], %[a1] offset:0\n"
+      "    v_add_u32 v237, %[a1], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 2 < 4 * %[nb]\n"
+      "  .if 2 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 2 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 2 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv0], v[248:251], %[pp1], %[dv0]\n"
+      "  .if 6 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[248:249], %[a1] offset:24576\n"
+      "    v_add_u32 v238, %[a1], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 3 < 4 * %[nb]\n"
+      "  .if 3 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 3 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 3 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk0], v[252:255], %[ds1], %[dk0]\n"
+      "  .if 7 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[252:253], %[a1] offset:8192\n"
+      "    v_add_u32 v239, %[a1], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 4 < 4 * %[nb]\n"
+      "  .if 4 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 4 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 4 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv1], v[240:243], %[pp0], %[dv1]\n"
+      "  .if 8 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[240:241], %[a2] offset:16384\n"
+      "    v_add_u32 v236, %[a2], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 5 < 4 * %[nb]\n"
+      "  .if 5 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 5 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 5 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk1], v[244:247], %[ds0], %[dk1]\n"
+      "  .if 9 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[244:245], %[a2] offset:0\n"
+      "    v_add_u32 v237, %[a2], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 6 < 4 * %[nb]\n"
+      "  .if 6 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 6 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 6 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv1], v[248:251], %[pp1], %[dv1]\n"
+      "  .if 10 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[248:249], %[a2] offset:24576\n"
+      "    v_add_u32 v238, %[a2], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 7 < 4 * %[nb]\n"
+      "  .if 7 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 7 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 7 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk1], v[252:255], %[ds1], %[dk1]\n"
+      "  .if 11 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[252:253], %[a2] offset:8192\n"
+      "    v_add_u32 v239, %[a2], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 8 < 4 * %[nb]\n"
+      "  .if 8 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 8 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 8 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv2], v[240:243], %[pp0], %[dv2]\n"
+      "  .if 12 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[240:241], %[a3] offset:16384\n"
+      "    v_add_u32 v236, %[a3], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 9 < 4 * %[nb]\n"
+      "  .if 9 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 9 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 9 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk2], v[244:247], %[ds0], %[dk2]\n"
+      "  .if 13 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[244:245], %[a3] offset:0\n"
+      "    v_add_u32 v237, %[a3], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 10 < 4 * %[nb]\n"
+      "  .if 10 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 10 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 10 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv2], v[248:251], %[pp1], %[dv2]\n"
+      "  .if 14 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[248:249], %[a3] offset:24576\n"
+      "    v_add_u32 v238, %[a3], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 11 < 4 * %[nb]\n"
+      "  .if 11 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 11 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 11 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk2], v[252:255], %[ds1], %[dk2]\n"
+      "  .if 15 < 4 * %[nb]\n"
+      "    ds_read_b64_tr_b16 v[252:253], %[a3] offset:8192\n"
+      "    v_add_u32 v239, %[a3], %[d2]\n"
+      "    ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
+      "  .endif\n"
+      ".endif\n"
+      ".if 12 < 4 * %[nb]\n"
+      "  .if 12 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 12 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 12 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv3], v[240:243], %[pp0], %[dv3]\n"
+      ".endif\n"
+      ".if 13 < 4 * %[nb]\n"
+      "  .if 13 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 13 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 13 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk3], v[244:247], %[ds0], %[dk3]\n"
+      ".endif\n"
+      ".if 14 < 4 * %[nb]\n"
+      "  .if 14 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 14 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 14 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dv3], v[248:251], %[pp1], %[dv3]\n"
+      ".endif\n"
+      ".if 15 < 4 * %[nb]\n"
+      "  .if 15 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
+      "  .elseif 15 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
+      "  .elseif 15 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
+      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
+      "  v_mfma_f32_32x32x16_bf16 %[dk3], v[252:255], %[ds1], %[dk3]\n"
+      ".endif\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 7\n"  // the MFMA results may be read by vector instructions right after
+      : [dv0] "+v"(dv0), [dv1] "+v"(dv1), [dv2] "+v"(dv2), [dv3] "+v"(dv3), [dk0] "+v"(dk0), [dk1] "+v"(dk1),
+        [dk2] "+v"(dk2), [dk3] "+v"(dk3), "=&{v[240:255]}"(junk), "=&{v[236:239]}"(junk2)
+      : [a0] "v"(addr[0]), [a1] "v"(addr[1]), [a2] "v"(addr[2]), [a3] "v"(addr[3]), [d2] "v"(d2), [pp0] "v"(pp0),
+        [pp1] "v"(pp1), [ds0] "v"(ds0), [ds1] "v"(ds1), [nb] "i"(NB)
+      : "memory");
+}
+
 template <int D_, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_d256_kernel(
     BwdArgs a, TileSched sched) {
@@ -101,10 +503,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
                                                       kgrp * (C::kXpBytes + C::kXdBytes) + C::kXpBytes) + lane;
   };
 
+  // query-tile copies: scalar base and loop-invariant per-lane offsets for
+  // whole tiles, rows clamped onto N-1 for a ragged last tile
+  RowTileCopier<D, DP, C::kQTile, W> cp;
+  cp.init(wave, lane);
   auto load_qtile = [&](int t) {
-    const int sl = t % 3;
-    copy_rows_lds<D, DP, C::kQTile, W>(Q, N, t * C::kQTile, qbuf(sl), wave, lane);
-    copy_rows_lds<D, DP, C::kQTile, W>(dO, N, t * C::kQTile, obuf(sl), wave, lane);
+    const int sl = t % 3, row0 = t * C::kQTile;
+    if (row0 + C::kQTile <= N) {
+      cp.copy_at(Q, (uint32_t)row0 * (D * 2), qbuf(sl));
+      cp.copy_at(dO, (uint32_t)row0 * (D * 2), obuf(sl));
+    } else {
+      cp.copy_clamped(Q, N, row0, qbuf(sl));
+      cp.copy_clamped(dO, N, row0, obuf(sl));
+    }
     if (wave == 0) {
       int r = t * C::kQTile + lane;
       r = r < N ? r : N - 1;
@@ -123,12 +534,38 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const float c = a.scale_log2;
   // K (S-forming wave) or V (dP-forming wave) of this wave's keys as B
   // operands: key column l32, d = ds*16 + half*8 + 0..7
-  bf16x8 kvf[kDSteps];
+  // (held as four 16-register groups, fragment ds at registers 4*(ds mod 4) of group ds/4)
+  f32x16 kvg[4];
   {
     const __bf16* __restrict__ src = dh == 0 ? K : V;
     const int crow = key < N ? key : N - 1;
 #pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds) kvf[ds] = *(const bf16x8*)(src + (size_t)crow * D + ds * 16 + half * 8);
+    for (int ds = 0; ds < 16; ++ds) {
+      const bf16x8 f = ds < kDSteps ? *(const bf16x8*)(src + (size_t)crow * D + ds * 16 + half * 8) : bf16x8{};
+      const f32x4 f4 = __builtin_bit_cast(f32x4, f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kvg[ds >> 2][(ds & 3) * 4 + i] = f4[i];
+    }
+  }
+  // the lane's byte offsets of fragments 0..7 of a row-major tile row l32
+  int roff[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ++ds) roff[ds] = lds_off_bytes<DP>(l32, ds * 2 + half);
+  // the lane's byte offsets of the first transposed read of d block
+  // dh*kHalfBlocks + i (queries 0..15 of a tile), and of its second read
+  // relative to the first (the same for every block)
+  int troff[4];
+  int trd2;
+  {
+    const int g = lane >> 4, j16 = lane & 15;
+    const int r1 = half * 4 + (j16 >> 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dcol = (dh * kHalfBlocks + i) * 32 + (g & 1) * 16 + (j16 & 3) * 4;
+      troff[i] = lds_off_bytes<DP>(r1, dcol >> 3) + (dcol & 7) * 2;
+    }
+    const int dcol0 = (dh * kHalfBlocks) * 32 + (g & 1) * 16 + (j16 & 3) * 4;
+    trd2 = lds_off_bytes<DP>(r1 + 8, dcol0 >> 3) - lds_off_bytes<DP>(r1, dcol0 >> 3);
   }
 
   // does key group kgrp see any query of tile t?
@@ -144,20 +581,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     if (t < n_qtiles && tile_work(t)) {
       const int sl = t % 3, xb = t & 1, tq0 = t * C::kQTile;
       const lds_char* at = dh == 0 ? qbuf(sl) : obuf(sl);
-      f32x16 mine;
+      int addr[8];
+      const int tb = (int)(uint32_t)(uintptr_t)at;
 #pragma unroll
-      for (int ds = 0; ds < kDSteps; ++ds)
-        mine = mfma32(read_row_operand<DP>(at, l32, ds, half), kvf[ds], ds == 0 ? f32x16{} : mine);
-      if (dh == 0) {  // P = exp(S - L), masked; queries of register r: (r/4)*8 + half*4 + r%4
-        const bool masked = (CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N);
-        // L of the lane's 16 queries: four runs of four consecutive rows
-        float lq[16];
+      for (int ds = 0; ds < 8; ++ds) addr[ds] = tb + roff[ds];
+      // L of the lane's 16 queries (four runs of four consecutive rows), read
+      // before the chain so that its latency overlaps the MFMAs
+      float lq[16];
+      if (dh == 0) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 l4 = *(const f32x4 __attribute__((address_space(3)))*)(lbuf(sl) + 4 * (g * 8 + half * 4));
 #pragma unroll
           for (int i = 0; i < 4; ++i) lq[g * 4 + i] = l4[i];
         }
+      }
+      f32x16 mine = kv_chain<kDSteps>(addr, kvg[0], kvg[1], kvg[2], kvg[3]);
+      if (dh == 0) {  // P = exp(S - L), masked; queries of register r: (r/4)*8 + half*4 + r%4
+        const bool masked = (CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N);
         // two instances: tiles that need no mask carry no selects
         auto exp_p = [&](auto mconst) {
           constexpr bool MASKED = decltype(mconst)::value;
@@ -229,15 +670,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         dspk[cc] = join8(dd[0], dd[1], dd[2], dd[3]);
       }
       // dV^T += dO^T P,  dK^T += Q^T dS over d blocks dh*kHalfBlocks ..
+      int taddr[4];
+      const int qb0 = (int)(uint32_t)(uintptr_t)qbuf(sl);
 #pragma unroll
-      for (int i = 0; i < kHalfBlocks; ++i) {
-        if (dh * kHalfBlocks + i >= C::kDBlocks) break;  // D = 160: half 1 has one block fewer
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int d0 = (dh * kHalfBlocks + i) * 32;
-          dv[i] = mfma32(read_tr_operand<DP>(obuf(sl), cc * 16, d0, lane), ppk[cc], dv[i]);
-          dk[i] = mfma32(read_tr_operand<DP>(qbuf(sl), cc * 16, d0, lane), dspk[cc], dk[i]);
-        }
+      for (int i = 0; i < 4; ++i) taddr[i] = qb0 + troff[i];
+      if constexpr (kHalfBlocks == 4) {
+        kv_tr_chain<4>(taddr, trd2, ppk[0], ppk[1], dspk[0], dspk[1], dv[0], dv[1], dv[2], dv[3], dk[0], dk[1], dk[2],
+                       dk[3]);
+      } else {
+        // D = 160: blocks 0..2 (half 0) or 3..4 (half 1); the unused operand
+        // slots take scratch accumulators (no two operands may name one variable)
+        f32x16 sv0 = {}, sk0 = {}, sv1 = {}, sk1 = {};
+        if (dh == 0)
+          kv_tr_chain<3>(taddr, trd2, ppk[0], ppk[1], dspk[0], dspk[1], dv[0], dv[1], dv[2], sv0, dk[0], dk[1], dk[2],
+                         sk0);
+        else
+          kv_tr_chain<2>(taddr, trd2, ppk[0], ppk[1], dspk[0], dspk[1], dv[0], dv[1], sv0, sv1, dk[0], dk[1], sk0,
+                         sk1);
       }
     }
   }

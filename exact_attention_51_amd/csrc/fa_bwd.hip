@@ -51,6 +51,170 @@ struct DqCfg {
   static constexpr int kRows = 32 * kWavesQ / kSplit;  // query rows per workgroup
 };
 
+// ------------------------------------------- dQ chains for 256-wide LDS rows
+//
+// At D = 160 and 256 a wave's step is 2 NS + 2 NB MFMAs whose A operands
+// all come from LDS.  Compiled from C++ the reads were issued one MFMA
+// ahead of their use, so every MFMA waited out an LDS round trip; these
+// two chains keep six fragments in flight instead.  Fixed registers: the
+// Q^T fragment of k-step ds in a[4 ds : 4 ds + 3] and the dO^T fragment in
+// a[64 + 4 ds : ...] (bound by the callers' operand constraints), six
+// fragment buffers in v[232:255], read addresses formed in v230 and v231.
+//
+// Read addresses: a tile row is 512 bytes and 512-aligned in LDS, and the
+// swizzle only permutes 16-byte chunks inside each 256-byte half, so the
+// lane's address of chunk c ^ swz equals its address of chunk swz with
+// the chunk bits flipped by c: one XOR with a constant per read.
+
+// DQ_WAIT n: s_waitcnt lgkmcnt(n) for an assemble-time n in 0..11
+#define DQ_WAIT_MACRO                                \
+  ".macro DQ_WAIT n\n"                               \
+  "  .if (\\n) <= 0\n    s_waitcnt lgkmcnt(0)\n"     \
+  "  .elseif (\\n) == 1\n    s_waitcnt lgkmcnt(1)\n" \
+  "  .elseif (\\n) == 2\n    s_waitcnt lgkmcnt(2)\n" \
+  "  .elseif (\\n) == 3\n    s_waitcnt lgkmcnt(3)\n" \
+  "  .elseif (\\n) == 4\n    s_waitcnt lgkmcnt(4)\n" \
+  "  .elseif (\\n) == 5\n    s_waitcnt lgkmcnt(5)\n" \
+  "  .elseif (\\n) == 6\n    s_waitcnt lgkmcnt(6)\n" \
+  "  .elseif (\\n) == 7\n    s_waitcnt lgkmcnt(7)\n" \
+  "  .elseif (\\n) == 8\n    s_waitcnt lgkmcnt(8)\n" \
+  "  .elseif (\\n) == 9\n    s_waitcnt lgkmcnt(9)\n" \
+  "  .elseif (\\n) == 10\n    s_waitcnt lgkmcnt(10)\n" \
+  "  .else\n    s_waitcnt lgkmcnt(11)\n"             \
+  "  .endif\n"                                       \
+  ".endm\n"
+
+#define DQ_CHAIN_CLOBBERS                                                                                      \
+  "memory", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", \
+      "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
+
+// S^T = K_j Q^T and dP^T = V_j dO^T over NS k-steps of 16 columns,
+// interleaved: MFMA i takes k-step i/2, S for even i and dP for odd i.  rb
+// is the lane's address of chunk 0 of its K row in the ring slot; k-step ds
+// is chunk 2 ds + half: rb ^ 32 (ds mod 8), 256 bytes further for ds >= 8,
+// and the V slot lies 32768 bytes after the K slot.  Each accumulator runs
+// its k-steps in order, as the plain loop does.
+template <int NS>
+__device__ __forceinline__ void dq_sdp_chain(int rb, const f32x16 (&qo)[8], f32x16& s, f32x16& dp) {
+  static_assert(NS >= 4 && NS <= 16, "chain length");
+  asm volatile(
+      DQ_WAIT_MACRO
+      // read fragment i into buffer i mod 6
+      ".macro DQ_RD i\n"
+      "  .if (\\i) < 2 * %[ns]\n"
+      "    .if (((\\i) >> 1) & 7) == 0\n"
+      "      ds_read_b128 v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], %[rb] "
+      "offset:(((\\i) & 1) * 32768 + (((\\i) >> 4) & 1) * 256)\n"
+      "    .else\n"
+      "      v_xor_b32 v[230 + ((\\i) & 1)], 32 * (((\\i) >> 1) & 7), %[rb]\n"
+      "      ds_read_b128 v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], v[230 + ((\\i) & 1)] "
+      "offset:(((\\i) & 1) * 32768 + (((\\i) >> 4) & 1) * 256)\n"
+      "    .endif\n"
+      "  .endif\n"
+      ".endm\n"
+      ".macro DQ_MM i, acc\n"
+      "  .if (\\i) < 2 * %[ns]\n"
+      "    .if (\\i) + 6 < 2 * %[ns]\n"
+      "      DQ_WAIT 5\n"
+      "    .else\n"
+      "      DQ_WAIT (2 * %[ns] - (\\i) - 1)\n"
+      "    .endif\n"
+      "    .if ((\\i) >> 1) == 0\n"
+      "      v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], "
+      "a[((\\i) & 1) * 64 + ((\\i) >> 1) * 4 : ((\\i) & 1) * 64 + ((\\i) >> 1) * 4 + 3], 0\n"
+      "    .else\n"
+      "      v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], "
+      "a[((\\i) & 1) * 64 + ((\\i) >> 1) * 4 : ((\\i) & 1) * 64 + ((\\i) >> 1) * 4 + 3], \\acc\n"
+      "    .endif\n"
+      "    DQ_RD (\\i) + 6\n"
+      "  .endif\n"
+      ".endm\n"
+      "DQ_RD 0\nDQ_RD 1\nDQ_RD 2\nDQ_RD 3\nDQ_RD 4\nDQ_RD 5\n"
+      "DQ_MM 0, %[s]\nDQ_MM 1, %[dp]\nDQ_MM 2, %[s]\nDQ_MM 3, %[dp]\n"
+      "DQ_MM 4, %[s]\nDQ_MM 5, %[dp]\nDQ_MM 6, %[s]\nDQ_MM 7, %[dp]\n"
+      "DQ_MM 8, %[s]\nDQ_MM 9, %[dp]\nDQ_MM 10, %[s]\nDQ_MM 11, %[dp]\n"
+      "DQ_MM 12, %[s]\nDQ_MM 13, %[dp]\nDQ_MM 14, %[s]\nDQ_MM 15, %[dp]\n"
+      "DQ_MM 16, %[s]\nDQ_MM 17, %[dp]\nDQ_MM 18, %[s]\nDQ_MM 19, %[dp]\n"
+      "DQ_MM 20, %[s]\nDQ_MM 21, %[dp]\nDQ_MM 22, %[s]\nDQ_MM 23, %[dp]\n"
+      "DQ_MM 24, %[s]\nDQ_MM 25, %[dp]\nDQ_MM 26, %[s]\nDQ_MM 27, %[dp]\n"
+      "DQ_MM 28, %[s]\nDQ_MM 29, %[dp]\nDQ_MM 30, %[s]\nDQ_MM 31, %[dp]\n"
+      "s_nop 7\ns_nop 7\ns_nop 7\n"  // S and dP are read by vector instructions next
+      ".purgem DQ_WAIT\n.purgem DQ_RD\n.purgem DQ_MM\n"
+      : [s] "=&v"(s), [dp] "=&v"(dp)
+      : [ns] "i"(NS), [rb] "v"(rb), "{a[0:15]}"(qo[0]), "{a[16:31]}"(qo[1]), "{a[32:47]}"(qo[2]),
+        "{a[48:63]}"(qo[3]), "{a[64:79]}"(qo[4]), "{a[80:95]}"(qo[5]), "{a[96:111]}"(qo[6]), "{a[112:127]}"(qo[7])
+      : DQ_CHAIN_CLOBBERS);
+}
+
+// dQ^T += K_j^T dS^T over NB 32-column blocks, K_j^T read transposed
+// (two ds_read_b64_tr_b16 per fragment, 8 rows apart).  Fragment order:
+// the first 16 keys (dS^T chunk d0) for blocks 0..NB-1, then the second 16
+// (d1), so each accumulator takes its two chunks in order.  t1 and t2 are
+// the lane's addresses of the two reads of block 0's first chunk; block db
+// is t ^ 64 (db mod 4), 256 bytes further for db >= 4, and the second chunk
+// 8192.  Accumulators past NB are not touched.
+template <int NB>
+__device__ __forceinline__ void dq_tr_chain(int t1, int t2, const bf16x8& d0, const bf16x8& d1, f32x16& q0,
+                                            f32x16& q1, f32x16& q2, f32x16& q3, f32x16& q4, f32x16& q5,
+                                            f32x16& q6, f32x16& q7) {
+  static_assert(NB >= 4 && NB <= 8, "blocks");
+  asm volatile(
+      DQ_WAIT_MACRO
+      // the two reads of block db, chunk offset co, into buffer f mod 6
+      ".macro DT_RDX db, co, f\n"
+      "  .if ((\\db) & 3) == 0\n"
+      "    ds_read_b64_tr_b16 v[232 + ((\\f) %% 6) * 4 : 233 + ((\\f) %% 6) * 4], %[t1] "
+      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
+      "    ds_read_b64_tr_b16 v[234 + ((\\f) %% 6) * 4 : 235 + ((\\f) %% 6) * 4], %[t2] "
+      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
+      "  .else\n"
+      "    v_xor_b32 v230, 64 * ((\\db) & 3), %[t1]\n"
+      "    v_xor_b32 v231, 64 * ((\\db) & 3), %[t2]\n"
+      "    ds_read_b64_tr_b16 v[232 + ((\\f) %% 6) * 4 : 233 + ((\\f) %% 6) * 4], v230 "
+      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
+      "    ds_read_b64_tr_b16 v[234 + ((\\f) %% 6) * 4 : 235 + ((\\f) %% 6) * 4], v231 "
+      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
+      "  .endif\n"
+      ".endm\n"
+      // fragment f: block f of the first chunk (f < NB) or f - NB of the second
+      ".macro DT_RD f\n"
+      "  .if (\\f) < %[nb]\n"
+      "    DT_RDX (\\f), 0, (\\f)\n"
+      "  .elseif (\\f) < 2 * %[nb]\n"
+      "    DT_RDX ((\\f) - %[nb]), 8192, (\\f)\n"
+      "  .endif\n"
+      ".endm\n"
+      ".macro DT_MM f, lim, acc, b\n"
+      "  .if (\\f) < (\\lim)\n"
+      "    .if (\\f) + 6 < 2 * %[nb]\n"
+      "      DQ_WAIT 10\n"
+      "    .else\n"
+      "      DQ_WAIT (2 * (2 * %[nb] - (\\f) - 1))\n"
+      "    .endif\n"
+      "    v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\f) %% 6) * 4 : 235 + ((\\f) %% 6) * 4], \\b, \\acc\n"
+      "    DT_RD (\\f) + 6\n"
+      "  .endif\n"
+      ".endm\n"
+      "DT_RD 0\nDT_RD 1\nDT_RD 2\nDT_RD 3\nDT_RD 4\nDT_RD 5\n"
+      "DT_MM 0, %[nb], %[q0], %[d0]\nDT_MM 1, %[nb], %[q1], %[d0]\n"
+      "DT_MM 2, %[nb], %[q2], %[d0]\nDT_MM 3, %[nb], %[q3], %[d0]\n"
+      "DT_MM 4, %[nb], %[q4], %[d0]\nDT_MM 5, %[nb], %[q5], %[d0]\n"
+      "DT_MM 6, %[nb], %[q6], %[d0]\nDT_MM 7, %[nb], %[q7], %[d0]\n"
+      "DT_MM %[nb]+0, 2*%[nb], %[q0], %[d1]\nDT_MM %[nb]+1, 2*%[nb], %[q1], %[d1]\n"
+      "DT_MM %[nb]+2, 2*%[nb], %[q2], %[d1]\nDT_MM %[nb]+3, 2*%[nb], %[q3], %[d1]\n"
+      "DT_MM %[nb]+4, 2*%[nb], %[q4], %[d1]\nDT_MM %[nb]+5, 2*%[nb], %[q5], %[d1]\n"
+      "DT_MM %[nb]+6, 2*%[nb], %[q6], %[d1]\nDT_MM %[nb]+7, 2*%[nb], %[q7], %[d1]\n"
+      "s_nop 7\ns_nop 7\ns_nop 7\n"  // the accumulators may be read by vector instructions next
+      ".purgem DQ_WAIT\n.purgem DT_RDX\n.purgem DT_RD\n.purgem DT_MM\n"
+      : [q0] "+v"(q0), [q1] "+v"(q1), [q2] "+v"(q2), [q3] "+v"(q3), [q4] "+v"(q4), [q5] "+v"(q5), [q6] "+v"(q6),
+        [q7] "+v"(q7)
+      : [nb] "i"(NB), [d0] "v"(d0), [d1] "v"(d1), [t1] "v"(t1), [t2] "v"(t2)
+      : DQ_CHAIN_CLOBBERS);
+}
+
+#undef DQ_WAIT_MACRO
+#undef DQ_CHAIN_CLOBBERS
+
 // ============================================================== dQ kernel
 //
 // Each wave owns 32 query rows (one lane column each).  Scores and dP are
@@ -64,10 +228,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   constexpr int KB = DqCfg<D>::kKB, kRowsQ = DqCfg<D>::kRows, kQBlocks = kWavesQ / DqCfg<D>::kSplit;
   constexpr int DP = DqCfg<D>::kDP;
   constexpr int kTileBytes = kKeyTile * DP * 2;
+  // 256-wide rows run the step as the two asm chains (one 32-key block per wave)
+  constexpr bool kChains = DP == 256;
+  static_assert(!kChains || (KB == 1 && kTileBytes == 32768), "chain layout");
+  constexpr bool kSplitMask = kChains;
+  // ring slots K0 V0 K1 V1: a slot's V tile lies kTileBytes after its K tile
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * kTileBytes];
   lds_char* smem = (lds_char*)smem_raw;
-  lds_char* kbuf[2] = {smem, smem + kTileBytes};
-  lds_char* vbuf[2] = {smem + 2 * kTileBytes, smem + 3 * kTileBytes};
+  lds_char* kbuf[2] = {smem, smem + 2 * kTileBytes};
+  lds_char* vbuf[2] = {smem + kTileBytes, smem + 3 * kTileBytes};
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
             half = lane >> 5;
@@ -128,11 +297,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   if (wave_active && kpart == 0 && half == 0 && row < N) a.delta[(size_t)bh * N + row] = delta;
   const float c = a.scale_log2;
 
-  f32x16 dq[kDBlocks];
+  // the chains take 8 accumulators; at D = 160 the last three stay unused
+  constexpr int kAcc = kChains ? 8 : kDBlocks;
+  f32x16 dq[kAcc];
 #pragma unroll
-  for (int db = 0; db < kDBlocks; ++db)
+  for (int db = 0; db < kAcc; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+
+  // chain operands: Q^T and dO^T fragments in groups of four k-steps,
+  // loaded again from global memory so that the chains' AGPR operands are
+  // their only use (the register allocator then leaves them in place), and
+  // the lane's addresses, relative to a K tile, of chunk 0 of its K row (row
+  // reads) and of block 0's two transposed reads
+  f32x16 qo[kChains ? 8 : 1];
+  int rofs = 0, tofs1 = 0, tofs2 = 0;
+  if constexpr (kChains) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int ds = (g & 3) * 4 + f;
+        const __bf16* __restrict__ src = g < 4 ? Q : dO;
+        const f32x4 v =
+            ds < kDSteps ? *(const f32x4*)(src + (size_t)crow * D + ds * 16 + half * 8) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qo[g][f * 4 + i] = v[i];
+      }
+    const int kr0 = kpart * 32, g4 = lane >> 4, j16 = lane & 15;
+    rofs = lds_off_bytes<DP>(kr0 + l32, half);
+    const int r1 = kr0 + half * 4 + (j16 >> 2), dcol = (g4 & 1) * 16 + (j16 & 3) * 4;
+    tofs1 = lds_off_bytes<DP>(r1, dcol >> 3) + (dcol & 7) * 2;
+    tofs2 = lds_off_bytes<DP>(r1 + 8, dcol >> 3) + (dcol & 7) * 2;
+  }
 
   for (int j = 0; j < nt; ++j) {
     wait_vmcnt<0>();
@@ -144,55 +341,76 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
     // S^T = K_j Q^T and dP^T = V_j dO^T, keys kr0 + kb*32.. (rows), this wave's queries (columns)
     const int kr0 = kpart * 32;
+    const int tb = (int)(uint32_t)(uintptr_t)kt;
     f32x16 s[KB], dp[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = mfma32(read_row_operand<DP>(kt, kr0 + kb * 32 + l32, ds, half), qf[ds], s[kb]);
-        dp[kb] = mfma32(read_row_operand<DP>(vt, kr0 + kb * 32 + l32, ds, half), dof[ds], dp[kb]);
-      }
-
-    const bool masked = (CAUSAL && j == wave_last) || (j == n_ktiles_all - 1 && (N % kKeyTile) != 0);
-    bf16x8 dsk[KB][2];  // dS^T packed: [key block][16-key chunk]
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        bf16x2 pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float e[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int r = cc * 8 + 2 * i + t;
-            float x = __builtin_fmaf(s[kb][r], c, -lse2);
-            if (masked) {
-              const int key = j * kKeyTile + kr0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-              bool keep = key < N;
-              if constexpr (CAUSAL) keep = keep && key <= row;
-              x = keep ? x : -__builtin_inff();
-            }
-            const float p = fast_exp2(x);
-            e[t] = p * (dp[kb][r] - delta);
-          }
-          pr[i] = pack_bf16(e[0], e[1]);
-        }
-        dsk[kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
-      }
-
-    // dQ^T += K_j^T dS^T
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
+    if constexpr (kChains) {
+      dq_sdp_chain<kDSteps>(tb + rofs, qo, s[0], dp[0]);
+    } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          dq[db] = mfma32(read_tr_operand<DP>(kt, kr0 + kb * 32 + cc * 16, db * 32, lane), dsk[kb][cc], dq[db]);
+        for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < kDSteps; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = mfma32(read_row_operand<DP>(kt, kr0 + kb * 32 + l32, ds, half), qf[ds], s[kb]);
+          dp[kb] = mfma32(read_row_operand<DP>(vt, kr0 + kb * 32 + l32, ds, half), dof[ds], dp[kb]);
+        }
+    }
+
+    const bool masked = (CAUSAL && j == wave_last) || (j == n_ktiles_all - 1 && (N % kKeyTile) != 0);
+    bf16x8 dsk[KB][2];  // dS^T packed: [key block][16-key chunk]
+    // dS^T = P^T (dP^T - delta), with the key mask only on the tiles that
+    // need it (the empty asm keeps the two variants apart: merged, the
+    // mask's compares and selects ran on every tile)
+    auto make_ds = [&](auto mask_tag) {
+      constexpr bool kMask = decltype(mask_tag)::value;
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x2 pr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int r = cc * 8 + 2 * i + t;
+              float x = __builtin_fmaf(s[kb][r], c, -lse2);
+              if (kMask && (kSplitMask || masked)) {
+                const int key = j * kKeyTile + kr0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                bool keep = key < N;
+                if constexpr (CAUSAL) keep = keep && key <= row;
+                x = keep ? x : -__builtin_inff();
+              }
+              const float p = fast_exp2(x);
+              e[t] = p * (dp[kb][r] - delta);
+            }
+            pr[i] = pack_bf16(e[0], e[1]);
+          }
+          dsk[kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
+        }
+    };
+    if (!kSplitMask || masked)
+      make_ds(std::true_type{});
+    else
+      make_ds(std::false_type{});
+
+    // dQ^T += K_j^T dS^T
+    if constexpr (kChains) {
+      dq_tr_chain<kDBlocks>(tb + tofs1, tb + tofs2, dsk[0][0], dsk[0][1], dq[0], dq[1], dq[2], dq[3], dq[4],
+                            dq[kAcc - 3], dq[kAcc - 2], dq[kAcc - 1]);
+    } else {
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+            dq[db] = mfma32(read_tr_operand<DP>(kt, kr0 + kb * 32 + cc * 16, db * 32, lane), dsk[kb][cc], dq[db]);
+    }
   }
 
   if constexpr (DqCfg<D>::kSplit == 2) {

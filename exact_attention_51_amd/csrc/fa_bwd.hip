@@ -51,169 +51,305 @@ struct DqCfg {
   static constexpr int kRows = 32 * kWavesQ / kSplit;  // query rows per workgroup
 };
 
-// ------------------------------------------- dQ chains for 256-wide LDS rows
+// ------------------------------------------ pipelined dQ step (DP = 256)
 //
-// At D = 160 and 256 a wave's step is 2 NS + 2 NB MFMAs whose A operands
-// all come from LDS.  Compiled from C++ the reads were issued one MFMA
-// ahead of their use, so every MFMA waited out an LDS round trip; these
-// two chains keep six fragments in flight instead.  Fixed registers: the
-// Q^T fragment of k-step ds in a[4 ds : 4 ds + 3] and the dO^T fragment in
-// a[64 + 4 ds : ...] (bound by the callers' operand constraints), six
-// fragment buffers in v[232:255], read addresses formed in v230 and v231.
+// At D = 160 and 256 a wave's work per key tile is 2 NS + 2 NB MFMAs
+// (S^T, dP^T, then dQ^T) whose A operands all come from LDS.  One asm
+// block per tile j runs S^T/dP^T of tile j, in their shadow dS^T of tile
+// j-1 from the S and dP the previous block left, then dQ^T += K_{j-1}^T
+// dS^T; its LDS reads run ten fragments ahead of their MFMA across both
+// parts.  The block is entered every step with a wave-uniform mode, so
+// that the dQ accumulators pass through the loop in place:
+//   0  nothing;
+//   1  S^T/dP^T only (the first tile);
+//   2  the full step;
+//   3  dQ^T only, with dS^T given by the caller (a wave's last tile, where
+//      the key mask may apply; the in-block dS is the unmasked one).
+// At D = 256 every mode also issues this wave's share of the next tile's
+// copy (16 global-to-LDS loads of 1 KB), spread between its MFMAs: issued
+// in one burst the loads stalled the wave for about a thousand cycles per
+// tile while the vector memory path drained them, with the matrix core
+// idle.
+// Per element the in-block dS is the plain loop's arithmetic, instruction
+// for instruction: x = fma(S, c, -L), p = exp2(x), (dP - delta) p, pairs
+// packed to bf16.
+//
+// Fixed registers: Q^T fragment of k-step ds in a[4 ds : 4 ds + 3], dO^T
+// in a[64 + 4 ds : ...]; dQ^T block db in a[128 + 16 db : +15]; S and dP
+// of the two alternating sets in v[142:173] and v[174:205] (S in the first
+// 16 of a set); dS^T pairs in v[206:213] (elements 2k, 2k+1 in
+// v[206 + k]); read and copy addresses formed in v214, v215; ten fragment
+// buffers in v[216:255].
 //
 // Read addresses: a tile row is 512 bytes and 512-aligned in LDS, and the
 // swizzle only permutes 16-byte chunks inside each 256-byte half, so the
 // lane's address of chunk c ^ swz equals its address of chunk swz with
-// the chunk bits flipped by c: one XOR with a constant per read.
+// the chunk bits flipped by c: one XOR with a constant per read.  rb, rv:
+// the lane's chunk-0 address of its K and V row in tile j's slots (k-step
+// ds at ^ 32 (ds mod 8), +256 bytes for ds >= 8); t1, t2: its addresses of
+// the two transposed reads of tile j-1's block 0 (block db at ^ 64 (db mod
+// 4), +256 bytes for db >= 4, second 16 keys +8192).
+#define DQ_STEP_TEXT                                                                                               \
+  /* s_waitcnt lgkmcnt(n), n an assemble-time expression, at most 15 */                                             \
+  ".macro FQ_WAIT n\n"                                                                                             \
+  "  .if (\\n) <= 0\n    s_waitcnt lgkmcnt(0)\n"                                                                   \
+  "  .elseif (\\n) == 1\n    s_waitcnt lgkmcnt(1)\n"                                                               \
+  "  .elseif (\\n) == 2\n    s_waitcnt lgkmcnt(2)\n"                                                               \
+  "  .elseif (\\n) == 3\n    s_waitcnt lgkmcnt(3)\n"                                                               \
+  "  .elseif (\\n) == 4\n    s_waitcnt lgkmcnt(4)\n"                                                               \
+  "  .elseif (\\n) == 5\n    s_waitcnt lgkmcnt(5)\n"                                                               \
+  "  .elseif (\\n) == 6\n    s_waitcnt lgkmcnt(6)\n"                                                               \
+  "  .elseif (\\n) == 7\n    s_waitcnt lgkmcnt(7)\n"                                                               \
+  "  .elseif (\\n) == 8\n    s_waitcnt lgkmcnt(8)\n"                                                               \
+  "  .elseif (\\n) == 9\n    s_waitcnt lgkmcnt(9)\n"                                                               \
+  "  .elseif (\\n) == 10\n    s_waitcnt lgkmcnt(10)\n"                                                             \
+  "  .elseif (\\n) == 11\n    s_waitcnt lgkmcnt(11)\n"          \
+  "  .elseif (\\n) == 12\n    s_waitcnt lgkmcnt(12)\n"          \
+  "  .elseif (\\n) == 13\n    s_waitcnt lgkmcnt(13)\n"          \
+  "  .elseif (\\n) == 14\n    s_waitcnt lgkmcnt(14)\n"          \
+  "  .else\n    s_waitcnt lgkmcnt(15)\n"          \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* row read of stream position p (k-step p/2) from base, address formed in tmp */                              \
+  ".macro FQ_RX p, base, tmp\n"                                                                                    \
+  "  .if (((\\p) >> 1) & 7) == 0\n"                                                                                \
+  "    ds_read_b128 v[216 + ((\\p) %% 10) * 4 : 219 + ((\\p) %% 10) * 4], \\base offset:((((\\p) >> 4) & 1) * 256)\n" \
+  "  .else\n"                                                                                                      \
+  "    v_xor_b32 \\tmp, 32 * (((\\p) >> 1) & 7), \\base\n"                                                        \
+  "    ds_read_b128 v[216 + ((\\p) %% 10) * 4 : 219 + ((\\p) %% 10) * 4], \\tmp offset:((((\\p) >> 4) & 1) * 256)\n"  \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* the two transposed reads of block db, chunk offset co, into the buffer of stream position p */              \
+  ".macro FQ_TX db, co, p\n"                                                                                       \
+  "  .if ((\\db) & 3) == 0\n"                                                                                      \
+  "    ds_read_b64_tr_b16 v[216 + ((\\p) %% 10) * 4 : 217 + ((\\p) %% 10) * 4], %[t1] "                            \
+  "offset:((\\co) + ((\\db) >> 2) * 256)\n"                                                                        \
+  "    ds_read_b64_tr_b16 v[218 + ((\\p) %% 10) * 4 : 219 + ((\\p) %% 10) * 4], %[t2] "                            \
+  "offset:((\\co) + ((\\db) >> 2) * 256)\n"                                                                        \
+  "  .else\n"                                                                                                      \
+  "    v_xor_b32 v214, 64 * ((\\db) & 3), %[t1]\n"                                                                \
+  "    v_xor_b32 v215, 64 * ((\\db) & 3), %[t2]\n"                                                                \
+  "    ds_read_b64_tr_b16 v[216 + ((\\p) %% 10) * 4 : 217 + ((\\p) %% 10) * 4], v214 "                             \
+  "offset:((\\co) + ((\\db) >> 2) * 256)\n"                                                                        \
+  "    ds_read_b64_tr_b16 v[218 + ((\\p) %% 10) * 4 : 219 + ((\\p) %% 10) * 4], v215 "                             \
+  "offset:((\\co) + ((\\db) >> 2) * 256)\n"                                                                        \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* a stream: nsx S/dP fragments (one LDS instruction each), then, if dq, 2 NB dQ */                            \
+  /* fragments (blocks of the first 16 keys, then of the second; two instructions each) */                       \
+  ".macro FQ_RD p, nsx, dq\n"                                                                                      \
+  "  .if (\\p) < (\\nsx)\n"                                                                                        \
+  "    .if ((\\p) & 1) == 0\n"                                                                                     \
+  "      FQ_RX (\\p), %[rb], v214\n"                                                                               \
+  "    .else\n"                                                                                                    \
+  "      FQ_RX (\\p), %[rv], v215\n"                                                                               \
+  "    .endif\n"                                                                                                   \
+  "  .elseif (\\dq) && ((\\p) < (\\nsx) + %[nb])\n"                                                                \
+  "    FQ_TX ((\\p) - (\\nsx)), 0, (\\p)\n"                                                                        \
+  "  .elseif (\\dq) && ((\\p) < (\\nsx) + 2 * %[nb])\n"                                                            \
+  "    FQ_TX ((\\p) - (\\nsx) - %[nb]), 8192, (\\p)\n"                                                             \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* wait for the fragments before position a with those before b issued */                                     \
+  ".macro FQ_WT2 a, b, nsx\n"                                                                                      \
+  "  .if (\\b) <= (\\nsx)\n"                                                                                       \
+  "    FQ_WAIT ((\\b) - (\\a))\n"                                                                                  \
+  "  .elseif (\\a) >= (\\nsx)\n"                                                                                   \
+  "    FQ_WAIT (2 * ((\\b) - (\\a)))\n"                                                                            \
+  "  .else\n"                                                                                                      \
+  "    FQ_WAIT (((\\nsx) - (\\a)) + 2 * ((\\b) - (\\nsx)))\n"                                                      \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  ".macro FQ_WT m, nsx, dq\n"                                                                                      \
+  "  .if (\\m) + 10 <= (\\nsx) + 2 * %[nb] * (\\dq)\n"                                                              \
+  "    FQ_WT2 ((\\m) + 1), ((\\m) + 10), (\\nsx)\n"                                                                 \
+  "  .else\n"                                                                                                      \
+  "    FQ_WT2 ((\\m) + 1), ((\\nsx) + 2 * %[nb] * (\\dq)), (\\nsx)\n"                                              \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* next tile's copy, load n (0..7 K rows, 8..15 V rows) of this wave's share: global */                      \
+  /* offset (co + 1024 i) ^ (k_i << 4), k_i = 8 (i & 1) + i / 2, into LDS at M0 */                             \
+  ".macro FQ_CP n\n"                                                                                              \
+  "  v_add_u32 v214, ((\\n) & 7) * 1024, %[co]\n"                                                                \
+  "  .if ((((\\n) & 1) << 3) | (((\\n) & 7) >> 1)) != 0\n"                                                       \
+  "    v_xor_b32 v214, ((((\\n) & 1) << 3) | (((\\n) & 7) >> 1)) << 4, v214\n"                                      \
+  "  .endif\n"                                                                                                     \
+  "  .if ((\\n) >> 3) == 0\n"                                                                                     \
+  "    s_add_u32 m0, %[lk], ((\\n) & 7) * 1024\n"                                                                 \
+  "  .else\n"                                                                                                      \
+  "    s_add_u32 m0, %[lv], ((\\n) & 7) * 1024\n"                                                                 \
+  "  .endif\n"                                                                                                     \
+  "  s_mov_b64 exec, %[cx]\n"                                                                                      \
+  "  .if ((\\n) >> 3) == 0\n"                                                                                     \
+  "    global_load_lds_dwordx4 v214, %[kg]\n"                                                                      \
+  "  .else\n"                                                                                                      \
+  "    global_load_lds_dwordx4 v214, %[vg]\n"                                                                      \
+  "  .endif\n"                                                                                                     \
+  "  s_mov_b64 exec, -1\n"                                                                                         \
+  ".endm\n"                                                                                                        \
+  /* after the MFMA at stream position m: copy load m / cps when m mod cps = cps - 1 */                           \
+  ".macro FQ_CPAT m, cps\n"                                                                                        \
+  "  .if %[cpon] && (((\\m) %% (\\cps)) == ((\\cps) - 1)) && (((\\m) / (\\cps)) < 16)\n"                         \
+  "    FQ_CP ((\\m) / (\\cps))\n"                                                                                  \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* dS work in the shadow of S/dP MFMA m: element m's fma and subtraction, element */                           \
+  /* m-1's exp, element m-2's product, pair (m-3)/2's pack */                                                    \
+  ".macro FQ_V m\n"                                                                                                \
+  "  .if (\\m) < 16\n"                                                                                             \
+  "    v_fma_f32 v[%[sp] + (\\m)], v[%[sp] + (\\m)], %[c], %[nl]\n"                                                \
+  "    v_sub_f32 v[%[sp] + 16 + (\\m)], v[%[sp] + 16 + (\\m)], %[dl]\n"                                            \
+  "  .endif\n"                                                                                                     \
+  "  .if ((\\m) >= 1) && ((\\m) <= 16)\n"                                                                          \
+  "    v_exp_f32 v[%[sp] + (\\m) - 1], v[%[sp] + (\\m) - 1]\n"                                                     \
+  "  .endif\n"                                                                                                     \
+  "  .if ((\\m) >= 2) && ((\\m) <= 17)\n"                                                                          \
+  "    v_mul_f32 v[%[sp] + (\\m) - 2], v[%[sp] + (\\m) - 2], v[%[sp] + 16 + (\\m) - 2]\n"                          \
+  "  .endif\n"                                                                                                     \
+  "  .if ((\\m) >= 3) && ((\\m) <= 17) && (((\\m) & 1) == 1)\n"                                                     \
+  "    v_cvt_pk_bf16_f32 v[206 + ((\\m) - 3) / 2], v[%[sp] + (\\m) - 3], v[%[sp] + (\\m) - 2]\n"                    \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* S/dP MFMA m (S for even m, dP for odd, k-step m/2), then the read 10 ahead and, if v, dS work */             \
+  ".macro FQ_SM m, nsx, dq, v, cps\n"                                                                                   \
+  "  .if (\\m) < (\\nsx)\n"                                                                                        \
+  "    FQ_WT (\\m), (\\nsx), (\\dq)\n"                                                                             \
+  "    .if ((\\m) >> 1) == 0\n"                                                                                    \
+  "      v_mfma_f32_32x32x16_bf16 v[%[sn] + ((\\m) & 1) * 16 : %[sn] + ((\\m) & 1) * 16 + 15], "                  \
+  "v[216 + ((\\m) %% 10) * 4 : 219 + ((\\m) %% 10) * 4], "                                                          \
+  "a[((\\m) & 1) * 64 + ((\\m) >> 1) * 4 : ((\\m) & 1) * 64 + ((\\m) >> 1) * 4 + 3], 0\n"                          \
+  "    .else\n"                                                                                                    \
+  "      v_mfma_f32_32x32x16_bf16 v[%[sn] + ((\\m) & 1) * 16 : %[sn] + ((\\m) & 1) * 16 + 15], "                  \
+  "v[216 + ((\\m) %% 10) * 4 : 219 + ((\\m) %% 10) * 4], "                                                          \
+  "a[((\\m) & 1) * 64 + ((\\m) >> 1) * 4 : ((\\m) & 1) * 64 + ((\\m) >> 1) * 4 + 3], "                            \
+  "v[%[sn] + ((\\m) & 1) * 16 : %[sn] + ((\\m) & 1) * 16 + 15]\n"                                                 \
+  "    .endif\n"                                                                                                   \
+  "    FQ_RD ((\\m) + 10), (\\nsx), (\\dq)\n"                                                                       \
+  "    .if (\\v)\n"                                                                                                \
+  "      FQ_V (\\m)\n"                                                                                             \
+  "    .endif\n"                                                                                                   \
+  "    FQ_CPAT (\\m), (\\cps)\n"                                                                                  \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* dQ MFMA of dQ fragment f (stream position nsx + f) into block a[128 + 16 db], B operand b */                \
+  ".macro FQ_DM f, lim, db, b, nsx, cps\n"                                                                              \
+  "  .if (\\f) < (\\lim)\n"                                                                                        \
+  "    FQ_WT ((\\nsx) + (\\f)), (\\nsx), 1\n"                                                                      \
+  "    v_mfma_f32_32x32x16_bf16 a[128 + 16 * (\\db) : 143 + 16 * (\\db)], "                                        \
+  "v[216 + (((\\nsx) + (\\f)) %% 10) * 4 : 219 + (((\\nsx) + (\\f)) %% 10) * 4], \\b, "                              \
+  "a[128 + 16 * (\\db) : 143 + 16 * (\\db)]\n"                                                                     \
+  "    FQ_RD ((\\nsx) + (\\f) + 10), (\\nsx), 1\n"                                                                  \
+  "    FQ_CPAT ((\\nsx) + (\\f)), (\\cps)\n"                                                                     \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  ".macro FQ_SMS nsx, dq, v, cps\n"                                                                                     \
+  "  FQ_SM 0, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 1, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 2, \\nsx, \\dq, \\v, \\cps\n"                          \
+  "  FQ_SM 3, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 4, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 5, \\nsx, \\dq, \\v, \\cps\n"                          \
+  "  FQ_SM 6, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 7, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 8, \\nsx, \\dq, \\v, \\cps\n"                          \
+  "  FQ_SM 9, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 10, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 11, \\nsx, \\dq, \\v, \\cps\n"                        \
+  "  FQ_SM 12, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 13, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 14, \\nsx, \\dq, \\v, \\cps\n"                       \
+  "  FQ_SM 15, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 16, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 17, \\nsx, \\dq, \\v, \\cps\n"                       \
+  "  FQ_SM 18, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 19, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 20, \\nsx, \\dq, \\v, \\cps\n"                       \
+  "  FQ_SM 21, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 22, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 23, \\nsx, \\dq, \\v, \\cps\n"                       \
+  "  FQ_SM 24, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 25, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 26, \\nsx, \\dq, \\v, \\cps\n"                       \
+  "  FQ_SM 27, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 28, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 29, \\nsx, \\dq, \\v, \\cps\n"                       \
+  "  FQ_SM 30, \\nsx, \\dq, \\v, \\cps\n  FQ_SM 31, \\nsx, \\dq, \\v, \\cps\n"                                                    \
+  ".endm\n"                                                                                                        \
+  ".macro FQ_DMS b0, b1, nsx, cps\n"                                                                                    \
+  "  FQ_DM 0, %[nb], 0, \\b0, \\nsx, \\cps\n  FQ_DM 1, %[nb], 1, \\b0, \\nsx, \\cps\n  FQ_DM 2, %[nb], 2, \\b0, \\nsx, \\cps\n"            \
+  "  FQ_DM 3, %[nb], 3, \\b0, \\nsx, \\cps\n  FQ_DM 4, %[nb], 4, \\b0, \\nsx, \\cps\n  FQ_DM 5, %[nb], 5, \\b0, \\nsx, \\cps\n"            \
+  "  FQ_DM 6, %[nb], 6, \\b0, \\nsx, \\cps\n  FQ_DM 7, %[nb], 7, \\b0, \\nsx, \\cps\n"                                             \
+  "  FQ_DM %[nb]+0, 2*%[nb], 0, \\b1, \\nsx, \\cps\n  FQ_DM %[nb]+1, 2*%[nb], 1, \\b1, \\nsx, \\cps\n"                              \
+  "  FQ_DM %[nb]+2, 2*%[nb], 2, \\b1, \\nsx, \\cps\n  FQ_DM %[nb]+3, 2*%[nb], 3, \\b1, \\nsx, \\cps\n"                              \
+  "  FQ_DM %[nb]+4, 2*%[nb], 4, \\b1, \\nsx, \\cps\n  FQ_DM %[nb]+5, 2*%[nb], 5, \\b1, \\nsx, \\cps\n"                              \
+  "  FQ_DM %[nb]+6, 2*%[nb], 6, \\b1, \\nsx, \\cps\n  FQ_DM %[nb]+7, 2*%[nb], 7, \\b1, \\nsx, \\cps\n"                              \
+  ".endm\n"                                                                                                        \
+  "s_cmp_eq_u32 %[mode], 2\n"                                                                                      \
+  "s_cbranch_scc1 L_full_%=\n"                                                                                     \
+  "s_cmp_eq_u32 %[mode], 1\n"                                                                                      \
+  "s_cbranch_scc1 L_first_%=\n"                                                                                    \
+  "s_cmp_eq_u32 %[mode], 3\n"                                                                                      \
+  "s_cbranch_scc1 L_dq_%=\n"                                                                                       \
+  ".if %[cpon]\n"                                                                                                 \
+  "  FQ_CP 0\n  FQ_CP 1\n  FQ_CP 2\n  FQ_CP 3\n  FQ_CP 4\n  FQ_CP 5\n  FQ_CP 6\n  FQ_CP 7\n"                        \
+  "  FQ_CP 8\n  FQ_CP 9\n  FQ_CP 10\n  FQ_CP 11\n  FQ_CP 12\n  FQ_CP 13\n  FQ_CP 14\n  FQ_CP 15\n"                  \
+  ".endif\n"                                                                                                       \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_full_%=:\n"                                                                                                   \
+  "FQ_RD 0, 2 * %[ns], 1\nFQ_RD 1, 2 * %[ns], 1\nFQ_RD 2, 2 * %[ns], 1\nFQ_RD 3, 2 * %[ns], 1\nFQ_RD 4, 2 * %[ns], 1\n"      \
+  "FQ_RD 5, 2 * %[ns], 1\nFQ_RD 6, 2 * %[ns], 1\nFQ_RD 7, 2 * %[ns], 1\nFQ_RD 8, 2 * %[ns], 1\nFQ_RD 9, 2 * %[ns], 1\n"      \
+  "FQ_SMS (2 * %[ns]), 1, 1, 3\n"                                                                                  \
+  "FQ_DMS v[206:209], v[210:213], (2 * %[ns]), 3\n"                                                                \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_first_%=:\n"                                                                                                  \
+  "FQ_RD 0, 2 * %[ns], 0\nFQ_RD 1, 2 * %[ns], 0\nFQ_RD 2, 2 * %[ns], 0\nFQ_RD 3, 2 * %[ns], 0\nFQ_RD 4, 2 * %[ns], 0\n"      \
+  "FQ_RD 5, 2 * %[ns], 0\nFQ_RD 6, 2 * %[ns], 0\nFQ_RD 7, 2 * %[ns], 0\nFQ_RD 8, 2 * %[ns], 0\nFQ_RD 9, 2 * %[ns], 0\n"      \
+  "FQ_SMS (2 * %[ns]), 0, 0, 2\n"                                                                                  \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_dq_%=:\n"                                                                                                     \
+  "FQ_RD 0, 0, 1\nFQ_RD 1, 0, 1\nFQ_RD 2, 0, 1\nFQ_RD 3, 0, 1\nFQ_RD 4, 0, 1\n"      \
+  "FQ_RD 5, 0, 1\nFQ_RD 6, 0, 1\nFQ_RD 7, 0, 1\nFQ_RD 8, 0, 1\nFQ_RD 9, 0, 1\n"      \
+  "FQ_DMS %[d0], %[d1], 0, 1\n"                                                                                    \
+  "L_end_%=:\n"                                                                                                    \
+  "s_nop 7\ns_nop 7\ns_nop 7\n" /* MFMA results may be read by vector instructions next */                         \
+  ".purgem FQ_WAIT\n.purgem FQ_RX\n.purgem FQ_TX\n.purgem FQ_RD\n.purgem FQ_WT2\n.purgem FQ_WT\n"                \
+  ".purgem FQ_V\n.purgem FQ_SM\n.purgem FQ_DM\n.purgem FQ_SMS\n.purgem FQ_DMS\n.purgem FQ_CP\n.purgem FQ_CPAT\n"
 
-// DQ_WAIT n: s_waitcnt lgkmcnt(n) for an assemble-time n in 0..11
-#define DQ_WAIT_MACRO                                \
-  ".macro DQ_WAIT n\n"                               \
-  "  .if (\\n) <= 0\n    s_waitcnt lgkmcnt(0)\n"     \
-  "  .elseif (\\n) == 1\n    s_waitcnt lgkmcnt(1)\n" \
-  "  .elseif (\\n) == 2\n    s_waitcnt lgkmcnt(2)\n" \
-  "  .elseif (\\n) == 3\n    s_waitcnt lgkmcnt(3)\n" \
-  "  .elseif (\\n) == 4\n    s_waitcnt lgkmcnt(4)\n" \
-  "  .elseif (\\n) == 5\n    s_waitcnt lgkmcnt(5)\n" \
-  "  .elseif (\\n) == 6\n    s_waitcnt lgkmcnt(6)\n" \
-  "  .elseif (\\n) == 7\n    s_waitcnt lgkmcnt(7)\n" \
-  "  .elseif (\\n) == 8\n    s_waitcnt lgkmcnt(8)\n" \
-  "  .elseif (\\n) == 9\n    s_waitcnt lgkmcnt(9)\n" \
-  "  .elseif (\\n) == 10\n    s_waitcnt lgkmcnt(10)\n" \
-  "  .else\n    s_waitcnt lgkmcnt(11)\n"             \
-  "  .endif\n"                                       \
-  ".endm\n"
+#define DQ_STEP_INPUTS                                                                                                 \
+  [ns] "i"(NS), [nb] "i"(NB), [cpon] "i"(NS == 16 ? 1 : 0), [mode] "s"(mode), [rb] "v"(rb), [rv] "v"(rv),         \
+      [t1] "v"(t1), [t2] "v"(t2), [c] "v"(c), [kg] "s"(cp.kg), [vg] "s"(cp.vg), [lk] "s"(cp.lk), [lv] "s"(cp.lv),   \
+      [cx] "s"(cp.exec), [co] "v"(cp.co),                                                                       \
+      [nl] "v"(nl), [dl] "v"(dl), [d0] "v"(d0), [d1] "v"(d1), "{a[0:15]}"(qo[0]), "{a[16:31]}"(qo[1]),             \
+      "{a[32:47]}"(qo[2]), "{a[48:63]}"(qo[3]), "{a[64:79]}"(qo[4]), "{a[80:95]}"(qo[5]), "{a[96:111]}"(qo[6]),    \
+      "{a[112:127]}"(qo[7])
+#define DQ_STEP_ACC                                                                                          \
+  "+{a[128:143]}"(q[0]), "+{a[144:159]}"(q[1]), "+{a[160:175]}"(q[2]), "+{a[176:191]}"(q[3]),               \
+      "+{a[192:207]}"(q[4]), "+{a[208:223]}"(q[5]), "+{a[224:239]}"(q[6]), "+{a[240:255]}"(q[7])
+#define DQ_STEP_CLOBBERS                                                                                          \
+  "memory", "scc", "m0", "exec", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", \
+      "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", \
+      "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", \
+      "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", \
+      "v255"
 
-#define DQ_CHAIN_CLOBBERS                                                                                      \
-  "memory", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", \
-      "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
+// The next tile's copy as the step issues it: this wave's loads i = 0..7
+// of K rows then of V rows, from global tile bases kg, vg (whole tiles) to
+// LDS lk, lv (this wave's share of the slots) + 1024 i, at lane offsets
+// (co + 1024 i) ^ (k_i << 4) with k_i = 8 (i mod 2) + i / 2 -- the
+// swizzled row copy's offsets, which differ from one load to the next only
+// in those bits.  exec = 0 leaves the loads out.
+struct DqStepCopy {
+  uint64_t kg, vg;
+  uint32_t lk, lv;
+  uint64_t exec;
+  int co;
+};
 
-// S^T = K_j Q^T and dP^T = V_j dO^T over NS k-steps of 16 columns,
-// interleaved: MFMA i takes k-step i/2, S for even i and dP for odd i.  rb
-// is the lane's address of chunk 0 of its K row in the ring slot; k-step ds
-// is chunk 2 ds + half: rb ^ 32 (ds mod 8), 256 bytes further for ds >= 8,
-// and the V slot lies 32768 bytes after the K slot.  Each accumulator runs
-// its k-steps in order, as the plain loop does.
-template <int NS>
-__device__ __forceinline__ void dq_sdp_chain(int rb, const f32x16 (&qo)[8], f32x16& s, f32x16& dp) {
-  static_assert(NS >= 4 && NS <= 16, "chain length");
-  asm volatile(
-      DQ_WAIT_MACRO
-      // read fragment i into buffer i mod 6
-      ".macro DQ_RD i\n"
-      "  .if (\\i) < 2 * %[ns]\n"
-      "    .if (((\\i) >> 1) & 7) == 0\n"
-      "      ds_read_b128 v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], %[rb] "
-      "offset:(((\\i) & 1) * 32768 + (((\\i) >> 4) & 1) * 256)\n"
-      "    .else\n"
-      "      v_xor_b32 v[230 + ((\\i) & 1)], 32 * (((\\i) >> 1) & 7), %[rb]\n"
-      "      ds_read_b128 v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], v[230 + ((\\i) & 1)] "
-      "offset:(((\\i) & 1) * 32768 + (((\\i) >> 4) & 1) * 256)\n"
-      "    .endif\n"
-      "  .endif\n"
-      ".endm\n"
-      ".macro DQ_MM i, acc\n"
-      "  .if (\\i) < 2 * %[ns]\n"
-      "    .if (\\i) + 6 < 2 * %[ns]\n"
-      "      DQ_WAIT 5\n"
-      "    .else\n"
-      "      DQ_WAIT (2 * %[ns] - (\\i) - 1)\n"
-      "    .endif\n"
-      "    .if ((\\i) >> 1) == 0\n"
-      "      v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], "
-      "a[((\\i) & 1) * 64 + ((\\i) >> 1) * 4 : ((\\i) & 1) * 64 + ((\\i) >> 1) * 4 + 3], 0\n"
-      "    .else\n"
-      "      v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\i) %% 6) * 4 : 235 + ((\\i) %% 6) * 4], "
-      "a[((\\i) & 1) * 64 + ((\\i) >> 1) * 4 : ((\\i) & 1) * 64 + ((\\i) >> 1) * 4 + 3], \\acc\n"
-      "    .endif\n"
-      "    DQ_RD (\\i) + 6\n"
-      "  .endif\n"
-      ".endm\n"
-      "DQ_RD 0\nDQ_RD 1\nDQ_RD 2\nDQ_RD 3\nDQ_RD 4\nDQ_RD 5\n"
-      "DQ_MM 0, %[s]\nDQ_MM 1, %[dp]\nDQ_MM 2, %[s]\nDQ_MM 3, %[dp]\n"
-      "DQ_MM 4, %[s]\nDQ_MM 5, %[dp]\nDQ_MM 6, %[s]\nDQ_MM 7, %[dp]\n"
-      "DQ_MM 8, %[s]\nDQ_MM 9, %[dp]\nDQ_MM 10, %[s]\nDQ_MM 11, %[dp]\n"
-      "DQ_MM 12, %[s]\nDQ_MM 13, %[dp]\nDQ_MM 14, %[s]\nDQ_MM 15, %[dp]\n"
-      "DQ_MM 16, %[s]\nDQ_MM 17, %[dp]\nDQ_MM 18, %[s]\nDQ_MM 19, %[dp]\n"
-      "DQ_MM 20, %[s]\nDQ_MM 21, %[dp]\nDQ_MM 22, %[s]\nDQ_MM 23, %[dp]\n"
-      "DQ_MM 24, %[s]\nDQ_MM 25, %[dp]\nDQ_MM 26, %[s]\nDQ_MM 27, %[dp]\n"
-      "DQ_MM 28, %[s]\nDQ_MM 29, %[dp]\nDQ_MM 30, %[s]\nDQ_MM 31, %[dp]\n"
-      "s_nop 7\ns_nop 7\ns_nop 7\n"  // S and dP are read by vector instructions next
-      ".purgem DQ_WAIT\n.purgem DQ_RD\n.purgem DQ_MM\n"
-      : [s] "=&v"(s), [dp] "=&v"(dp)
-      : [ns] "i"(NS), [rb] "v"(rb), "{a[0:15]}"(qo[0]), "{a[16:31]}"(qo[1]), "{a[32:47]}"(qo[2]),
-        "{a[48:63]}"(qo[3]), "{a[64:79]}"(qo[4]), "{a[80:95]}"(qo[5]), "{a[96:111]}"(qo[6]), "{a[112:127]}"(qo[7])
-      : DQ_CHAIN_CLOBBERS);
+// PAR 0: the new S/dP go to v[142:173] (set A), the previous ones are in
+// v[174:205] (set B); PAR 1 the other way round.  Both sets are in-out
+// operands in every mode, so that they too stay in place.
+template <int NS, int NB, int PAR>
+__device__ __forceinline__ void dq_step(int mode, int rb, int rv, int t1, int t2, float c, float nl, float dl,
+                                        const bf16x8& d0, const bf16x8& d1, const DqStepCopy& cp,
+                                        const f32x16 (&qo)[8], f32x16& sa, f32x16& da, f32x16& sb, f32x16& db,
+                                        f32x16 (&q)[8]) {
+  static_assert(NS >= 9 && NS <= 16 && NB >= 4 && NB <= 8, "shape");  // in-block dS ends at MFMA 17
+  if constexpr (PAR == 0) {
+    asm volatile(DQ_STEP_TEXT
+                 : "+{v[142:157]}"(sa), "+{v[158:173]}"(da), "+{v[174:189]}"(sb), "+{v[190:205]}"(db), DQ_STEP_ACC
+                 : [sn] "i"(142), [sp] "i"(174), DQ_STEP_INPUTS
+                 : DQ_STEP_CLOBBERS);
+  } else {
+    asm volatile(DQ_STEP_TEXT
+                 : "+{v[142:157]}"(sa), "+{v[158:173]}"(da), "+{v[174:189]}"(sb), "+{v[190:205]}"(db), DQ_STEP_ACC
+                 : [sn] "i"(174), [sp] "i"(142), DQ_STEP_INPUTS
+                 : DQ_STEP_CLOBBERS);
+  }
 }
-
-// dQ^T += K_j^T dS^T over NB 32-column blocks, K_j^T read transposed
-// (two ds_read_b64_tr_b16 per fragment, 8 rows apart).  Fragment order:
-// the first 16 keys (dS^T chunk d0) for blocks 0..NB-1, then the second 16
-// (d1), so each accumulator takes its two chunks in order.  t1 and t2 are
-// the lane's addresses of the two reads of block 0's first chunk; block db
-// is t ^ 64 (db mod 4), 256 bytes further for db >= 4, and the second chunk
-// 8192.  Accumulators past NB are not touched.
-template <int NB>
-__device__ __forceinline__ void dq_tr_chain(int t1, int t2, const bf16x8& d0, const bf16x8& d1, f32x16& q0,
-                                            f32x16& q1, f32x16& q2, f32x16& q3, f32x16& q4, f32x16& q5,
-                                            f32x16& q6, f32x16& q7) {
-  static_assert(NB >= 4 && NB <= 8, "blocks");
-  asm volatile(
-      DQ_WAIT_MACRO
-      // the two reads of block db, chunk offset co, into buffer f mod 6
-      ".macro DT_RDX db, co, f\n"
-      "  .if ((\\db) & 3) == 0\n"
-      "    ds_read_b64_tr_b16 v[232 + ((\\f) %% 6) * 4 : 233 + ((\\f) %% 6) * 4], %[t1] "
-      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
-      "    ds_read_b64_tr_b16 v[234 + ((\\f) %% 6) * 4 : 235 + ((\\f) %% 6) * 4], %[t2] "
-      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
-      "  .else\n"
-      "    v_xor_b32 v230, 64 * ((\\db) & 3), %[t1]\n"
-      "    v_xor_b32 v231, 64 * ((\\db) & 3), %[t2]\n"
-      "    ds_read_b64_tr_b16 v[232 + ((\\f) %% 6) * 4 : 233 + ((\\f) %% 6) * 4], v230 "
-      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
-      "    ds_read_b64_tr_b16 v[234 + ((\\f) %% 6) * 4 : 235 + ((\\f) %% 6) * 4], v231 "
-      "offset:((\\co) + ((\\db) >> 2) * 256)\n"
-      "  .endif\n"
-      ".endm\n"
-      // fragment f: block f of the first chunk (f < NB) or f - NB of the second
-      ".macro DT_RD f\n"
-      "  .if (\\f) < %[nb]\n"
-      "    DT_RDX (\\f), 0, (\\f)\n"
-      "  .elseif (\\f) < 2 * %[nb]\n"
-      "    DT_RDX ((\\f) - %[nb]), 8192, (\\f)\n"
-      "  .endif\n"
-      ".endm\n"
-      ".macro DT_MM f, lim, acc, b\n"
-      "  .if (\\f) < (\\lim)\n"
-      "    .if (\\f) + 6 < 2 * %[nb]\n"
-      "      DQ_WAIT 10\n"
-      "    .else\n"
-      "      DQ_WAIT (2 * (2 * %[nb] - (\\f) - 1))\n"
-      "    .endif\n"
-      "    v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\f) %% 6) * 4 : 235 + ((\\f) %% 6) * 4], \\b, \\acc\n"
-      "    DT_RD (\\f) + 6\n"
-      "  .endif\n"
-      ".endm\n"
-      "DT_RD 0\nDT_RD 1\nDT_RD 2\nDT_RD 3\nDT_RD 4\nDT_RD 5\n"
-      "DT_MM 0, %[nb], %[q0], %[d0]\nDT_MM 1, %[nb], %[q1], %[d0]\n"
-      "DT_MM 2, %[nb], %[q2], %[d0]\nDT_MM 3, %[nb], %[q3], %[d0]\n"
-      "DT_MM 4, %[nb], %[q4], %[d0]\nDT_MM 5, %[nb], %[q5], %[d0]\n"
-      "DT_MM 6, %[nb], %[q6], %[d0]\nDT_MM 7, %[nb], %[q7], %[d0]\n"
-      "DT_MM %[nb]+0, 2*%[nb], %[q0], %[d1]\nDT_MM %[nb]+1, 2*%[nb], %[q1], %[d1]\n"
-      "DT_MM %[nb]+2, 2*%[nb], %[q2], %[d1]\nDT_MM %[nb]+3, 2*%[nb], %[q3], %[d1]\n"
-      "DT_MM %[nb]+4, 2*%[nb], %[q4], %[d1]\nDT_MM %[nb]+5, 2*%[nb], %[q5], %[d1]\n"
-      "DT_MM %[nb]+6, 2*%[nb], %[q6], %[d1]\nDT_MM %[nb]+7, 2*%[nb], %[q7], %[d1]\n"
-      "s_nop 7\ns_nop 7\ns_nop 7\n"  // the accumulators may be read by vector instructions next
-      ".purgem DQ_WAIT\n.purgem DT_RDX\n.purgem DT_RD\n.purgem DT_MM\n"
-      : [q0] "+v"(q0), [q1] "+v"(q1), [q2] "+v"(q2), [q3] "+v"(q3), [q4] "+v"(q4), [q5] "+v"(q5), [q6] "+v"(q6),
-        [q7] "+v"(q7)
-      : [nb] "i"(NB), [d0] "v"(d0), [d1] "v"(d1), [t1] "v"(t1), [t2] "v"(t2)
-      : DQ_CHAIN_CLOBBERS);
-}
-
-#undef DQ_WAIT_MACRO
-#undef DQ_CHAIN_CLOBBERS
+#undef DQ_STEP_TEXT
+#undef DQ_STEP_INPUTS
+#undef DQ_STEP_ACC
+#undef DQ_STEP_CLOBBERS
 
 // ============================================================== dQ kernel
 //
@@ -228,15 +364,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   constexpr int KB = DqCfg<D>::kKB, kRowsQ = DqCfg<D>::kRows, kQBlocks = kWavesQ / DqCfg<D>::kSplit;
   constexpr int DP = DqCfg<D>::kDP;
   constexpr int kTileBytes = kKeyTile * DP * 2;
-  // 256-wide rows run the step as the two asm chains (one 32-key block per wave)
+  // 256-wide rows run the pipelined asm step (one 32-key block per wave)
   constexpr bool kChains = DP == 256;
   static_assert(!kChains || (KB == 1 && kTileBytes == 32768), "chain layout");
-  constexpr bool kSplitMask = kChains;
-  // ring slots K0 V0 K1 V1: a slot's V tile lies kTileBytes after its K tile
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * kTileBytes];
+  // ring: with the pipelined step K tiles j-1, j and V tile j are read while
+  // tile j+1 loads, in three K slots (tile t in slot t mod 3) and two V
+  // slots (slot 3 + t mod 2), 160 KB; otherwise K0 K1 V0 V1
+  constexpr int kSlots = kChains ? 5 : 4;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kSlots * kTileBytes];
   lds_char* smem = (lds_char*)smem_raw;
-  lds_char* kbuf[2] = {smem, smem + 2 * kTileBytes};
-  lds_char* vbuf[2] = {smem + kTileBytes, smem + 3 * kTileBytes};
+  lds_char* kbuf[2] = {smem, smem + kTileBytes};
+  lds_char* vbuf[2] = {smem + 2 * kTileBytes, smem + 3 * kTileBytes};
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
             half = lane >> 5;
@@ -266,17 +404,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   // per-lane offsets, rows clamped onto N-1 only for a ragged last tile
   RowTileCopier<D, DP, kKeyTile, kWavesQ> cp;
   cp.init(wave, lane);
-  auto copy_tile = [&](int t, int b) {
+  auto copy_tile = [&](int t, lds_char* kd, lds_char* vd) {
     const int row0 = t * kKeyTile;
     if (row0 + kKeyTile <= N) {
-      cp.copy_at(K, (uint32_t)row0 * (D * 2), kbuf[b]);
-      cp.copy_at(V, (uint32_t)row0 * (D * 2), vbuf[b]);
+      cp.copy_at(K, (uint32_t)row0 * (D * 2), kd);
+      cp.copy_at(V, (uint32_t)row0 * (D * 2), vd);
     } else {
-      cp.copy_clamped(K, N, row0, kbuf[b]);
-      cp.copy_clamped(V, N, row0, vbuf[b]);
+      cp.copy_clamped(K, N, row0, kd);
+      cp.copy_clamped(V, N, row0, vd);
     }
   };
-  copy_tile(0, 0);
+  if constexpr (kChains)
+    copy_tile(0, smem, smem + 3 * kTileBytes);
+  else
+    copy_tile(0, kbuf[0], vbuf[0]);
 
   // Q^T and dO^T as B operands (lane = query column), delta and L per lane.
   const int row = wq0 + l32;
@@ -331,21 +472,127 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     tofs2 = lds_off_bytes<DP>(r1 + 8, dcol >> 3) + (dcol & 7) * 2;
   }
 
-  for (int j = 0; j < nt; ++j) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (j + 1 < nt) copy_tile(j + 1, (j + 1) & 1);
-    if (!wave_active || j > wave_last) continue;
-    const lds_char* kt = kbuf[j & 1];
-    const lds_char* vt = vbuf[j & 1];
+  if constexpr (kChains) {
+    auto kslot = [&](int k) { return (int)(uint32_t)(uintptr_t)(smem + k * kTileBytes); };
+    const float nl = -lse2;
+    f32x16 sA, dA, sB, dB;  // S^T and dP^T of the last two tiles, tile t in set A for even t
+    // dS^T of tile jt (this wave's last, after its step) from its S and dP,
+    // masked where the tile needs it
+    auto last_ds = [&](int jt, const f32x16& st, const f32x16& dt, bf16x8& d0, bf16x8& d1) {
+      const bool masked = (CAUSAL && jt == wave_last) || (jt == n_ktiles_all - 1 && (N % kKeyTile) != 0);
+      auto make_ds = [&](auto mask_tag) {
+        constexpr bool kMask = decltype(mask_tag)::value;
+        asm volatile("" ::: "memory");  // keeps the two variants from being merged into selects
+        bf16x8 dsk[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x2 pr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int r = cc * 8 + 2 * i + t;
+              float x = __builtin_fmaf(st[r], c, nl);
+              if constexpr (kMask) {
+                const int key = jt * kKeyTile + kpart * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                bool keep = key < N;
+                if constexpr (CAUSAL) keep = keep && key <= row;
+                x = keep ? x : -__builtin_inff();
+              }
+              e[t] = fast_exp2(x) * (dt[r] - delta);
+            }
+            pr[i] = pack_bf16(e[0], e[1]);
+          }
+          dsk[cc] = join8(pr[0], pr[1], pr[2], pr[3]);
+        }
+        d0 = dsk[0];
+        d1 = dsk[1];
+      };
+      if (masked)
+        make_ds(std::true_type{});
+      else
+        make_ds(std::false_type{});
+    };
+    // this wave's copy offsets: the row copy's (co + 1024 i) ^ (k_i << 4) at D = 256
+    constexpr bool kAsmCopy = D == 256;
+    const int co = (wave * 16 + half) * 512 + ((l32 ^ (half << 2)) << 4);
+    const uint32_t smem_u = (uint32_t)(uintptr_t)smem;
+    int ks = 0;  // K slot of tile j
+    // step j (j may be nt, a step with nothing to do): publishes tile j,
+    // starts loading j+1, then S/dP of tile j with dS and dQ of tile j-1
+    // (mode 1 at j = 0, 2 after); a wave one past its last tile finishes
+    // that tile (mode 3)
+    auto step = [&](int j, auto par_tag) {
+      constexpr int P = decltype(par_tag)::value;  // j mod 2: S/dP of tile j go to set A (0) or B (1)
+      wait_vmcnt<0>();
+      __syncthreads();
+      const int ks_next = ks == 2 ? 0 : ks + 1, ks_prev = ks == 0 ? 2 : ks - 1;
+      DqStepCopy cpy = {0, 0, 0, 0, 0, co};
+      if (j + 1 < nt) {
+        const int vs_next = 3 + ((j + 1) & 1);
+        if (kAsmCopy && (j + 2) * kKeyTile <= N) {  // a whole tile: the step issues it
+          const size_t off = (size_t)(j + 1) * kKeyTile * D;
+          cpy.kg = (uint64_t)(uintptr_t)(K + off);
+          cpy.vg = (uint64_t)(uintptr_t)(V + off);
+          cpy.lk = smem_u + ks_next * kTileBytes + wave * 8192;
+          cpy.lv = smem_u + vs_next * kTileBytes + wave * 8192;
+          cpy.exec = ~0ull;
+        } else {
+          copy_tile(j + 1, smem + ks_next * kTileBytes, smem + vs_next * kTileBytes);
+        }
+      }
+      int mode = 0;
+      bf16x8 d0 = {}, d1 = {};
+      if (wave_active) {
+        if (j <= wave_last) {
+          mode = j == 0 ? 1 : 2;
+        } else if (CAUSAL && j == wave_last + 1 && j < nt) {  // (unmasked, a wave's last tile is nt-1)
+          mode = 3;
+          if constexpr (P == 1)
+            last_ds(j - 1, sA, dA, d0, d1);
+          else
+            last_ds(j - 1, sB, dB, d0, d1);
+        }
+      }
+      const int kb = kslot(ks), vb = kslot(3 + P), pb = kslot(ks_prev);
+      dq_step<kDSteps, kDBlocks, P>(__builtin_amdgcn_readfirstlane(mode), kb + rofs, vb + rofs, pb + tofs1,
+                                    pb + tofs2, c, nl, delta, d0, d1, cpy, qo, sA, dA, sB, dB, dq);
+      ks = ks_next;
+    };
+    for (int j = 0; j < nt; j += 2) {
+      step(j, std::integral_constant<int, 0>{});
+      step(j + 1, std::integral_constant<int, 1>{});
+    }
+    // the workgroup's last tile nt-1, if it is this wave's last, in its K
+    // slot (nt-1) mod 3
+    {
+      int mode = 0;
+      bf16x8 d0 = {}, d1 = {};
+      if (wave_active && wave_last == nt - 1) {
+        mode = 3;
+        if ((nt - 1) & 1)
+          last_ds(nt - 1, sB, dB, d0, d1);
+        else
+          last_ds(nt - 1, sA, dA, d0, d1);
+      }
+      const int pb = kslot((nt - 1) % 3);
+      const DqStepCopy none = {0, 0, 0, 0, 0, co};
+      dq_step<kDSteps, kDBlocks, 0>(__builtin_amdgcn_readfirstlane(mode), 0, 0, pb + tofs1, pb + tofs2, c, nl, delta,
+                                    d0, d1, none, qo, sA, dA, sB, dB, dq);
+    }
+  } else {
+    for (int j = 0; j < nt; ++j) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 1 < nt) copy_tile(j + 1, kbuf[(j + 1) & 1], vbuf[(j + 1) & 1]);
+      if (!wave_active || j > wave_last) continue;
+      const lds_char* kt = kbuf[j & 1];
+      const lds_char* vt = vbuf[j & 1];
 
-    // S^T = K_j Q^T and dP^T = V_j dO^T, keys kr0 + kb*32.. (rows), this wave's queries (columns)
-    const int kr0 = kpart * 32;
-    const int tb = (int)(uint32_t)(uintptr_t)kt;
-    f32x16 s[KB], dp[KB];
-    if constexpr (kChains) {
-      dq_sdp_chain<kDSteps>(tb + rofs, qo, s[0], dp[0]);
-    } else {
+      // S^T = K_j Q^T and dP^T = V_j dO^T, keys kr0 + kb*32.. (rows), this wave's queries (columns)
+      const int kr0 = kpart * 32;
+      f32x16 s[KB], dp[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -357,16 +604,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
           s[kb] = mfma32(read_row_operand<DP>(kt, kr0 + kb * 32 + l32, ds, half), qf[ds], s[kb]);
           dp[kb] = mfma32(read_row_operand<DP>(vt, kr0 + kb * 32 + l32, ds, half), dof[ds], dp[kb]);
         }
-    }
 
-    const bool masked = (CAUSAL && j == wave_last) || (j == n_ktiles_all - 1 && (N % kKeyTile) != 0);
-    bf16x8 dsk[KB][2];  // dS^T packed: [key block][16-key chunk]
-    // dS^T = P^T (dP^T - delta), with the key mask only on the tiles that
-    // need it (the empty asm keeps the two variants apart: merged, the
-    // mask's compares and selects ran on every tile)
-    auto make_ds = [&](auto mask_tag) {
-      constexpr bool kMask = decltype(mask_tag)::value;
-      asm volatile("" ::: "memory");
+      const bool masked = (CAUSAL && j == wave_last) || (j == n_ktiles_all - 1 && (N % kKeyTile) != 0);
+      bf16x8 dsk[KB][2];  // dS^T packed: [key block][16-key chunk]
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -379,7 +619,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
             for (int t = 0; t < 2; ++t) {
               const int r = cc * 8 + 2 * i + t;
               float x = __builtin_fmaf(s[kb][r], c, -lse2);
-              if (kMask && (kSplitMask || masked)) {
+              if (masked) {
                 const int key = j * kKeyTile + kr0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
                 bool keep = key < N;
                 if constexpr (CAUSAL) keep = keep && key <= row;
@@ -392,17 +632,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
           }
           dsk[kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
         }
-    };
-    if (!kSplitMask || masked)
-      make_ds(std::true_type{});
-    else
-      make_ds(std::false_type{});
 
-    // dQ^T += K_j^T dS^T
-    if constexpr (kChains) {
-      dq_tr_chain<kDBlocks>(tb + tofs1, tb + tofs2, dsk[0][0], dsk[0][1], dq[0], dq[1], dq[2], dq[3], dq[4],
-                            dq[kAcc - 3], dq[kAcc - 2], dq[kAcc - 1]);
-    } else {
+      // dQ^T += K_j^T dS^T
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
@@ -417,7 +648,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     // add the second key half's dQ partial sums (lane-major through LDS)
     float __attribute__((address_space(3)))* x =
         (float __attribute__((address_space(3)))*)smem + qblk * 64 * kDBlocks * 16 + lane;
-    static_assert(kQBlocks * 64 * kDBlocks * 16 * 4 <= 4 * kTileBytes, "merge buffer exceeds the ring");
+    static_assert(kQBlocks * 64 * kDBlocks * 16 * 4 <= kSlots * kTileBytes, "merge buffer exceeds the ring");
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with the K/V tiles
     if (kpart == 1) {

@@ -88,7 +88,7 @@ def test_workload_backward_c5():
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 256])
-@pytest.mark.parametrize("N", [1, 40, 64, 100, 256, 333])
+@pytest.mark.parametrize("N", [1, 40, 64, 100, 160, 256, 320, 333])
 def test_backward_shapes(N, D, causal):
     w = WORKLOADS["c5"].with_(name="edge", B=1, H=2, N=N, D=D, causal=causal, seed=3 * N + D)
     log(f"test_backward_shapes N={N} D={D} causal={causal}")

@@ -260,6 +260,14 @@ struct RowTileCopier {
     for (int i = 0; i < kLoads; ++i) load_lds16_s(base, off[i], lds + i * 64 * 16);
   }
 
+  // Load i (of kLoads) of copy_at alone, for copies spread between other work.
+  __device__ __forceinline__ void copy_one_at(const __bf16* __restrict__ src, uint32_t byte_off, lds_char* buf,
+                                              int i) const {
+    const char* base = (const char*)src + (uint32_t)__builtin_amdgcn_readfirstlane((int)byte_off);
+    const uint32_t lds = (uint32_t)(uintptr_t)buf + lds_wave;
+    load_lds16_s(base, off[i], lds + i * 64 * 16);
+  }
+
   // A tile reaching past row N-1 (row0 <= N-1): rows past it are clamped
   // onto it per lane.
   __device__ __forceinline__ void copy_clamped(const __bf16* __restrict__ src, int N, int row0, lds_char* buf) const {

@@ -123,6 +123,12 @@ struct FwdCfg {
   // set-up off the path from the barrier to the first score MFMAs.  The
   // 2-slot ring of D = 256 cannot spare the half step of lead.
   static constexpr bool kLateRefill = kDP == 128;
+  // 256-wide rows: the refill loads go between the step's MFMAs instead
+  // (K tile during phase A, V tile during phase B, about one load per two
+  // MFMAs).  Issued in one burst, the 16 loads of 1 KB per wave stalled
+  // the wave for about a thousand cycles a step while the vector memory
+  // path drained them, with the matrix core idle.
+  static constexpr bool kSpreadRefill = kDP == 256;
 };
 
 template <int D, bool CAUSAL, int QB, int W, bool QREG = false>
@@ -309,9 +315,19 @@ struct FwdKernel {
     return __builtin_bit_cast(bf16x8, v8);
   }
 
-  // S of the next tile (K buffer kt, into sn) + exp of this tile (sc).
+  // Loads n of a refill of L loads that go after MFMA i of M: [i L / M, (i + 1) L / M)
+  template <typename R>
+  __device__ __forceinline__ static void refill_after(R& refill, int i, int M) {
+    constexpr int L = C::kLoadsPerTile;
+#pragma unroll
+    for (int n = i * L / M; n < (i + 1) * L / M; ++n) refill(n);
+  }
+
+  // S of the next tile (K buffer kt, into sn) + exp of this tile (sc);
+  // refill(n) issues load n of a K refill (with kSpreadRefill).
+  template <typename R>
   __device__ __forceinline__ void phase_a(const lds_char* kt, const f32x16 (&sc)[KB][QB], f32x16 (&sn)[KB][QB],
-                                          float c) {
+                                          float c, R& refill) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mc[QB];
 #pragma unroll
@@ -351,12 +367,15 @@ struct FwdKernel {
         kf[i + kPf] = kfrag(kt, i + kPf);
         if (C::kQInLds && (i + kPf) % KB == 0) qv[(i + kPf) / KB] = qfrag(0, (i + kPf) / KB);
       }
+      if constexpr (C::kSpreadRefill) refill_after(refill, i, kKFrags);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // P V of the tile whose P is in pk (V buffer vt).
-  __device__ __forceinline__ void phase_b(const lds_char* vt) {
+  // P V of the tile whose P is in pk (V buffer vt); refill(n) issues load n
+  // of a V refill (with kSpreadRefill).
+  template <typename R>
+  __device__ __forceinline__ void phase_b(const lds_char* vt, R& refill) {
     bf16x8 vf[kVFrags];
 #pragma unroll
     for (int j = 0; j < kPf; ++j) vf[j] = vfrag(vt, j);
@@ -367,6 +386,7 @@ struct FwdKernel {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[j], pk[qb][kc >> 1][kc & 1], o[qb][db]);
       if (j + kPf < kVFrags) vf[j + kPf] = vfrag(vt, j + kPf);
+      if constexpr (C::kSpreadRefill) refill_after(refill, j, kVFrags);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -669,20 +689,38 @@ fwd_bf16_kernel(FwdArgs a, TileSched sched) {
     constexpr int j = decltype(jconst)::value;  // p % kUnroll
     constexpr int b = j % NB;                   // p % NB
     constexpr int cur = j & 1;                  // p % 2
-    wait_vmcnt<C::kStepsInFlight * 2 * C::kLoadsPerTile>();
+    // spread refills (whole tiles; SMALL copies clamp rows per lane and go
+    // in one burst): load n of K(p + LK), V(p + LV), slots freed by the
+    // barrier.  The V loads, issued last, may still be in flight here: the
+    // step waits for them (and a second barrier publishes them) just before
+    // phase B, the first reader of V(p).
+    constexpr bool kSpread = C::kSpreadRefill && !SMALL;
+    wait_vmcnt<kSpread ? C::kLoadsPerTile : C::kStepsInFlight * 2 * C::kLoadsPerTile>();
     __syncthreads();
-    if constexpr (!C::kLateRefill) {
+    if constexpr (!C::kLateRefill && !kSpread) {
       issue_k(p + LK, (b + LK) % NB);
       issue_v(p + LV, (b + LV) % NB);
     }
-    k.phase_a(k.kbuf((b + 1) % NB), k.s[cur], k.s[cur ^ 1], c);
+    const uint32_t rk_off = kSpread ? tile_bytes(p + LK) : 0u;
+    const uint32_t rv_off = kSpread ? tile_bytes(p + LV) : 0u;
+    auto refill_k = [&](int n) {
+      if constexpr (kSpread) cp.copy_one_at(K, rk_off, k.kbuf((b + LK) % NB), n);
+    };
+    auto refill_v = [&](int n) {
+      if constexpr (kSpread) cp.copy_one_at(V, rv_off, k.vbuf((b + LV) % NB), n);
+    };
+    k.phase_a(k.kbuf((b + 1) % NB), k.s[cur], k.s[cur ^ 1], c, refill_k);
     if constexpr (C::kLateRefill) {
       issue_k(p + LK, (b + LK) % NB);
       issue_v(p + LV, (b + LV) % NB);
     }
     k.settle_tile(k.s[cur], c);
     if (needs_mask(p + 1)) mask_tile(k.s[cur ^ 1], p + 1);
-    k.phase_b(k.vslot(b));
+    if constexpr (kSpread) {
+      wait_vmcnt<C::kLoadsPerTile>();  // V(p), older than this step's K loads
+      __syncthreads();
+    }
+    k.phase_b(k.vslot(b), refill_v);
   };
   for (int i = 0; i < nt; i += C::kUnroll)
     unrolled(i, nt, step, std::make_integer_sequence<int, C::kUnroll>());

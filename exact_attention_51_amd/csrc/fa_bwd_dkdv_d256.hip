@@ -64,13 +64,52 @@ struct KvDsplitCfg {
 // ds < 8; fragment ds >= 8 lies 256 bytes further (the swizzle permutes
 // chunks within each 16-chunk half of a 512-byte row).  Compiler-scheduled,
 // at 256 VGPRs this chain read one fragment at a time and waited for it.
+//
+// The chain also issues this wave's share of the next query tile's copy
+// (cp: 4 loads of Q rows, then 4 of dO rows, from the tiles' global bases
+// qg, og to LDS lq, lo + 1024 i at the copier's lane offsets), spread
+// between its MFMAs; exec = 0 leaves them out.  Issued in one burst after
+// the step's barrier, the 8 loads of 1 KB stalled the wave for about 500
+// cycles while the vector memory path drained them.
+struct KvCopy {
+  uint64_t qg, og;
+  uint32_t lq, lo;
+  uint64_t exec;
+  uint32_t off[4];
+};
+
 template <int NS>
 __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& kv0, const f32x16& kv1,
-                                           const f32x16& kv2, const f32x16& kv3) {
-  static_assert(NS >= 6 && NS <= 16, "chain length");
+                                           const f32x16& kv2, const f32x16& kv3, const KvCopy& cp) {
+  static_assert(NS >= 8 && NS <= 16, "chain length");
   f32x16 acc;
   f32x4 b[6];  // fragment buffers: fragment ds in buffer ds mod 6
   asm volatile(
+      // copy load n: Q rows (n < 4) or dO rows, load n mod 4 of the wave's share
+      ".macro KC_LD n\n"
+      "  .if ((\\n) >> 2) == 0\n"
+      "    s_add_u32 m0, %[lq], ((\\n) & 3) * 1024\n"
+      "  .else\n"
+      "    s_add_u32 m0, %[lo], ((\\n) & 3) * 1024\n"
+      "  .endif\n"
+      "  s_mov_b64 exec, %[cx]\n"
+      "  .if (\\n) == 0\n    global_load_lds_dwordx4 %[o0], %[qg]\n"
+      "  .elseif (\\n) == 1\n    global_load_lds_dwordx4 %[o1], %[qg]\n"
+      "  .elseif (\\n) == 2\n    global_load_lds_dwordx4 %[o2], %[qg]\n"
+      "  .elseif (\\n) == 3\n    global_load_lds_dwordx4 %[o3], %[qg]\n"
+      "  .elseif (\\n) == 4\n    global_load_lds_dwordx4 %[o0], %[og]\n"
+      "  .elseif (\\n) == 5\n    global_load_lds_dwordx4 %[o1], %[og]\n"
+      "  .elseif (\\n) == 6\n    global_load_lds_dwordx4 %[o2], %[og]\n"
+      "  .else\n    global_load_lds_dwordx4 %[o3], %[og]\n"
+      "  .endif\n"
+      "  s_mov_b64 exec, -1\n"
+      ".endm\n"
+      // after MFMA i of NS: loads [8 i / NS, 8 (i + 1) / NS) (at most one, NS >= 8)
+      ".macro KC_AT i\n"
+      "  .if ((((\\i) + 1) * 8) / %[ns]) > (((\\i) * 8) / %[ns])\n"
+      "    KC_LD (((\\i) * 8) / %[ns])\n"
+      "  .endif\n"
+      ".endm\n"
       "ds_read_b128 %[f0], %[a0]\n"
       "ds_read_b128 %[f1], %[a1]\n"
       "ds_read_b128 %[f2], %[a2]\n"
@@ -85,6 +124,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 0 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[0:3], 0\n"
+      "  KC_AT 0\n"
       "  .if 6 < %[ns]\n    ds_read_b128 %[f0], %[a6]\n  .endif\n"
       ".endif\n"
       ".if 1 < %[ns]\n"
@@ -95,6 +135,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 1 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[4:7], %[acc]\n"
+      "  KC_AT 1\n"
       "  .if 7 < %[ns]\n    ds_read_b128 %[f1], %[a7]\n  .endif\n"
       ".endif\n"
       ".if 2 < %[ns]\n"
@@ -105,6 +146,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 2 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[8:11], %[acc]\n"
+      "  KC_AT 2\n"
       "  .if 8 < %[ns]\n    ds_read_b128 %[f2], %[a0] offset:256\n  .endif\n"
       ".endif\n"
       ".if 3 < %[ns]\n"
@@ -115,6 +157,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 3 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[12:15], %[acc]\n"
+      "  KC_AT 3\n"
       "  .if 9 < %[ns]\n    ds_read_b128 %[f3], %[a1] offset:256\n  .endif\n"
       ".endif\n"
       ".if 4 < %[ns]\n"
@@ -125,6 +168,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 4 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f4], a[16:19], %[acc]\n"
+      "  KC_AT 4\n"
       "  .if 10 < %[ns]\n    ds_read_b128 %[f4], %[a2] offset:256\n  .endif\n"
       ".endif\n"
       ".if 5 < %[ns]\n"
@@ -135,6 +179,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 5 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f5], a[20:23], %[acc]\n"
+      "  KC_AT 5\n"
       "  .if 11 < %[ns]\n    ds_read_b128 %[f5], %[a3] offset:256\n  .endif\n"
       ".endif\n"
       ".if 6 < %[ns]\n"
@@ -145,6 +190,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 6 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[24:27], %[acc]\n"
+      "  KC_AT 6\n"
       "  .if 12 < %[ns]\n    ds_read_b128 %[f0], %[a4] offset:256\n  .endif\n"
       ".endif\n"
       ".if 7 < %[ns]\n"
@@ -155,6 +201,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 7 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[28:31], %[acc]\n"
+      "  KC_AT 7\n"
       "  .if 13 < %[ns]\n    ds_read_b128 %[f1], %[a5] offset:256\n  .endif\n"
       ".endif\n"
       ".if 8 < %[ns]\n"
@@ -165,6 +212,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 8 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[32:35], %[acc]\n"
+      "  KC_AT 8\n"
       "  .if 14 < %[ns]\n    ds_read_b128 %[f2], %[a6] offset:256\n  .endif\n"
       ".endif\n"
       ".if 9 < %[ns]\n"
@@ -175,6 +223,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 9 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[36:39], %[acc]\n"
+      "  KC_AT 9\n"
       "  .if 15 < %[ns]\n    ds_read_b128 %[f3], %[a7] offset:256\n  .endif\n"
       ".endif\n"
       ".if 10 < %[ns]\n"
@@ -185,6 +234,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 10 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f4], a[40:43], %[acc]\n"
+      "  KC_AT 10\n"
       ".endif\n"
       ".if 11 < %[ns]\n"
       "  .if 11 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
@@ -194,6 +244,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 11 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f5], a[44:47], %[acc]\n"
+      "  KC_AT 11\n"
       ".endif\n"
       ".if 12 < %[ns]\n"
       "  .if 12 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
@@ -203,6 +254,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 12 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[48:51], %[acc]\n"
+      "  KC_AT 12\n"
       ".endif\n"
       ".if 13 < %[ns]\n"
       "  .if 13 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
@@ -212,6 +264,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 13 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[52:55], %[acc]\n"
+      "  KC_AT 13\n"
       ".endif\n"
       ".if 14 < %[ns]\n"
       "  .if 14 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
@@ -221,6 +274,7 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 14 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[56:59], %[acc]\n"
+      "  KC_AT 14\n"
       ".endif\n"
       ".if 15 < %[ns]\n"
       "  .if 15 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
@@ -230,15 +284,19 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .elseif 15 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
       "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
       "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[60:63], %[acc]\n"
+      "  KC_AT 15\n"
       ".endif\n"
       "s_nop 7\n"
       "s_nop 7\n"
       "s_nop 7\n"  // the MFMA results may be read by vector instructions right after
+      ".purgem KC_LD\n"
+      ".purgem KC_AT\n"
       : [acc] "=&v"(acc), [f0] "=&v"(b[0]), [f1] "=&v"(b[1]), [f2] "=&v"(b[2]), [f3] "=&v"(b[3]), [f4] "=&v"(b[4]), [f5] "=&v"(b[5])
       : [a0] "v"(addr[0]), [a1] "v"(addr[1]), [a2] "v"(addr[2]), [a3] "v"(addr[3]), [a4] "v"(addr[4]),
         [a5] "v"(addr[5]), [a6] "v"(addr[6]), [a7] "v"(addr[7]), [ns] "i"(NS), "{a[0:15]}"(kv0), "{a[16:31]}"(kv1),
-        "{a[32:47]}"(kv2), "{a[48:63]}"(kv3)
-      : "memory");
+        "{a[32:47]}"(kv2), "{a[48:63]}"(kv3), [qg] "s"(cp.qg), [og] "s"(cp.og), [lq] "s"(cp.lq), [lo] "s"(cp.lo),
+        [cx] "s"(cp.exec), [o0] "v"(cp.off[0]), [o1] "v"(cp.off[1]), [o2] "v"(cp.off[2]), [o3] "v"(cp.off[3])
+      : "memory", "m0", "exec", "scc");
   return acc;
 }
 
@@ -507,7 +565,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   // whole tiles, rows clamped onto N-1 for a ragged last tile
   RowTileCopier<D, DP, C::kQTile, W> cp;
   cp.init(wave, lane);
-  auto load_qtile = [&](int t) {
+  auto load_rows = [&](int t) {  // Q and dO rows of tile t
     const int sl = t % 3, row0 = t * C::kQTile;
     if (row0 + C::kQTile <= N) {
       cp.copy_at(Q, (uint32_t)row0 * (D * 2), qbuf(sl));
@@ -516,6 +574,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       cp.copy_clamped(Q, N, row0, qbuf(sl));
       cp.copy_clamped(dO, N, row0, obuf(sl));
     }
+  };
+  auto load_stats = [&](int t) {  // L and delta of tile t (wave 0)
+    const int sl = t % 3;
     if (wave == 0) {
       int r = t * C::kQTile + lane;
       r = r < N ? r : N - 1;
@@ -523,7 +584,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       load_lds4(Dg + r, dbuf(sl));
     }
   };
-  load_qtile(t_begin);
+  load_rows(t_begin);
+  load_stats(t_begin);
 
   // this wave's half of dK^T and dV^T: d blocks dh*kHalfBlocks .. (those below kDBlocks)
   f32x16 dk[kHalfBlocks], dv[kHalfBlocks];
@@ -575,7 +637,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     // publishes tile t (loaded last step) and the exchange of tile t-1
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < n_qtiles) load_qtile(t + 1);  // into the slot of tile t-2, finished last step
+    // tile t+1 into the slot of tile t-2, finished last step: its Q and dO
+    // rows from inside this wave's part-1 chain (a whole tile and a chain to
+    // run), else here
+    const bool part1 = t < n_qtiles && tile_work(t);
+    KvCopy kc = {0, 0, 0, 0, 0, {cp.off[0], cp.off[1], cp.off[2], cp.off[3]}};
+    if (t + 1 < n_qtiles) {
+      const int sl1 = (t + 1) % 3, row1 = (t + 1) * C::kQTile;
+      if (part1 && row1 + C::kQTile <= N) {
+        kc.qg = (uint64_t)(uintptr_t)(Q + (size_t)row1 * D);
+        kc.og = (uint64_t)(uintptr_t)(dO + (size_t)row1 * D);
+        kc.lq = (uint32_t)(uintptr_t)qbuf(sl1) + cp.lds_wave;
+        kc.lo = (uint32_t)(uintptr_t)obuf(sl1) + cp.lds_wave;
+        kc.exec = ~0ull;
+      } else {
+        load_rows(t + 1);
+      }
+      load_stats(t + 1);
+    }
 
     // 1. tile t: S = Q_t K^T (dh = 0) or dP = dO_t V^T (dh = 1), to the exchange
     if (t < n_qtiles && tile_work(t)) {
@@ -596,7 +675,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
           for (int i = 0; i < 4; ++i) lq[g * 4 + i] = l4[i];
         }
       }
-      f32x16 mine = kv_chain<kDSteps>(addr, kvg[0], kvg[1], kvg[2], kvg[3]);
+      f32x16 mine = kv_chain<kDSteps>(addr, kvg[0], kvg[1], kvg[2], kvg[3], kc);
       if (dh == 0) {  // P = exp(S - L), masked; queries of register r: (r/4)*8 + half*4 + r%4
         const bool masked = (CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N);
         // two instances: tiles that need no mask carry no selects

@@ -69,7 +69,9 @@ struct DqCfg {
 // copy (16 global-to-LDS loads of 1 KB), spread between its MFMAs: issued
 // in one burst the loads stalled the wave for about a thousand cycles per
 // tile while the vector memory path drained them, with the matrix core
-// idle.
+// idle.  The full step issues them one per MFMA from its first, which
+// leaves them most of the step to land before the next step's wait (spread
+// over the whole step they left a wait of about 300 cycles).
 // Per element the in-block dS is the plain loop's arithmetic, instruction
 // for instruction: x = fma(S, c, -L), p = exp2(x), (dP - delta) p, pairs
 // packed to bf16.
@@ -278,8 +280,8 @@ struct DqCfg {
   "L_full_%=:\n"                                                                                                   \
   "FQ_RD 0, 2 * %[ns], 1\nFQ_RD 1, 2 * %[ns], 1\nFQ_RD 2, 2 * %[ns], 1\nFQ_RD 3, 2 * %[ns], 1\nFQ_RD 4, 2 * %[ns], 1\n"      \
   "FQ_RD 5, 2 * %[ns], 1\nFQ_RD 6, 2 * %[ns], 1\nFQ_RD 7, 2 * %[ns], 1\nFQ_RD 8, 2 * %[ns], 1\nFQ_RD 9, 2 * %[ns], 1\n"      \
-  "FQ_SMS (2 * %[ns]), 1, 1, 3\n"                                                                                  \
-  "FQ_DMS v[206:209], v[210:213], (2 * %[ns]), 3\n"                                                                \
+  "FQ_SMS (2 * %[ns]), 1, 1, 1\n"                                                                                  \
+  "FQ_DMS v[206:209], v[210:213], (2 * %[ns]), 1\n"                                                                \
   "s_branch L_end_%=\n"                                                                                            \
   "L_first_%=:\n"                                                                                                  \
   "FQ_RD 0, 2 * %[ns], 0\nFQ_RD 1, 2 * %[ns], 0\nFQ_RD 2, 2 * %[ns], 0\nFQ_RD 3, 2 * %[ns], 0\nFQ_RD 4, 2 * %[ns], 0\n"      \

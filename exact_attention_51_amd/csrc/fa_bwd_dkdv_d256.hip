@@ -67,8 +67,8 @@ struct KvDsplitCfg {
 //
 // The chain also issues this wave's share of the next query tile's copy
 // (cp: 4 loads of Q rows, then 4 of dO rows, from the tiles' global bases
-// qg, og to LDS lq, lo + 1024 i at the copier's lane offsets), spread
-// between its MFMAs; exec = 0 leaves them out.  Issued in one burst after
+// qg, og to LDS lq, lo + 1024 i at the copier's lane offsets), one after
+// each of its first 8 MFMAs; exec = 0 leaves them out.  Issued in one burst after
 // the step's barrier, the 8 loads of 1 KB stalled the wave for about 500
 // cycles while the vector memory path drained them.
 struct KvCopy {
@@ -104,10 +104,11 @@ __device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& k
       "  .endif\n"
       "  s_mov_b64 exec, -1\n"
       ".endm\n"
-      // after MFMA i of NS: loads [8 i / NS, 8 (i + 1) / NS) (at most one, NS >= 8)
+      // after MFMA i: load i of the 8 (the earliest issue leaves them the
+      // most time to land before the next step's wait)
       ".macro KC_AT i\n"
-      "  .if ((((\\i) + 1) * 8) / %[ns]) > (((\\i) * 8) / %[ns])\n"
-      "    KC_LD (((\\i) * 8) / %[ns])\n"
+      "  .if (\\i) < 8\n"
+      "    KC_LD (\\i)\n"
       "  .endif\n"
       ".endm\n"
       "ds_read_b128 %[f0], %[a0]\n"

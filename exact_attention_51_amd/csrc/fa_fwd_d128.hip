@@ -926,7 +926,7 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
 int launch_fwd_d128(const FwdArgs& a, hipStream_t stream) {
   if (a.D != 128 || a.N < d128::kBlockN) return -2;
   const int n_qtiles = (a.N + d128::kRows - 1) / d128::kRows;
-  const TileSched sched = make_sched(n_qtiles, a.B * a.H, a.causal != 0);
+  TileSched sched = make_sched(n_qtiles, a.B * a.H, a.causal != 0);
   const long n_blocks = (long)n_qtiles * a.B * a.H;
   long grid = n_blocks;
   int cont = 0;
@@ -934,6 +934,7 @@ int launch_fwd_d128(const FwdArgs& a, hipStream_t stream) {
   if (a.N >= 4 * d128::kBlockN && cus >= 8 && n_blocks > cus) {
     grid = cus & ~7;
     cont = 1;
+    sched.head_major = 1;
   }
   if (a.causal)
     hipLaunchKernelGGL(d128::fwd_d128_kernel<true>, dim3((unsigned)grid), dim3(64 * d128::kWaves), 0, stream, a, sched,

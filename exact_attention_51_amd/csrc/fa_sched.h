@@ -20,6 +20,7 @@ struct TileSched {
   int bh;             // B * H
   int heads_per_xcd;  // B*H / 8 when B*H % 8 == 0, else 0 (no XCD grouping)
   int heavy_first;    // 1: tile order n_qtiles-1 .. 0 (causal)
+  int head_major;     // with XCD grouping: an XCD's items run head by head (else rank by rank across its heads)
 };
 
 __host__ inline TileSched make_sched(int n_qtiles, int bh, bool causal) {
@@ -28,6 +29,7 @@ __host__ inline TileSched make_sched(int n_qtiles, int bh, bool causal) {
   s.bh = bh;
   s.heads_per_xcd = (bh % 8 == 0) ? bh / 8 : 0;
   s.heavy_first = causal ? 1 : 0;
+  s.head_major = 0;
   return s;
 }
 
@@ -35,8 +37,13 @@ __device__ __forceinline__ void sched_item(const TileSched& s, int hw, int& qtil
   int rank;
   if (s.heads_per_xcd > 0) {
     const int xcd = hw & 7, slot = hw >> 3;
-    rank = slot / s.heads_per_xcd;
-    bh = xcd * s.heads_per_xcd + slot % s.heads_per_xcd;
+    if (s.head_major) {
+      rank = slot % s.n_qtiles;
+      bh = xcd * s.heads_per_xcd + slot / s.n_qtiles;
+    } else {
+      rank = slot / s.heads_per_xcd;
+      bh = xcd * s.heads_per_xcd + slot % s.heads_per_xcd;
+    }
   } else {
     rank = hw / s.bh;
     bh = hw % s.bh;

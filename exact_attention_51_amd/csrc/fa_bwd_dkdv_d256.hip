@@ -57,20 +57,12 @@ struct KvDsplitCfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 };
 
-// S = A K^T over d as one accumulator chain of NS (6 <= NS <= 16) MFMAs,
-// the A fragments read from LDS 6 ahead of their MFMA (one buffer each).
-// The B operands (this wave's K or V rows) are held in a[0:63], fragment ds
-// in a[4ds : 4ds+3].  addr[ds] is the lane's LDS byte address of fragment
-// ds < 8; fragment ds >= 8 lies 256 bytes further (the swizzle permutes
-// chunks within each 16-chunk half of a 512-byte row).  Compiler-scheduled,
-// at 256 VGPRs this chain read one fragment at a time and waited for it.
-//
-// The chain also issues this wave's share of the next query tile's copy
-// (cp: 4 loads of Q rows, then 4 of dO rows, from the tiles' global bases
-// qg, og to LDS lq, lo + 1024 i at the copier's lane offsets), one after
-// each of its first 8 MFMAs; exec = 0 leaves them out.  Issued in one burst after
-// the step's barrier, the 8 loads of 1 KB stalled the wave for about 500
-// cycles while the vector memory path drained them.
+// The next query tile's copy, issued from inside the step (one load after
+// each of its first 8 MFMAs): 4 loads of Q rows, then 4 of dO rows, from the
+// tiles' global bases qg, og to LDS lq, lo + 1024 i at the copier's lane
+// offsets; exec = 0 leaves them out.  Issued in one burst after the step's
+// barrier, the 8 loads of 1 KB stalled the wave for about 500 cycles while
+// the vector memory path drained them.
 struct KvCopy {
   uint64_t qg, og;
   uint32_t lq, lo;
@@ -78,445 +70,322 @@ struct KvCopy {
   uint32_t off[4];
 };
 
-template <int NS>
-__device__ __forceinline__ f32x16 kv_chain(const int (&addr)[8], const f32x16& kv0, const f32x16& kv1,
-                                           const f32x16& kv2, const f32x16& kv3, const KvCopy& cp) {
-  static_assert(NS >= 8 && NS <= 16, "chain length");
-  f32x16 acc;
-  f32x4 b[6];  // fragment buffers: fragment ds in buffer ds mod 6
-  asm volatile(
-      // copy load n: Q rows (n < 4) or dO rows, load n mod 4 of the wave's share
-      ".macro KC_LD n\n"
-      "  .if ((\\n) >> 2) == 0\n"
-      "    s_add_u32 m0, %[lq], ((\\n) & 3) * 1024\n"
-      "  .else\n"
-      "    s_add_u32 m0, %[lo], ((\\n) & 3) * 1024\n"
-      "  .endif\n"
-      "  s_mov_b64 exec, %[cx]\n"
-      "  .if (\\n) == 0\n    global_load_lds_dwordx4 %[o0], %[qg]\n"
-      "  .elseif (\\n) == 1\n    global_load_lds_dwordx4 %[o1], %[qg]\n"
-      "  .elseif (\\n) == 2\n    global_load_lds_dwordx4 %[o2], %[qg]\n"
-      "  .elseif (\\n) == 3\n    global_load_lds_dwordx4 %[o3], %[qg]\n"
-      "  .elseif (\\n) == 4\n    global_load_lds_dwordx4 %[o0], %[og]\n"
-      "  .elseif (\\n) == 5\n    global_load_lds_dwordx4 %[o1], %[og]\n"
-      "  .elseif (\\n) == 6\n    global_load_lds_dwordx4 %[o2], %[og]\n"
-      "  .else\n    global_load_lds_dwordx4 %[o3], %[og]\n"
-      "  .endif\n"
-      "  s_mov_b64 exec, -1\n"
-      ".endm\n"
-      // after MFMA i: load i of the 8 (the earliest issue leaves them the
-      // most time to land before the next step's wait)
-      ".macro KC_AT i\n"
-      "  .if (\\i) < 8\n"
-      "    KC_LD (\\i)\n"
-      "  .endif\n"
-      ".endm\n"
-      "ds_read_b128 %[f0], %[a0]\n"
-      "ds_read_b128 %[f1], %[a1]\n"
-      "ds_read_b128 %[f2], %[a2]\n"
-      "ds_read_b128 %[f3], %[a3]\n"
-      "ds_read_b128 %[f4], %[a4]\n"
-      "ds_read_b128 %[f5], %[a5]\n"
-      ".if 0 < %[ns]\n"
-      "  .if 0 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 0 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 0 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 0 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 0 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[0:3], 0\n"
-      "  KC_AT 0\n"
-      "  .if 6 < %[ns]\n    ds_read_b128 %[f0], %[a6]\n  .endif\n"
-      ".endif\n"
-      ".if 1 < %[ns]\n"
-      "  .if 1 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 1 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 1 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 1 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 1 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[4:7], %[acc]\n"
-      "  KC_AT 1\n"
-      "  .if 7 < %[ns]\n    ds_read_b128 %[f1], %[a7]\n  .endif\n"
-      ".endif\n"
-      ".if 2 < %[ns]\n"
-      "  .if 2 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 2 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 2 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 2 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 2 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[8:11], %[acc]\n"
-      "  KC_AT 2\n"
-      "  .if 8 < %[ns]\n    ds_read_b128 %[f2], %[a0] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 3 < %[ns]\n"
-      "  .if 3 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 3 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 3 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 3 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 3 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[12:15], %[acc]\n"
-      "  KC_AT 3\n"
-      "  .if 9 < %[ns]\n    ds_read_b128 %[f3], %[a1] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 4 < %[ns]\n"
-      "  .if 4 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 4 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 4 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 4 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 4 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f4], a[16:19], %[acc]\n"
-      "  KC_AT 4\n"
-      "  .if 10 < %[ns]\n    ds_read_b128 %[f4], %[a2] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 5 < %[ns]\n"
-      "  .if 5 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 5 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 5 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 5 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 5 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f5], a[20:23], %[acc]\n"
-      "  KC_AT 5\n"
-      "  .if 11 < %[ns]\n    ds_read_b128 %[f5], %[a3] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 6 < %[ns]\n"
-      "  .if 6 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 6 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 6 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 6 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 6 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[24:27], %[acc]\n"
-      "  KC_AT 6\n"
-      "  .if 12 < %[ns]\n    ds_read_b128 %[f0], %[a4] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 7 < %[ns]\n"
-      "  .if 7 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 7 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 7 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 7 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 7 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[28:31], %[acc]\n"
-      "  KC_AT 7\n"
-      "  .if 13 < %[ns]\n    ds_read_b128 %[f1], %[a5] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 8 < %[ns]\n"
-      "  .if 8 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 8 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 8 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 8 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 8 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[32:35], %[acc]\n"
-      "  KC_AT 8\n"
-      "  .if 14 < %[ns]\n    ds_read_b128 %[f2], %[a6] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 9 < %[ns]\n"
-      "  .if 9 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 9 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 9 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 9 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 9 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[36:39], %[acc]\n"
-      "  KC_AT 9\n"
-      "  .if 15 < %[ns]\n    ds_read_b128 %[f3], %[a7] offset:256\n  .endif\n"
-      ".endif\n"
-      ".if 10 < %[ns]\n"
-      "  .if 10 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 10 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 10 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 10 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 10 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f4], a[40:43], %[acc]\n"
-      "  KC_AT 10\n"
-      ".endif\n"
-      ".if 11 < %[ns]\n"
-      "  .if 11 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 11 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 11 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 11 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 11 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f5], a[44:47], %[acc]\n"
-      "  KC_AT 11\n"
-      ".endif\n"
-      ".if 12 < %[ns]\n"
-      "  .if 12 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 12 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 12 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 12 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 12 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f0], a[48:51], %[acc]\n"
-      "  KC_AT 12\n"
-      ".endif\n"
-      ".if 13 < %[ns]\n"
-      "  .if 13 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 13 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 13 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 13 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 13 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f1], a[52:55], %[acc]\n"
-      "  KC_AT 13\n"
-      ".endif\n"
-      ".if 14 < %[ns]\n"
-      "  .if 14 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 14 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 14 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 14 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 14 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f2], a[56:59], %[acc]\n"
-      "  KC_AT 14\n"
-      ".endif\n"
-      ".if 15 < %[ns]\n"
-      "  .if 15 + 5 < %[ns]\n    s_waitcnt lgkmcnt(5)\n"
-      "  .elseif 15 + 4 < %[ns]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 15 + 3 < %[ns]\n    s_waitcnt lgkmcnt(3)\n"
-      "  .elseif 15 + 2 < %[ns]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .elseif 15 + 1 < %[ns]\n    s_waitcnt lgkmcnt(1)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[acc], %[f3], a[60:63], %[acc]\n"
-      "  KC_AT 15\n"
-      ".endif\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 7\n"  // the MFMA results may be read by vector instructions right after
-      ".purgem KC_LD\n"
-      ".purgem KC_AT\n"
-      : [acc] "=&v"(acc), [f0] "=&v"(b[0]), [f1] "=&v"(b[1]), [f2] "=&v"(b[2]), [f3] "=&v"(b[3]), [f4] "=&v"(b[4]), [f5] "=&v"(b[5])
-      : [a0] "v"(addr[0]), [a1] "v"(addr[1]), [a2] "v"(addr[2]), [a3] "v"(addr[3]), [a4] "v"(addr[4]),
-        [a5] "v"(addr[5]), [a6] "v"(addr[6]), [a7] "v"(addr[7]), [ns] "i"(NS), "{a[0:15]}"(kv0), "{a[16:31]}"(kv1),
-        "{a[32:47]}"(kv2), "{a[48:63]}"(kv3), [qg] "s"(cp.qg), [og] "s"(cp.og), [lq] "s"(cp.lq), [lo] "s"(cp.lo),
-        [cx] "s"(cp.exec), [o0] "v"(cp.off[0]), [o1] "v"(cp.off[1]), [o2] "v"(cp.off[2]), [o3] "v"(cp.off[3])
-      : "memory", "m0", "exec", "scc");
-  return acc;
-}
+// ------------------------------------------------ one pipelined query-tile step
+//
+// One asm block per query tile t runs the NS S (or dP) MFMAs of tile t with,
+// in their shadow, dS of tile t-1 (from the exchange the partner wave
+// published last step), then the 4 NB dV/dK MFMAs of tile t-1 with, in
+// their shadow, the exponentials of tile t; P (or dP) of tile t goes to the
+// exchange at the end.  The LDS reads run six fragments ahead of their MFMA
+// across both chains, and the next tile's copy goes out between the first
+// eight MFMAs.  Issued between the chains instead, the vector work took as
+// long as the chains themselves: one wave per SIMD issues a vector
+// instruction only every ~9 cycles.  Per element the arithmetic is the
+// plain loop's, instruction for instruction: dS = float(P) (dP - delta),
+// P = exp2(fma(S, c, -L log2 e)), pairs packed to bf16 with round to
+// nearest even.
+//
+// mode (wave-uniform): bit 0 tile t is this wave's (S or dP chain), bit 1
+// tile t-1 is (dS and the dV/dK chain), bit 2 the exponentials (or dP's
+// store) go in the block too -- left out for a masked tile, which the
+// caller finishes from the returned S.
+//
+// Registers: K or V rows in a[0:63] (fragment ds at a[4 ds : 4 ds + 3]); dV
+// block i in a[64 + 16 i : +15], dK block i in a[128 + 16 i : +15]; S or dP
+// of tile t in v[152:167]; L of tile t in v[168:183], whose first 8
+// registers then take tile t's packed P; tile t-1's packed P in v[184:191],
+// its dP in v[192:207], delta in v[208:223], packed dS in v[224:231]; six
+// fragment buffers in v[232:255]; temporaries v148, v149.
+// Addresses: r[ds] the lane's row fragment ds (< 8) in tile t's Q or dO
+// slot, fragment ds + 8 256 bytes further; ta[i], tb[i] the two transposed
+// reads of local d block i in tile t-1's Q slot (queries 16..31 8192 bytes
+// further, the dO slot 16384); xpr, xpw the lane's exchange entries of
+// tiles t-1 and t (P at +0 and +1024, dP at +2048 + 1024 g); dlr delta of
+// tile t-1, llr L of tile t (four runs 32 bytes apart).
+#define KS_DSCHK(N) "  .if (" #N " >= (\\lo)) && (" #N " < (\\hi))\n    KS_DS1 " #N "\n  .endif\n"
+#define KS_EXCHK(N) "  .if (" #N " >= (\\lo)) && (" #N " < (\\hi))\n    KS_EX1 " #N "\n  .endif\n"
+#define KS_SMC(N) "  KS_SM " #N ", \\nsx, \\kv, \\ds, \\lr\n"
+#define KS_KMC(N) "  KS_KM " #N ", \\nsx, \\ex\n"
+#define KS_LGK(N) "  .elseif (\\n) == " #N "\n    s_waitcnt lgkmcnt(" #N ")\n"
+#define KV_STEP_TEXT                                                                                               \
+  ".macro KS_WAIT n\n"                                                                                             \
+  "  .if (\\n) <= 0\n    s_waitcnt lgkmcnt(0)\n"                                                                   \
+  KS_LGK(1) KS_LGK(2) KS_LGK(3) KS_LGK(4) KS_LGK(5) KS_LGK(6) KS_LGK(7) KS_LGK(8) KS_LGK(9) KS_LGK(10) KS_LGK(11)   \
+  KS_LGK(12) KS_LGK(13) KS_LGK(14)                                                                                 \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* copy load n: Q rows (n < 4) or dO rows, load n mod 4 of the wave's share */                                  \
+  ".macro KC_LD n\n"                                                                                               \
+  "  .if ((\\n) >> 2) == 0\n    s_add_u32 m0, %[lq], ((\\n) & 3) * 1024\n"                                        \
+  "  .else\n    s_add_u32 m0, %[lo], ((\\n) & 3) * 1024\n  .endif\n"                                              \
+  "  s_mov_b64 exec, %[cx]\n"                                                                                      \
+  "  .if (\\n) == 0\n    global_load_lds_dwordx4 %[o0], %[qg]\n"                                                   \
+  "  .elseif (\\n) == 1\n    global_load_lds_dwordx4 %[o1], %[qg]\n"                                               \
+  "  .elseif (\\n) == 2\n    global_load_lds_dwordx4 %[o2], %[qg]\n"                                               \
+  "  .elseif (\\n) == 3\n    global_load_lds_dwordx4 %[o3], %[qg]\n"                                               \
+  "  .elseif (\\n) == 4\n    global_load_lds_dwordx4 %[o0], %[og]\n"                                               \
+  "  .elseif (\\n) == 5\n    global_load_lds_dwordx4 %[o1], %[og]\n"                                               \
+  "  .elseif (\\n) == 6\n    global_load_lds_dwordx4 %[o2], %[og]\n"                                               \
+  "  .else\n    global_load_lds_dwordx4 %[o3], %[og]\n  .endif\n"                                                 \
+  "  s_mov_b64 exec, -1\n"                                                                                         \
+  ".endm\n"                                                                                                        \
+  /* tile t-1's P, dP and delta (10 reads) */                                                                     \
+  ".macro KS_XR\n"                                                                                                 \
+  "  ds_read_b128 v[184:187], %[xpr]\n  ds_read_b128 v[188:191], %[xpr] offset:1024\n"                             \
+  "  ds_read_b128 v[192:195], %[xpr] offset:2048\n  ds_read_b128 v[196:199], %[xpr] offset:3072\n"                 \
+  "  ds_read_b128 v[200:203], %[xpr] offset:4096\n  ds_read_b128 v[204:207], %[xpr] offset:5120\n"                 \
+  "  ds_read_b128 v[208:211], %[dlr]\n  ds_read_b128 v[212:215], %[dlr] offset:32\n"                               \
+  "  ds_read_b128 v[216:219], %[dlr] offset:64\n  ds_read_b128 v[220:223], %[dlr] offset:96\n"                     \
+  ".endm\n"                                                                                                        \
+  /* tile t's L (4 reads, S wave) */                                                                              \
+  ".macro KS_LR\n"                                                                                                 \
+  "  .if %[dh] == 0\n"                                                                                             \
+  "    ds_read_b128 v[168:171], %[llr]\n    ds_read_b128 v[172:175], %[llr] offset:32\n"                           \
+  "    ds_read_b128 v[176:179], %[llr] offset:64\n    ds_read_b128 v[180:183], %[llr] offset:96\n"                 \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* S/dP fragment p (one read) into buffer p mod 6 */                                                            \
+  ".macro KS_RX p\n"                                                                                               \
+  "  .if ((\\p) & 7) == 0\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r0] "          \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .elseif ((\\p) & 7) == 1\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r1] "      \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .elseif ((\\p) & 7) == 2\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r2] "      \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .elseif ((\\p) & 7) == 3\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r3] "      \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .elseif ((\\p) & 7) == 4\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r4] "      \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .elseif ((\\p) & 7) == 5\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r5] "      \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .elseif ((\\p) & 7) == 6\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r6] "      \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .else\n    ds_read_b128 v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], %[r7] "                         \
+  "offset:(((\\p) >> 3) * 256)\n"                                                                                  \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* dV/dK fragment (query chunk cc, local d block i, dv: dO^T, else Q^T) into buffer p mod 6 (two reads) */      \
+  ".macro KS_TR2 ra, rb, off, p\n"                                                                                 \
+  "  ds_read_b64_tr_b16 v[232 + ((\\p) %% 6) * 4 : 233 + ((\\p) %% 6) * 4], \\ra offset:(\\off)\n"               \
+  "  ds_read_b64_tr_b16 v[234 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], \\rb offset:(\\off)\n"               \
+  ".endm\n"                                                                                                        \
+  ".macro KS_TX cc, i, dv, p\n"                                                                                    \
+  "  .if (\\i) == 0\n    KS_TR2 %[ta0], %[tb0], ((\\cc) * 8192 + (\\dv) * 16384), (\\p)\n"                         \
+  "  .elseif (\\i) == 1\n    KS_TR2 %[ta1], %[tb1], ((\\cc) * 8192 + (\\dv) * 16384), (\\p)\n"                     \
+  "  .elseif (\\i) == 2\n    KS_TR2 %[ta2], %[tb2], ((\\cc) * 8192 + (\\dv) * 16384), (\\p)\n"                     \
+  "  .else\n    KS_TR2 %[ta3], %[tb3], ((\\cc) * 8192 + (\\dv) * 16384), (\\p)\n  .endif\n"                       \
+  ".endm\n"                                                                                                        \
+  /* stream position p: S/dP fragments, then with kv the dV/dK fragments (cc outer, block, dV before dK) */       \
+  ".macro KS_RD p, nsx, kv\n"                                                                                      \
+  "  .if (\\p) < (\\nsx)\n"                                                                                        \
+  "    KS_RX (\\p)\n"                                                                                              \
+  "  .elseif (\\kv) && ((\\p) < (\\nsx) + 4 * %[nb])\n"                                                            \
+  "    KS_TX ((((\\p) - (\\nsx))) / (2 * %[nb])), (((((\\p) - (\\nsx))) %% (2 * %[nb])) >> 1), "                   \
+  "(1 - (((\\p) - (\\nsx)) & 1)), (\\p)\n"                                                                         \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  ".macro KS_RD6 nsx, kv\n"                                                                                        \
+  "  KS_RD 0, \\nsx, \\kv\n  KS_RD 1, \\nsx, \\kv\n  KS_RD 2, \\nsx, \\kv\n"                                      \
+  "  KS_RD 3, \\nsx, \\kv\n  KS_RD 4, \\nsx, \\kv\n  KS_RD 5, \\nsx, \\kv\n"                                      \
+  ".endm\n"                                                                                                        \
+  /* wait until at most the reads of stream positions a..b-1 (one each before nsx, two after) plus x remain */   \
+  ".macro KS_WT2 a, b, nsx, x\n"                                                                                   \
+  "  .if (\\b) <= (\\nsx)\n    KS_WAIT ((\\b) - (\\a) + (\\x))\n"                                                  \
+  "  .elseif (\\a) >= (\\nsx)\n    KS_WAIT (2 * ((\\b) - (\\a)) + (\\x))\n"                                        \
+  "  .else\n    KS_WAIT (((\\nsx) - (\\a)) + 2 * ((\\b) - (\\nsx)) + (\\x))\n  .endif\n"                           \
+  ".endm\n"                                                                                                        \
+  /* before the MFMA of position m: its fragment landed (positions m+1..m+5 may be in flight, and the x */        \
+  /* L reads issued after position 5 while m < 6) */                                                              \
+  ".macro KS_WT3 m, nsx, kv, x\n"                                                                                  \
+  "  .if (\\m) + 6 <= (\\nsx) + 4 * %[nb] * (\\kv)\n    KS_WT2 ((\\m) + 1), ((\\m) + 6), (\\nsx), (\\x)\n"      \
+  "  .else\n    KS_WT2 ((\\m) + 1), ((\\nsx) + 4 * %[nb] * (\\kv)), (\\nsx), (\\x)\n  .endif\n"                   \
+  ".endm\n"                                                                                                        \
+  ".macro KS_WT m, nsx, kv, lr\n"                                                                                  \
+  "  .if (\\m) < 6\n    KS_WT3 (\\m), (\\nsx), (\\kv), (\\lr)\n"                                                   \
+  "  .else\n    KS_WT3 (\\m), (\\nsx), (\\kv), 0\n  .endif\n"                                                      \
+  ".endm\n"                                                                                                        \
+  /* dS half-step h of pair k = h/2 (elements 2k, 2k+1; P word k): unpack and dP - delta, then product and pack */ \
+  ".macro KS_DS1 h\n"                                                                                              \
+  "  .if ((\\h) & 1) == 0\n"                                                                                       \
+  "    v_lshlrev_b32 v148, 16, v[184 + ((\\h) >> 1)]\n"                                                            \
+  "    v_and_b32 v149, 0xffff0000, v[184 + ((\\h) >> 1)]\n"                                                        \
+  "    v_sub_f32 v[192 + (\\h)], v[192 + (\\h)], v[208 + (\\h)]\n"                                                 \
+  "    v_sub_f32 v[193 + (\\h)], v[193 + (\\h)], v[209 + (\\h)]\n"                                                 \
+  "  .else\n"                                                                                                      \
+  "    v_mul_f32 v148, v148, v[191 + (\\h)]\n"                                                                     \
+  "    v_mul_f32 v149, v149, v[192 + (\\h)]\n"                                                                     \
+  "    v_cvt_pk_bf16_f32 v[224 + ((\\h) >> 1)], v148, v149\n"                                                      \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  ".macro KS_DSR lo, hi\n"                                                                                         \
+  KS_DSCHK(0) KS_DSCHK(1) KS_DSCHK(2) KS_DSCHK(3) KS_DSCHK(4) KS_DSCHK(5) KS_DSCHK(6) KS_DSCHK(7)                  \
+  KS_DSCHK(8) KS_DSCHK(9) KS_DSCHK(10) KS_DSCHK(11) KS_DSCHK(12) KS_DSCHK(13) KS_DSCHK(14) KS_DSCHK(15)            \
+  ".endm\n"                                                                                                        \
+  /* exponential slot s (S wave): element s's exponent, element s-1's exp2, pair (s-3)/2's pack -- an */        \
+  /* exp2 result is read no sooner than one slot later */                                                         \
+  ".macro KS_EX1 s\n"                                                                                              \
+  "  .if %[dh] == 0\n"                                                                                             \
+  "    .if (\\s) < 16\n"                                                                                           \
+  "      v_mul_f32 v[168 + (\\s)], 0xbfb8aa3b, v[168 + (\\s)]\n"                                                   \
+  "      v_fma_f32 v[152 + (\\s)], v[152 + (\\s)], %[c], v[168 + (\\s)]\n"                                         \
+  "    .endif\n"                                                                                                   \
+  "    .if ((\\s) >= 1) && ((\\s) <= 16)\n"                                                                        \
+  "      v_exp_f32 v[151 + (\\s)], v[151 + (\\s)]\n"                                                               \
+  "    .endif\n"                                                                                                   \
+  "    .if (\\s) == 17\n      s_nop 0\n    .endif\n" /* exp2 result read by the next instruction */                     \
+  "    .if ((\\s) >= 3) && (((\\s) & 1) == 1)\n"                                                                   \
+  "      v_cvt_pk_bf16_f32 v[168 + ((\\s) - 3) / 2], v[149 + (\\s)], v[150 + (\\s)]\n"                             \
+  "    .endif\n"                                                                                                   \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  ".macro KS_EXR lo, hi\n"                                                                                         \
+  KS_EXCHK(0) KS_EXCHK(1) KS_EXCHK(2) KS_EXCHK(3) KS_EXCHK(4) KS_EXCHK(5) KS_EXCHK(6) KS_EXCHK(7)                  \
+  KS_EXCHK(8) KS_EXCHK(9) KS_EXCHK(10) KS_EXCHK(11) KS_EXCHK(12) KS_EXCHK(13) KS_EXCHK(14) KS_EXCHK(15)            \
+  KS_EXCHK(16) KS_EXCHK(17)                                                                                        \
+  ".endm\n"                                                                                                        \
+  /* tile t's P (S wave) or dP (dP wave) to the exchange */                                                       \
+  ".macro KS_ST\n"                                                                                                 \
+  "  s_nop 1\n"                                                                                                    \
+  "  .if %[dh] == 0\n"                                                                                             \
+  "    ds_write_b128 %[xpw], v[168:171]\n    ds_write_b128 %[xpw], v[172:175] offset:1024\n"                       \
+  "  .else\n"                                                                                                      \
+  "    ds_write_b128 %[xpw], v[152:155] offset:2048\n    ds_write_b128 %[xpw], v[156:159] offset:3072\n"           \
+  "    ds_write_b128 %[xpw], v[160:163] offset:4096\n    ds_write_b128 %[xpw], v[164:167] offset:5120\n"           \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* S/dP MFMA m, the read of position m+6, copy load m (m < 8), and with ds its share of dS */                  \
+  ".macro KS_SM m, nsx, kv, ds, lr\n"                                                                              \
+  "  .if (\\m) < (\\nsx)\n"                                                                                        \
+  "    KS_WT (\\m), (\\nsx), (\\kv), (\\lr)\n"                                                                     \
+  "    .if (\\m) == 0\n"                                                                                           \
+  "      v_mfma_f32_32x32x16_bf16 v[152:167], v[232 + ((\\m) %% 6) * 4 : 235 + ((\\m) %% 6) * 4], "                \
+  "a[(\\m) * 4 : (\\m) * 4 + 3], 0\n"                                                                             \
+  "    .else\n"                                                                                                    \
+  "      v_mfma_f32_32x32x16_bf16 v[152:167], v[232 + ((\\m) %% 6) * 4 : 235 + ((\\m) %% 6) * 4], "                \
+  "a[(\\m) * 4 : (\\m) * 4 + 3], v[152:167]\n"                                                                     \
+  "    .endif\n"                                                                                                   \
+  "    KS_RD ((\\m) + 6), (\\nsx), (\\kv)\n"                                                                       \
+  "    .if (\\m) < 8\n      KC_LD (\\m)\n    .endif\n"                                                           \
+  "    .if (\\ds)\n      KS_DSR (((\\m) * 16) / (\\nsx)), ((((\\m) + 1) * 16) / (\\nsx))\n    .endif\n"            \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* dV/dK MFMA of fragment f (position nsx + f), the read 6 ahead, and with ex its exponential slots */         \
+  /* one dV/dK MFMA: acc += fragment buffer (p mod 6) x B (4 registers from vb) */                               \
+  ".macro KS_MF acc, p, vb\n"                                                                                       \
+  "  v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], v[\\vb : (\\vb) + 3], \\acc\n" \
+  ".endm\n"                                                                                                        \
+  ".macro KS_KM2 cc, i, dv, p\n"                                                                                   \
+  "  .if (\\dv) && ((\\i) == 0)\n    KS_MF %[dv0], (\\p), (184 + 4 * (\\cc))\n"                                       \
+  "  .elseif (\\dv) && ((\\i) == 1)\n    KS_MF %[dv1], (\\p), (184 + 4 * (\\cc))\n"                                   \
+  "  .elseif (\\dv) && ((\\i) == 2)\n    KS_MF %[dv2], (\\p), (184 + 4 * (\\cc))\n"                                   \
+  "  .elseif (\\dv)\n    KS_MF %[dv3], (\\p), (184 + 4 * (\\cc))\n"                                                    \
+  "  .elseif (\\i) == 0\n    KS_MF %[dk0], (\\p), (224 + 4 * (\\cc))\n"                                                 \
+  "  .elseif (\\i) == 1\n    KS_MF %[dk1], (\\p), (224 + 4 * (\\cc))\n"                                                 \
+  "  .elseif (\\i) == 2\n    KS_MF %[dk2], (\\p), (224 + 4 * (\\cc))\n"                                                 \
+  "  .else\n    KS_MF %[dk3], (\\p), (224 + 4 * (\\cc))\n  .endif\n"                                                   \
+  ".endm\n"                                                                                                        \
+  ".macro KS_KM f, nsx, ex\n"                                                                                      \
+  "  .if (\\f) < 4 * %[nb]\n"                                                                                      \
+  "    KS_WT ((\\nsx) + (\\f)), (\\nsx), 1, 0\n"                                                                   \
+  "    KS_KM2 ((\\f) / (2 * %[nb])), (((\\f) %% (2 * %[nb])) >> 1), (1 - ((\\f) & 1)), ((\\nsx) + (\\f))\n"       \
+  "    KS_RD ((\\nsx) + (\\f) + 6), (\\nsx), 1\n"                                                                  \
+  "    .if (\\ex) && (%[dh] == 0)\n"                                                                               \
+  "      .if (\\f) == 0\n        s_nop 7\n        s_nop 7\n        s_nop 7\n      .endif\n"                        \
+  "      KS_EXR (((\\f) * 18) / (4 * %[nb])), ((((\\f) + 1) * 18) / (4 * %[nb]))\n"                                \
+  "    .endif\n"                                                                                                   \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  ".macro KS_SMS nsx, kv, ds, lr\n"                                                                                \
+  KS_SMC(0) KS_SMC(1) KS_SMC(2) KS_SMC(3) KS_SMC(4) KS_SMC(5) KS_SMC(6) KS_SMC(7)                                  \
+  KS_SMC(8) KS_SMC(9) KS_SMC(10) KS_SMC(11) KS_SMC(12) KS_SMC(13) KS_SMC(14) KS_SMC(15)                            \
+  ".endm\n"                                                                                                        \
+  ".macro KS_KMS nsx, ex\n"                                                                                        \
+  KS_KMC(0) KS_KMC(1) KS_KMC(2) KS_KMC(3) KS_KMC(4) KS_KMC(5) KS_KMC(6) KS_KMC(7)                                  \
+  KS_KMC(8) KS_KMC(9) KS_KMC(10) KS_KMC(11) KS_KMC(12) KS_KMC(13) KS_KMC(14) KS_KMC(15)                            \
+  ".endm\n"                                                                                                        \
+  "s_cmp_eq_u32 %[mode], 7\ns_cbranch_scc1 L_full_%=\n"                                                            \
+  "s_cmp_eq_u32 %[mode], 3\ns_cbranch_scc1 L_p12_%=\n"                                                             \
+  "s_cmp_eq_u32 %[mode], 5\ns_cbranch_scc1 L_p1e_%=\n"                                                             \
+  "s_cmp_eq_u32 %[mode], 1\ns_cbranch_scc1 L_p1_%=\n"                                                              \
+  "s_cmp_eq_u32 %[mode], 2\ns_cbranch_scc1 L_p2_%=\n"                                                              \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_full_%=:\n"                                                                                                   \
+  "KS_XR\nKS_RD6 %[ns], 1\nKS_LR\nKS_SMS %[ns], 1, 1, (4 - 4 * %[dh])\nKS_KMS %[ns], 1\nKS_ST\n"                  \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_p12_%=:\n"                                                                                                    \
+  "KS_XR\nKS_RD6 %[ns], 1\nKS_SMS %[ns], 1, 1, 0\nKS_KMS %[ns], 0\n"                                               \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_p1e_%=:\n"                                                                                                    \
+  "KS_RD6 %[ns], 0\nKS_LR\nKS_SMS %[ns], 0, 0, (4 - 4 * %[dh])\n"                                                  \
+  "s_nop 7\ns_nop 7\ns_nop 7\n"                                                                                    \
+  "KS_EXR 0, 18\nKS_ST\n"                                                                                          \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_p1_%=:\n"                                                                                                     \
+  "KS_RD6 %[ns], 0\nKS_SMS %[ns], 0, 0, 0\n"                                                                       \
+  "s_branch L_end_%=\n"                                                                                            \
+  "L_p2_%=:\n"                                                                                                     \
+  "KS_XR\nKS_RD6 0, 1\nKS_WT2 0, 6, 0, 0\nKS_DSR 0, 16\nKS_KMS 0, 0\n"                                             \
+  "L_end_%=:\n"                                                                                                    \
+  "s_waitcnt lgkmcnt(0)\n"                                                                                         \
+  "s_nop 7\ns_nop 7\ns_nop 7\n" /* MFMA results may be read by vector instructions next */                         \
+  ".purgem KS_WAIT\n.purgem KC_LD\n.purgem KS_XR\n.purgem KS_LR\n.purgem KS_RX\n.purgem KS_TR2\n"                  \
+  ".purgem KS_TX\n.purgem KS_RD\n.purgem KS_RD6\n.purgem KS_WT2\n.purgem KS_WT3\n.purgem KS_WT\n"                  \
+  ".purgem KS_DS1\n.purgem KS_DSR\n.purgem KS_EX1\n.purgem KS_EXR\n.purgem KS_ST\n.purgem KS_SM\n"                 \
+  ".purgem KS_MF\n.purgem KS_KM2\n.purgem KS_KM\n.purgem KS_SMS\n.purgem KS_KMS\n"
 
-// dV^T += dO^T P and dK^T += Q^T dS over NB 32-column blocks, the Oᵀ and Qᵀ
-// operands read transposed from the query tile 3 fragments ahead of their
-// MFMA (fragment buffers v[240:255], second-read addresses in
-// v236..v239).  addr[i] is the lane's address of block i's first
-// transposed read in the Q tile (cc = 0); the dO tile lies 16384 bytes
-// further, the second 16 queries (cc = 1) 8192, the read 8 rows down d2.
-template <int NB>
-__device__ __forceinline__ void kv_tr_chain(const int (&addr)[4], int d2, const bf16x8& pp0, const bf16x8& pp1,
-                                            const bf16x8& ds0, const bf16x8& ds1, f32x16& dv0, f32x16& dv1,
-                                            f32x16& dv2, f32x16& dv3, f32x16& dk0, f32x16& dk1, f32x16& dk2,
-                                            f32x16& dk3) {
-  static_assert(NB >= 1 && NB <= 4, "blocks");
-  f32x16 junk;
-  f32x4 junk2;
-  asm volatile(
-      ".if 0 < 4 * %[nb]\n"
-      "  ds_read_b64_tr_b16 v[240:241], %[a0] offset:16384\n"
-      "  v_add_u32 v236, %[a0], %[d2]\n"
-      "  ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
-      ".endif\n"
-      ".if 1 < 4 * %[nb]\n"
-      "  ds_read_b64_tr_b16 v[244:245], %[a0] offset:0\n"
-      "  v_add_u32 v237, %[a0], %[d2]\n"
-      "  ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
-      ".endif\n"
-      ".if 2 < 4 * %[nb]\n"
-      "  ds_read_b64_tr_b16 v[248:249], %[a0] offset:24576\n"
-      "  v_add_u32 v238, %[a0], %[d2]\n"
-      "  ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
-      ".endif\n"
-      ".if 3 < 4 * %[nb]\n"
-      "  ds_read_b64_tr_b16 v[252:253], %[a0] offset:8192\n"
-      "  v_add_u32 v239, %[a0], %[d2]\n"
-      "  ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
-      ".endif\n"
-      ".if 0 < 4 * %[nb]\n"
-      "  .if 0 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 0 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 0 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv0], v[240:243], %[pp0], %[dv0]\n"
-      "  .if 4 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[240:241], %[a1] offset:16384\n"
-      "    v_add_u32 v236, %[a1], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 1 < 4 * %[nb]\n"
-      "  .if 1 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 1 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 1 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk0], v[244:247], %[ds0], %[dk0]\n"
-      "  .if 5 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[244:245], %[a1] offset:0\n"
-      "    v_add_u32 v237, %[a1], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 2 < 4 * %[nb]\n"
-      "  .if 2 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 2 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 2 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv0], v[248:251], %[pp1], %[dv0]\n"
-      "  .if 6 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[248:249], %[a1] offset:24576\n"
-      "    v_add_u32 v238, %[a1], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 3 < 4 * %[nb]\n"
-      "  .if 3 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 3 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 3 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk0], v[252:255], %[ds1], %[dk0]\n"
-      "  .if 7 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[252:253], %[a1] offset:8192\n"
-      "    v_add_u32 v239, %[a1], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 4 < 4 * %[nb]\n"
-      "  .if 4 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 4 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 4 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv1], v[240:243], %[pp0], %[dv1]\n"
-      "  .if 8 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[240:241], %[a2] offset:16384\n"
-      "    v_add_u32 v236, %[a2], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 5 < 4 * %[nb]\n"
-      "  .if 5 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 5 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 5 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk1], v[244:247], %[ds0], %[dk1]\n"
-      "  .if 9 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[244:245], %[a2] offset:0\n"
-      "    v_add_u32 v237, %[a2], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 6 < 4 * %[nb]\n"
-      "  .if 6 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 6 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 6 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv1], v[248:251], %[pp1], %[dv1]\n"
-      "  .if 10 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[248:249], %[a2] offset:24576\n"
-      "    v_add_u32 v238, %[a2], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 7 < 4 * %[nb]\n"
-      "  .if 7 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 7 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 7 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk1], v[252:255], %[ds1], %[dk1]\n"
-      "  .if 11 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[252:253], %[a2] offset:8192\n"
-      "    v_add_u32 v239, %[a2], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 8 < 4 * %[nb]\n"
-      "  .if 8 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 8 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 8 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv2], v[240:243], %[pp0], %[dv2]\n"
-      "  .if 12 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[240:241], %[a3] offset:16384\n"
-      "    v_add_u32 v236, %[a3], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[242:243], v236 offset:16384\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 9 < 4 * %[nb]\n"
-      "  .if 9 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 9 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 9 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk2], v[244:247], %[ds0], %[dk2]\n"
-      "  .if 13 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[244:245], %[a3] offset:0\n"
-      "    v_add_u32 v237, %[a3], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[246:247], v237 offset:0\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 10 < 4 * %[nb]\n"
-      "  .if 10 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 10 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 10 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv2], v[248:251], %[pp1], %[dv2]\n"
-      "  .if 14 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[248:249], %[a3] offset:24576\n"
-      "    v_add_u32 v238, %[a3], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[250:251], v238 offset:24576\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 11 < 4 * %[nb]\n"
-      "  .if 11 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 11 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 11 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk2], v[252:255], %[ds1], %[dk2]\n"
-      "  .if 15 < 4 * %[nb]\n"
-      "    ds_read_b64_tr_b16 v[252:253], %[a3] offset:8192\n"
-      "    v_add_u32 v239, %[a3], %[d2]\n"
-      "    ds_read_b64_tr_b16 v[254:255], v239 offset:8192\n"
-      "  .endif\n"
-      ".endif\n"
-      ".if 12 < 4 * %[nb]\n"
-      "  .if 12 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 12 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 12 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv3], v[240:243], %[pp0], %[dv3]\n"
-      ".endif\n"
-      ".if 13 < 4 * %[nb]\n"
-      "  .if 13 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 13 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 13 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk3], v[244:247], %[ds0], %[dk3]\n"
-      ".endif\n"
-      ".if 14 < 4 * %[nb]\n"
-      "  .if 14 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 14 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 14 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dv3], v[248:251], %[pp1], %[dv3]\n"
-      ".endif\n"
-      ".if 15 < 4 * %[nb]\n"
-      "  .if 15 + 3 < 4 * %[nb]\n    s_waitcnt lgkmcnt(6)\n"
-      "  .elseif 15 + 2 < 4 * %[nb]\n    s_waitcnt lgkmcnt(4)\n"
-      "  .elseif 15 + 1 < 4 * %[nb]\n    s_waitcnt lgkmcnt(2)\n"
-      "  .else\n    s_waitcnt lgkmcnt(0)\n  .endif\n"
-      "  v_mfma_f32_32x32x16_bf16 %[dk3], v[252:255], %[ds1], %[dk3]\n"
-      ".endif\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 7\n"  // the MFMA results may be read by vector instructions right after
-      : [dv0] "+v"(dv0), [dv1] "+v"(dv1), [dv2] "+v"(dv2), [dv3] "+v"(dv3), [dk0] "+v"(dk0), [dk1] "+v"(dk1),
-        [dk2] "+v"(dk2), [dk3] "+v"(dk3), "=&{v[240:255]}"(junk), "=&{v[236:239]}"(junk2)
-      : [a0] "v"(addr[0]), [a1] "v"(addr[1]), [a2] "v"(addr[2]), [a3] "v"(addr[3]), [d2] "v"(d2), [pp0] "v"(pp0),
-        [pp1] "v"(pp1), [ds0] "v"(ds0), [ds1] "v"(ds1), [nb] "i"(NB)
-      : "memory");
+#define KV_STEP_IN                                                                                                 \
+  [ns] "i"(NS), [nb] "i"(NB), [dh] "i"(DH), [mode] "s"(mode), [r0] "v"(r[0]), [r1] "v"(r[1]), \
+                 [r2] "v"(r[2]), [r3] "v"(r[3]), [r4] "v"(r[4]), [r5] "v"(r[5]), [r6] "v"(r[6]), [r7] "v"(r[7]), \
+                 [ta0] "v"(ta[0]), [ta1] "v"(ta[1]), [ta2] "v"(ta[2]), [ta3] "v"(ta[3]), [tb0] "v"(tb[0]), \
+                 [tb1] "v"(tb[1]), [tb2] "v"(tb[2]), [tb3] "v"(tb[3]), [xpr] "v"(xpr), [xpw] "v"(xpw), [dlr] "v"(dlr), \
+                 [llr] "v"(llr), [c] "v"(c), [qg] "s"(cp.qg), [og] "s"(cp.og), [lq] "s"(cp.lq), [lo] "s"(cp.lo), \
+                 [cx] "s"(cp.exec), [o0] "v"(cp.off[0]), [o1] "v"(cp.off[1]), [o2] "v"(cp.off[2]), \
+                 [o3] "v"(cp.off[3]), "{a[0:15]}"(kvg[0]), "{a[16:31]}"(kvg[1]), "{a[32:47]}"(kvg[2]), \
+                 "{a[48:63]}"(kvg[3])
+#define KV_STEP_CLOB                                                                                               \
+  "memory", "scc", "m0", "exec", "v148", "v149", "v168", "v169", "v170", "v171", "v172", "v173", "v174", \
+                 "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", \
+                 "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", \
+                 "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", \
+                 "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", \
+                 "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", \
+                 "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", \
+                 "v253", "v254", "v255"
+
+// acc[i]: dV block i, acc[4 + i]: dK block i (i < NB; the rest unused, and
+// their operand names taken by immediates that the assembler never sees)
+template <int NS, int NB, int DH>
+__device__ __forceinline__ void kv_step(int mode, const int (&r)[8], const int (&ta)[4], const int (&tb)[4], int xpr,
+                                        int xpw, int dlr, int llr, float c, const KvCopy& cp, const f32x16 (&kvg)[4],
+                                        f32x16& mine, f32x16 (&acc)[8]) {
+  static_assert(NS >= 8 && NS <= 16 && NB >= 2 && NB <= 4, "shape");
+  if constexpr (NB == 4)
+    asm volatile(KV_STEP_TEXT
+                 : "=&{v[152:167]}"(mine), [dv0] "+a"(acc[0]), [dv1] "+a"(acc[1]), [dv2] "+a"(acc[2]),
+                   [dv3] "+a"(acc[3]), [dk0] "+a"(acc[4]), [dk1] "+a"(acc[5]), [dk2] "+a"(acc[6]), [dk3] "+a"(acc[7])
+                 : KV_STEP_IN
+                 : KV_STEP_CLOB);
+  else if constexpr (NB == 3)
+    asm volatile(KV_STEP_TEXT
+                 : "=&{v[152:167]}"(mine), [dv0] "+a"(acc[0]), [dv1] "+a"(acc[1]), [dv2] "+a"(acc[2]),
+                   [dk0] "+a"(acc[4]), [dk1] "+a"(acc[5]), [dk2] "+a"(acc[6])
+                 : KV_STEP_IN, [dv3] "i"(0), [dk3] "i"(0)
+                 : KV_STEP_CLOB);
+  else
+    asm volatile(KV_STEP_TEXT
+                 : "=&{v[152:167]}"(mine), [dv0] "+a"(acc[0]), [dv1] "+a"(acc[1]), [dk0] "+a"(acc[4]),
+                   [dk1] "+a"(acc[5])
+                 : KV_STEP_IN, [dv2] "i"(0), [dv3] "i"(0), [dk2] "i"(0), [dk3] "i"(0)
+                 : KV_STEP_CLOB);
 }
+#undef KV_STEP_TEXT
+#undef KV_STEP_IN
+#undef KV_STEP_CLOB
+#undef KS_DSCHK
+#undef KS_EXCHK
+#undef KS_SMC
+#undef KS_KMC
+#undef KS_LGK
 
 template <int D_, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_d256_kernel(
@@ -530,6 +399,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   auto obuf = [&](int sl) { return qbuf(sl) + C::kTileBytes; };
   auto lbuf = [&](int sl) { return qbuf(sl) + 2 * C::kTileBytes; };
   auto dbuf = [&](int sl) { return qbuf(sl) + 2 * C::kTileBytes + C::kStatBytes; };
+  auto lds_addr = [](const lds_char* p) { return (int)(uint32_t)(uintptr_t)p; };
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
             half = lane >> 5;
@@ -552,15 +422,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const int n_qtiles = (N + C::kQTile - 1) / C::kQTile;
   const int t_begin = CAUSAL ? k0 / C::kQTile : 0;  // earlier query tiles see none of these keys
   // exchange of tile t in buffer t % 2: [key group][P (bf16x8 [cc][lane]),
-  // dP (fp32x4 [r/4][lane]: each lane's 16 values as four 16-byte runs)]
+  // dP (fp32x4 [r/4][lane]: each lane's 16 values as four 16-byte runs)];
+  // the lane's entry of buffer xb
   auto xp = [&](int xb) {
     return (bf16x8 __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
                                                          kgrp * (C::kXpBytes + C::kXdBytes)) + lane;
   };
-  auto xdp = [&](int xb) {
-    return (f32x4 __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
-                                                      kgrp * (C::kXpBytes + C::kXdBytes) + C::kXpBytes) + lane;
-  };
+  auto xlane = [&](int xb) { return lds_addr((const lds_char*)xp(xb)); };
 
   // query-tile copies: scalar base and loop-invariant per-lane offsets for
   // whole tiles, rows clamped onto N-1 for a ragged last tile
@@ -588,207 +456,159 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   load_rows(t_begin);
   load_stats(t_begin);
 
-  // this wave's half of dK^T and dV^T: d blocks dh*kHalfBlocks .. (those below kDBlocks)
-  f32x16 dk[kHalfBlocks], dv[kHalfBlocks];
-#pragma unroll
-  for (int i = 0; i < kHalfBlocks; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
   const float c = a.scale_log2;
-  // K (S-forming wave) or V (dP-forming wave) of this wave's keys as B
-  // operands: key column l32, d = ds*16 + half*8 + 0..7
-  // (held as four 16-register groups, fragment ds at registers 4*(ds mod 4) of group ds/4)
-  f32x16 kvg[4];
-  {
-    const __bf16* __restrict__ src = dh == 0 ? K : V;
-    const int crow = key < N ? key : N - 1;
-#pragma unroll
-    for (int ds = 0; ds < 16; ++ds) {
-      const bf16x8 f = ds < kDSteps ? *(const bf16x8*)(src + (size_t)crow * D + ds * 16 + half * 8) : bf16x8{};
-      const f32x4 f4 = __builtin_bit_cast(f32x4, f);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kvg[ds >> 2][(ds & 3) * 4 + i] = f4[i];
-    }
-  }
   // the lane's byte offsets of fragments 0..7 of a row-major tile row l32
   int roff[8];
 #pragma unroll
   for (int ds = 0; ds < 8; ++ds) roff[ds] = lds_off_bytes<DP>(l32, ds * 2 + half);
-  // the lane's byte offsets of the first transposed read of d block
-  // dh*kHalfBlocks + i (queries 0..15 of a tile), and of its second read
-  // relative to the first (the same for every block)
-  int troff[4];
-  int trd2;
-  {
-    const int g = lane >> 4, j16 = lane & 15;
-    const int r1 = half * 4 + (j16 >> 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int dcol = (dh * kHalfBlocks + i) * 32 + (g & 1) * 16 + (j16 & 3) * 4;
-      troff[i] = lds_off_bytes<DP>(r1, dcol >> 3) + (dcol & 7) * 2;
-    }
-    const int dcol0 = (dh * kHalfBlocks) * 32 + (g & 1) * 16 + (j16 & 3) * 4;
-    trd2 = lds_off_bytes<DP>(r1 + 8, dcol0 >> 3) - lds_off_bytes<DP>(r1, dcol0 >> 3);
-  }
-
   // does key group kgrp see any query of tile t?
   auto tile_work = [&](int t) { return group_active && !(CAUSAL && t * C::kQTile + C::kQTile - 1 < wk0); };
 
-  for (int t = t_begin; t <= n_qtiles; ++t) {
-    // publishes tile t (loaded last step) and the exchange of tile t-1
-    wait_vmcnt<0>();
-    __syncthreads();
-    // tile t+1 into the slot of tile t-2, finished last step: its Q and dO
-    // rows from inside this wave's part-1 chain (a whole tile and a chain to
-    // run), else here
-    const bool part1 = t < n_qtiles && tile_work(t);
-    KvCopy kc = {0, 0, 0, 0, 0, {cp.off[0], cp.off[1], cp.off[2], cp.off[3]}};
-    if (t + 1 < n_qtiles) {
-      const int sl1 = (t + 1) % 3, row1 = (t + 1) * C::kQTile;
-      if (part1 && row1 + C::kQTile <= N) {
-        kc.qg = (uint64_t)(uintptr_t)(Q + (size_t)row1 * D);
-        kc.og = (uint64_t)(uintptr_t)(dO + (size_t)row1 * D);
-        kc.lq = (uint32_t)(uintptr_t)qbuf(sl1) + cp.lds_wave;
-        kc.lo = (uint32_t)(uintptr_t)obuf(sl1) + cp.lds_wave;
-        kc.exec = ~0ull;
-      } else {
-        load_rows(t + 1);
-      }
-      load_stats(t + 1);
-    }
-
-    // 1. tile t: S = Q_t K^T (dh = 0) or dP = dO_t V^T (dh = 1), to the exchange
-    if (t < n_qtiles && tile_work(t)) {
-      const int sl = t % 3, xb = t & 1, tq0 = t * C::kQTile;
-      const lds_char* at = dh == 0 ? qbuf(sl) : obuf(sl);
-      int addr[8];
-      const int tb = (int)(uint32_t)(uintptr_t)at;
+  // The two output halves run separate instances of the loop, each with one
+  // step site, so that the accumulators stay in their registers throughout.
+  auto run = [&](auto dhc) {
+    constexpr int DH = decltype(dhc)::value;
+    constexpr int HB = DH * kHalfBlocks;                             // first d block of this half
+    constexpr int NB = DH == 0 ? kHalfBlocks : C::kDBlocks - kHalfBlocks;  // its blocks
+    // K (S-forming wave) or V (dP-forming wave) of this wave's keys as B
+    // operands: key column l32, d = ds*16 + half*8 + 0..7, fragment ds at
+    // registers 4*(ds mod 4) of group ds/4.  Past D (D = 160) the step reads
+    // no fragment; those registers take a copy of an earlier one, since
+    // registers partly set from constants were rebuilt on every step.
+    f32x16 kvg[4];
+    {
+      const __bf16* __restrict__ src = DH == 0 ? K : V;
+      const int crow = key < N ? key : N - 1;
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds) addr[ds] = tb + roff[ds];
-      // L of the lane's 16 queries (four runs of four consecutive rows), read
-      // before the chain so that its latency overlaps the MFMAs
-      float lq[16];
-      if (dh == 0) {
+      for (int ds = 0; ds < 16; ++ds) {
+        const int dsl = ds < kDSteps ? ds : ds - 8;
+        const bf16x8 f = *(const bf16x8*)(src + (size_t)crow * D + dsl * 16 + half * 8);
+        const f32x4 f4 = __builtin_bit_cast(f32x4, f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kvg[ds >> 2][(ds & 3) * 4 + i] = f4[i];
+      }
+    }
+    // the lane's byte offsets of the two transposed reads of d block HB + i
+    // (queries 0..15 of a tile: rows r1 and r1 + 8)
+    int troff[4], trd2;
+    {
+      const int g = lane >> 4, j16 = lane & 15;
+      const int r1 = half * 4 + (j16 >> 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dcol = (HB + i) * 32 + (g & 1) * 16 + (j16 & 3) * 4;
+        troff[i] = lds_off_bytes<DP>(r1, dcol >> 3) + (dcol & 7) * 2;
+      }
+      // the same for every block: the row swizzles of r1 and r1 + 8 differ in
+      // one bit, which meets the same bit of every block's chunk index
+      const int dcol0 = HB * 32 + (g & 1) * 16 + (j16 & 3) * 4;
+      trd2 = lds_off_bytes<DP>(r1 + 8, dcol0 >> 3) - lds_off_bytes<DP>(r1, dcol0 >> 3);
+    }
+    // this wave's half of dV^T (acc[0..NB-1]) and dK^T (acc[4..4+NB-1])
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+    for (int t = t_begin; t <= n_qtiles; ++t) {
+      // publishes tile t (loaded last step) and the exchange of tile t-1
+      wait_vmcnt<0>();
+      __syncthreads();
+      // (t through an empty asm: a first step told apart from the rest by the
+      // compiler was peeled off the loop, and with two step sites the
+      // accumulators were moved out of their registers and back every step)
+      int tt = t;
+      asm volatile("" : "+s"(tt));
+      const bool part1 = t < n_qtiles && tile_work(t);
+      const bool part2 = tt > t_begin && tile_work(tt - 1);
+      // tile t+1 into the slot of tile t-2, finished last step: its Q and dO
+      // rows from inside the step's first chain (a whole tile and a chain to
+      // run), else here
+      KvCopy kc = {0, 0, 0, 0, 0, {cp.off[0], cp.off[1], cp.off[2], cp.off[3]}};
+      if (t + 1 < n_qtiles) {
+        const int sl1 = (t + 1) % 3, row1 = (t + 1) * C::kQTile;
+        if (part1 && row1 + C::kQTile <= N) {
+          kc.qg = (uint64_t)(uintptr_t)(Q + (size_t)row1 * D);
+          kc.og = (uint64_t)(uintptr_t)(dO + (size_t)row1 * D);
+          kc.lq = (uint32_t)(uintptr_t)qbuf(sl1) + cp.lds_wave;
+          kc.lo = (uint32_t)(uintptr_t)obuf(sl1) + cp.lds_wave;
+          kc.exec = ~0ull;
+        } else {
+          load_rows(t + 1);
+        }
+        load_stats(t + 1);
+      }
+      const int sl = t % 3, slp = (t + 2) % 3, tq0 = t * C::kQTile;
+      // P of a tile that crosses the diagonal or the end of the sequence
+      // needs the mask: computed after the step from the returned S
+      const bool masked = DH == 0 && ((CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N));
+      const int mode =
+          __builtin_amdgcn_readfirstlane((part1 ? 1 : 0) | (part2 ? 2 : 0) | (part1 && !masked ? 4 : 0));
+      int r[8], ta[4], tb[4];
+      const int rbase = lds_addr(DH == 0 ? qbuf(sl) : obuf(sl)), tbase = lds_addr(qbuf(slp));
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) r[ds] = rbase + roff[ds];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ta[i] = tbase + troff[i];
+        tb[i] = ta[i] + trd2;
+      }
+      const int xpw = xlane(t & 1), xpr = xlane((t + 1) & 1);
+      const int dlr = lds_addr(dbuf(slp)) + 16 * half, llr = lds_addr(lbuf(sl)) + 16 * half;
+      f32x16 mine;
+      kv_step<kDSteps, NB, DH>(mode, r, ta, tb, xpr, xpw, dlr, llr, c, kc, kvg, mine, acc);
+      if (DH == 0 && part1 && masked) {
+        // P = exp(S - L) with the mask; queries of register r: (r/4)*8 + half*4 + r%4
+        float lq[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 l4 = *(const f32x4 __attribute__((address_space(3)))*)(lbuf(sl) + 4 * (g * 8 + half * 4));
 #pragma unroll
           for (int i = 0; i < 4; ++i) lq[g * 4 + i] = l4[i];
         }
-      }
-      f32x16 mine = kv_chain<kDSteps>(addr, kvg[0], kvg[1], kvg[2], kvg[3], kc);
-      if (dh == 0) {  // P = exp(S - L), masked; queries of register r: (r/4)*8 + half*4 + r%4
-        const bool masked = (CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N);
-        // two instances: tiles that need no mask carry no selects
-        auto exp_p = [&](auto mconst) {
-          constexpr bool MASKED = decltype(mconst)::value;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-            float x = __builtin_fmaf(mine[r], c, -lq[r] * kLog2e);
-            if constexpr (MASKED) {
-              bool keep = tq0 + qr < N;
-              if constexpr (CAUSAL) keep = keep && key <= tq0 + qr;
-              x = keep ? x : -__builtin_inff();
-            }
-            mine[r] = fast_exp2(x);
-          }
-        };
-        if (masked)
-          exp_p(std::integral_constant<bool, true>());
-        else
-          exp_p(std::integral_constant<bool, false>());
+        for (int rr = 0; rr < 16; ++rr) {
+          const int qr = (rr >> 2) * 8 + half * 4 + (rr & 3);
+          float x = __builtin_fmaf(mine[rr], c, -lq[rr] * kLog2e);
+          bool keep = tq0 + qr < N;
+          if constexpr (CAUSAL) keep = keep && key <= tq0 + qr;
+          mine[rr] = fast_exp2(keep ? x : -__builtin_inff());
+        }
         // P rounded to bf16 once; both waves form dS from this rounded P
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           bf16x2 pp[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) pp[i] = pack_bf16(mine[cc * 8 + 2 * i], mine[cc * 8 + 2 * i + 1]);
-          xp(xb)[cc * 64] = join8(pp[0], pp[1], pp[2], pp[3]);
+          xp(t & 1)[cc * 64] = join8(pp[0], pp[1], pp[2], pp[3]);
         }
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          xdp(xb)[g * 64] = f32x4{mine[4 * g], mine[4 * g + 1], mine[4 * g + 2], mine[4 * g + 3]};
       }
     }
 
-    // 2. tile t-1, both waves: P (bf16) and dS = P (dP - delta) as bf16
-    // operands from the exchange, then their half of dV and dK
-    if (t > t_begin && tile_work(t - 1)) {
-      const int sl = (t - 1) % 3, xb = (t - 1) & 1;
-      float dl[16];  // delta of the lane's 16 queries, read as four runs of four
+    wait_vmcnt<0>();  // no direct-to-LDS copy may outlive the workgroup
+    if (!group_active || key >= N) return;
+    __bf16* __restrict__ dK = (__bf16*)a.dk + head_off;
+    __bf16* __restrict__ dV = (__bf16*)a.dv + head_off;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 d4 = *(const f32x4 __attribute__((address_space(3)))*)(dbuf(sl) + 4 * (g * 8 + half * 4));
+    for (int i = 0; i < NB; ++i) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dl[g * 4 + i] = d4[i];
-      }
-      float dpv[16];  // dP of the lane's 16 queries
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 p4 = xdp(xb)[g * 64];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dpv[g * 4 + i] = p4[i];
-      }
-      bf16x8 ppk[2], dspk[2];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        ppk[cc] = xp(xb)[cc * 64];
-        const bf16x2* pp = (const bf16x2*)&ppk[cc];
-        bf16x2 dd[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float dsv[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = cc * 8 + 2 * i + u;
-            dsv[u] = (float)pp[i][u] * (dpv[r] - dl[r]);
-          }
-          dd[i] = pack_bf16(dsv[0], dsv[1]);
-        }
-        dspk[cc] = join8(dd[0], dd[1], dd[2], dd[3]);
-      }
-      // dV^T += dO^T P,  dK^T += Q^T dS over d blocks dh*kHalfBlocks ..
-      int taddr[4];
-      const int qb0 = (int)(uint32_t)(uintptr_t)qbuf(sl);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) taddr[i] = qb0 + troff[i];
-      if constexpr (kHalfBlocks == 4) {
-        kv_tr_chain<4>(taddr, trd2, ppk[0], ppk[1], dspk[0], dspk[1], dv[0], dv[1], dv[2], dv[3], dk[0], dk[1], dk[2],
-                       dk[3]);
-      } else {
-        // D = 160: blocks 0..2 (half 0) or 3..4 (half 1); the unused operand
-        // slots take scratch accumulators (no two operands may name one variable)
-        f32x16 sv0 = {}, sk0 = {}, sv1 = {}, sk1 = {};
-        if (dh == 0)
-          kv_tr_chain<3>(taddr, trd2, ppk[0], ppk[1], dspk[0], dspk[1], dv[0], dv[1], dv[2], sv0, dk[0], dk[1], dk[2],
-                         sk0);
-        else
-          kv_tr_chain<2>(taddr, trd2, ppk[0], ppk[1], dspk[0], dspk[1], dv[0], dv[1], sv0, sv1, dk[0], dk[1], sk0,
-                         sk1);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const size_t off = (size_t)key * D + (HB + i) * 32 + g4 * 8 + half * 4;
+        const f32x16& k4 = acc[4 + i];
+        const f32x16& v4 = acc[i];
+        u32x2 wk = {pack_bf16_u32(k4[g4 * 4 + 0] * a.scale, k4[g4 * 4 + 1] * a.scale),
+                    pack_bf16_u32(k4[g4 * 4 + 2] * a.scale, k4[g4 * 4 + 3] * a.scale)};
+        u32x2 wv = {pack_bf16_u32(v4[g4 * 4 + 0], v4[g4 * 4 + 1]), pack_bf16_u32(v4[g4 * 4 + 2], v4[g4 * 4 + 3])};
+        *(u32x2*)(dK + off) = wk;
+        *(u32x2*)(dV + off) = wv;
       }
     }
-  }
-
-  wait_vmcnt<0>();  // no direct-to-LDS copy may outlive the workgroup
-  if (!group_active || key >= N) return;
-  __bf16* __restrict__ dK = (__bf16*)a.dk + head_off;
-  __bf16* __restrict__ dV = (__bf16*)a.dv + head_off;
-#pragma unroll
-  for (int i = 0; i < kHalfBlocks; ++i) {
-    if (dh * kHalfBlocks + i >= C::kDBlocks) break;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const size_t off = (size_t)key * D + (dh * kHalfBlocks + i) * 32 + g4 * 8 + half * 4;
-      u32x2 wk = {pack_bf16_u32(dk[i][g4 * 4 + 0] * a.scale, dk[i][g4 * 4 + 1] * a.scale),
-                  pack_bf16_u32(dk[i][g4 * 4 + 2] * a.scale, dk[i][g4 * 4 + 3] * a.scale)};
-      u32x2 wv = {pack_bf16_u32(dv[i][g4 * 4 + 0], dv[i][g4 * 4 + 1]),
-                  pack_bf16_u32(dv[i][g4 * 4 + 2], dv[i][g4 * 4 + 3])};
-      *(u32x2*)(dK + off) = wk;
-      *(u32x2*)(dV + off) = wv;
-    }
-  }
+  };
+  if (dh == 0)
+    run(std::integral_constant<int, 0>());
+  else
+    run(std::integral_constant<int, 1>());
 }
 
 template <int D, bool CAUSAL>

@@ -20,11 +20,13 @@
 // LDS rows of D = 256 (the chunks past 160 unused, global rows 160 wide);
 // its five 32-column output blocks split 3 + 2 over the two waves.
 //
-// The loop is skewed by one query tile so that a step has one barrier and
-// two independent halves of MFMA work: step i forms S (or dP) of tile i and
-// publishes P (or dP) to the exchange, then finishes tile i-1 from the
-// exchange the previous step published (dS, dV, dK).  Query tiles live two
-// steps (a 3-slot ring) and the exchange is double-buffered.
+// The loop is skewed by one query tile so that a step has two independent
+// halves of MFMA work: step i forms S (or dP) of tile i and publishes P (or
+// dP) to the exchange, then finishes tile i-1 (dV, dK).  dS of tile i-1 is
+// formed once, by the dP wave from the P the S wave published the step
+// before, and reaches the S wave through the exchange across a barrier in
+// the middle of the step.  Query tiles live two steps (a 3-slot ring) and
+// the exchange is double-buffered.
 //
 // Layouts are those of the general kernel (fa_bwd.hip): S = Q K^T and
 // dP = dO V^T put a key in every lane column and 16 queries in its
@@ -51,8 +53,10 @@ struct KvDsplitCfg {
   static constexpr int kStatBytes = 256;       // 64 floats of L or delta (rows past the tile are spare)
   static constexpr int kXpBytes = 2 * 64 * 16;  // P: two bf16x8 operands per lane
   static constexpr int kXdBytes = 16 * 64 * 4;  // dP: a 32x32 fp32 accumulator, [r/4][lane] x 4
+  static constexpr int kXsBytes = 2 * 64 * 16;  // dS: as P
   static constexpr int kSlotBytes = 2 * kTileBytes + 2 * kStatBytes;  // Q, dO, L, delta of one tile
-  static constexpr int kXBytes = 2 * (kXpBytes + kXdBytes);            // both key groups
+  static constexpr int kXGroupBytes = kXpBytes + kXdBytes + kXsBytes;  // one key group
+  static constexpr int kXBytes = 2 * kXGroupBytes;                     // both key groups
   static constexpr int kLdsBytes = 3 * kSlotBytes + 2 * kXBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 };
@@ -72,27 +76,31 @@ struct KvCopy {
 
 // ------------------------------------------------ one pipelined query-tile step
 //
-// One asm block per query tile t runs the NS S (or dP) MFMAs of tile t with,
-// in their shadow, dS of tile t-1 (from the exchange the partner wave
-// published last step), then the 4 NB dV/dK MFMAs of tile t-1 with, in
-// their shadow, the exponentials of tile t; P (or dP) of tile t goes to the
-// exchange at the end.  The LDS reads run six fragments ahead of their MFMA
-// across both chains, and the next tile's copy goes out between the first
-// eight MFMAs.  Issued between the chains instead, the vector work took as
-// long as the chains themselves: one wave per SIMD issues a vector
-// instruction only every ~9 cycles.  Per element the arithmetic is the
-// plain loop's, instruction for instruction: dS = float(P) (dP - delta),
+// One asm block per query tile t.  The S wave (dh = 0) runs the NS S MFMAs
+// of tile t, then the 4 NB dV/dK MFMAs of tile t-1 with, in their shadow,
+// the exponentials of tile t, and publishes P of tile t at the end.  The dP
+// wave runs the NS dP MFMAs of tile t with, in their shadow, dS of tile t-1
+// (from P the S wave published last step and its own dP), publishes dS
+// before a barrier in the middle of the step, then its dV/dK MFMAs of tile
+// t-1 and dP of tile t.  The S wave reads dS after that barrier; its dV
+// MFMAs, which need none, go first.  So each wave carries one of the two
+// element-wise passes (16 exponentials or 16 dS per lane and tile): one
+// wave per SIMD issues a vector instruction only every ~9 cycles, and the
+// step waits for its slowest wave.  The LDS reads run six fragments ahead
+// of their MFMA across both chains, and the next tile's copy goes out
+// between the first eight MFMAs.  Per element the arithmetic is the plain
+// loop's, instruction for instruction: dS = float(P) (dP - delta),
 // P = exp2(fma(S, c, -L log2 e)), pairs packed to bf16 with round to
 // nearest even.
 //
 // mode (wave-uniform): bit 0 tile t is this wave's (S or dP chain), bit 1
 // tile t-1 is (dS and the dV/dK chain), bit 2 the exponentials (or dP's
 // store) go in the block too -- left out for a masked tile, which the
-// caller finishes from the returned S.
+// caller finishes from the returned S.  Every mode passes the middle
+// barrier once.
 //
-// Registers: K or V rows in a[0:63] (fragment ds at a[4 ds : 4 ds + 3]); dV
-// block i in a[64 + 16 i : +15], dK block i in a[128 + 16 i : +15]; S or dP
-// of tile t in v[152:167]; L of tile t in v[168:183], whose first 8
+// Registers: K or V rows in a[0:63] (fragment ds at a[4 ds : 4 ds + 3]); S
+// or dP of tile t in v[152:167]; L of tile t in v[168:183], whose first 8
 // registers then take tile t's packed P; tile t-1's packed P in v[184:191],
 // its dP in v[192:207], delta in v[208:223], packed dS in v[224:231]; six
 // fragment buffers in v[232:255]; temporaries v148, v149.
@@ -100,12 +108,12 @@ struct KvCopy {
 // slot, fragment ds + 8 256 bytes further; ta[i], tb[i] the two transposed
 // reads of local d block i in tile t-1's Q slot (queries 16..31 8192 bytes
 // further, the dO slot 16384); xpr, xpw the lane's exchange entries of
-// tiles t-1 and t (P at +0 and +1024, dP at +2048 + 1024 g); dlr delta of
-// tile t-1, llr L of tile t (four runs 32 bytes apart).
+// tiles t-1 and t (P at +0 and +1024, dP at +2048 + 1024 g, dS at +6144 and
+// +7168); dlr delta of tile t-1, llr L of tile t (four runs 32 bytes apart).
 #define KS_DSCHK(N) "  .if (" #N " >= (\\lo)) && (" #N " < (\\hi))\n    KS_DS1 " #N "\n  .endif\n"
 #define KS_EXCHK(N) "  .if (" #N " >= (\\lo)) && (" #N " < (\\hi))\n    KS_EX1 " #N "\n  .endif\n"
-#define KS_SMC(N) "  KS_SM " #N ", \\nsx, \\kv, \\ds, \\lr\n"
-#define KS_KMC(N) "  KS_KM " #N ", \\nsx, \\ex\n"
+#define KS_SMC(N) "  KS_SM " #N ", \\nsx, \\kv, \\ds, \\lr, \\bs, \\bp\n"
+#define KS_KMC(N) "  KS_KM " #N ", \\nsx, \\ex, \\bs, \\bp\n"
 #define KS_LGK(N) "  .elseif (\\n) == " #N "\n    s_waitcnt lgkmcnt(" #N ")\n"
 #define KV_STEP_TEXT                                                                                               \
   ".macro KS_WAIT n\n"                                                                                             \
@@ -129,13 +137,15 @@ struct KvCopy {
   "  .else\n    global_load_lds_dwordx4 %[o3], %[og]\n  .endif\n"                                                 \
   "  s_mov_b64 exec, -1\n"                                                                                         \
   ".endm\n"                                                                                                        \
-  /* tile t-1's P, dP and delta (10 reads) */                                                                     \
+  /* tile t-1's P; for the dP wave also its dP and delta */                                                       \
   ".macro KS_XR\n"                                                                                                 \
   "  ds_read_b128 v[184:187], %[xpr]\n  ds_read_b128 v[188:191], %[xpr] offset:1024\n"                             \
-  "  ds_read_b128 v[192:195], %[xpr] offset:2048\n  ds_read_b128 v[196:199], %[xpr] offset:3072\n"                 \
-  "  ds_read_b128 v[200:203], %[xpr] offset:4096\n  ds_read_b128 v[204:207], %[xpr] offset:5120\n"                 \
-  "  ds_read_b128 v[208:211], %[dlr]\n  ds_read_b128 v[212:215], %[dlr] offset:32\n"                               \
-  "  ds_read_b128 v[216:219], %[dlr] offset:64\n  ds_read_b128 v[220:223], %[dlr] offset:96\n"                     \
+  "  .if %[dh] == 1\n"                                                                                             \
+  "    ds_read_b128 v[192:195], %[xpr] offset:2048\n    ds_read_b128 v[196:199], %[xpr] offset:3072\n"             \
+  "    ds_read_b128 v[200:203], %[xpr] offset:4096\n    ds_read_b128 v[204:207], %[xpr] offset:5120\n"             \
+  "    ds_read_b128 v[208:211], %[dlr]\n    ds_read_b128 v[212:215], %[dlr] offset:32\n"                           \
+  "    ds_read_b128 v[216:219], %[dlr] offset:64\n    ds_read_b128 v[220:223], %[dlr] offset:96\n"                 \
+  "  .endif\n"                                                                                                     \
   ".endm\n"                                                                                                        \
   /* tile t's L (4 reads, S wave) */                                                                              \
   ".macro KS_LR\n"                                                                                                 \
@@ -175,13 +185,14 @@ struct KvCopy {
   "  .elseif (\\i) == 2\n    KS_TR2 %[ta2], %[tb2], ((\\cc) * 8192 + (\\dv) * 16384), (\\p)\n"                     \
   "  .else\n    KS_TR2 %[ta3], %[tb3], ((\\cc) * 8192 + (\\dv) * 16384), (\\p)\n  .endif\n"                       \
   ".endm\n"                                                                                                        \
-  /* stream position p: S/dP fragments, then with kv the dV/dK fragments (cc outer, block, dV before dK) */       \
+  /* stream position p: S/dP fragments, then with kv the dV fragments (cc outer, block inner), then dK's */       \
   ".macro KS_RD p, nsx, kv\n"                                                                                      \
   "  .if (\\p) < (\\nsx)\n"                                                                                        \
   "    KS_RX (\\p)\n"                                                                                              \
+  "  .elseif (\\kv) && ((\\p) < (\\nsx) + 2 * %[nb])\n"                                                            \
+  "    KS_TX (((\\p) - (\\nsx)) / %[nb]), (((\\p) - (\\nsx)) %% %[nb]), 1, (\\p)\n"                               \
   "  .elseif (\\kv) && ((\\p) < (\\nsx) + 4 * %[nb])\n"                                                            \
-  "    KS_TX ((((\\p) - (\\nsx))) / (2 * %[nb])), (((((\\p) - (\\nsx))) %% (2 * %[nb])) >> 1), "                   \
-  "(1 - (((\\p) - (\\nsx)) & 1)), (\\p)\n"                                                                         \
+  "    KS_TX (((\\p) - (\\nsx) - 2 * %[nb]) / %[nb]), (((\\p) - (\\nsx) - 2 * %[nb]) %% %[nb]), 0, (\\p)\n"       \
   "  .endif\n"                                                                                                     \
   ".endm\n"                                                                                                        \
   ".macro KS_RD6 nsx, kv\n"                                                                                        \
@@ -194,15 +205,21 @@ struct KvCopy {
   "  .elseif (\\a) >= (\\nsx)\n    KS_WAIT (2 * ((\\b) - (\\a)) + (\\x))\n"                                        \
   "  .else\n    KS_WAIT (((\\nsx) - (\\a)) + 2 * ((\\b) - (\\nsx)) + (\\x))\n  .endif\n"                           \
   ".endm\n"                                                                                                        \
-  /* before the MFMA of position m: its fragment landed (positions m+1..m+5 may be in flight, and the x */        \
-  /* L reads issued after position 5 while m < 6) */                                                              \
   ".macro KS_WT3 m, nsx, kv, x\n"                                                                                  \
   "  .if (\\m) + 6 <= (\\nsx) + 4 * %[nb] * (\\kv)\n    KS_WT2 ((\\m) + 1), ((\\m) + 6), (\\nsx), (\\x)\n"      \
   "  .else\n    KS_WT2 ((\\m) + 1), ((\\nsx) + 4 * %[nb] * (\\kv)), (\\nsx), (\\x)\n  .endif\n"                   \
   ".endm\n"                                                                                                        \
-  ".macro KS_WT m, nsx, kv, lr\n"                                                                                  \
-  "  .if (\\m) < 6\n    KS_WT3 (\\m), (\\nsx), (\\kv), (\\lr)\n"                                                   \
-  "  .else\n    KS_WT3 (\\m), (\\nsx), (\\kv), 0\n  .endif\n"                                                      \
+  /* before the MFMA of position m: its fragment landed.  Positions m+1..m+5 may be in flight, and also */       \
+  /* the lr L reads issued after position 5 (m < 6) and the two dS reads issued after the middle barrier, */     \
+  /* which follows the MFMA of position bs and the read of position bs + 6 (bs < m <= bs + 6) */                  \
+  ".macro KS_WT m, nsx, kv, lr, bs\n"                                                                              \
+  "  .if ((\\m) > (\\bs)) && ((\\m) <= (\\bs) + 6)\n"                                                              \
+  "    .if (\\m) < 6\n      KS_WT3 (\\m), (\\nsx), (\\kv), ((\\lr) + 2)\n"                                         \
+  "    .else\n      KS_WT3 (\\m), (\\nsx), (\\kv), 2\n    .endif\n"                                                  \
+  "  .else\n"                                                                                                      \
+  "    .if (\\m) < 6\n      KS_WT3 (\\m), (\\nsx), (\\kv), (\\lr)\n"                                               \
+  "    .else\n      KS_WT3 (\\m), (\\nsx), (\\kv), 0\n    .endif\n"                                                  \
+  "  .endif\n"                                                                                                     \
   ".endm\n"                                                                                                        \
   /* dS half-step h of pair k = h/2 (elements 2k, 2k+1; P word k): unpack and dP - delta, then product and pack */ \
   ".macro KS_DS1 h\n"                                                                                              \
@@ -222,7 +239,7 @@ struct KvCopy {
   KS_DSCHK(8) KS_DSCHK(9) KS_DSCHK(10) KS_DSCHK(11) KS_DSCHK(12) KS_DSCHK(13) KS_DSCHK(14) KS_DSCHK(15)            \
   ".endm\n"                                                                                                        \
   /* exponential slot s (S wave): element s's exponent, element s-1's exp2, pair (s-3)/2's pack -- an */        \
-  /* exp2 result is read no sooner than one slot later */                                                         \
+  /* exp2 result is read no sooner than one instruction later */                                                  \
   ".macro KS_EX1 s\n"                                                                                              \
   "  .if %[dh] == 0\n"                                                                                             \
   "    .if (\\s) < 16\n"                                                                                           \
@@ -232,7 +249,7 @@ struct KvCopy {
   "    .if ((\\s) >= 1) && ((\\s) <= 16)\n"                                                                        \
   "      v_exp_f32 v[151 + (\\s)], v[151 + (\\s)]\n"                                                               \
   "    .endif\n"                                                                                                   \
-  "    .if (\\s) == 17\n      s_nop 0\n    .endif\n" /* exp2 result read by the next instruction */                     \
+  "    .if (\\s) == 17\n      s_nop 0\n    .endif\n"                                                             \
   "    .if ((\\s) >= 3) && (((\\s) & 1) == 1)\n"                                                                   \
   "      v_cvt_pk_bf16_f32 v[168 + ((\\s) - 3) / 2], v[149 + (\\s)], v[150 + (\\s)]\n"                             \
   "    .endif\n"                                                                                                   \
@@ -253,10 +270,27 @@ struct KvCopy {
   "    ds_write_b128 %[xpw], v[160:163] offset:4096\n    ds_write_b128 %[xpw], v[164:167] offset:5120\n"           \
   "  .endif\n"                                                                                                     \
   ".endm\n"                                                                                                        \
-  /* S/dP MFMA m, the read of position m+6, copy load m (m < 8), and with ds its share of dS */                  \
-  ".macro KS_SM m, nsx, kv, ds, lr\n"                                                                              \
+  /* the middle barrier; with kv the dP wave publishes tile t-1's dS before it and the S wave reads it after */  \
+  ".macro KS_MB kv\n"                                                                                              \
+  "  .if %[dh] == 1\n"                                                                                             \
+  "    .if (\\kv)\n"                                                                                               \
+  "      s_nop 1\n"                                                                                                \
+  "      ds_write_b128 %[xpr], v[224:227] offset:6144\n      ds_write_b128 %[xpr], v[228:231] offset:7168\n"       \
+  "      s_waitcnt lgkmcnt(0)\n"                                                                                   \
+  "    .endif\n"                                                                                                   \
+  "    s_barrier\n"                                                                                                \
+  "  .else\n"                                                                                                      \
+  "    s_barrier\n"                                                                                                \
+  "    .if (\\kv)\n"                                                                                               \
+  "      ds_read_b128 v[224:227], %[xpr] offset:6144\n      ds_read_b128 v[228:231], %[xpr] offset:7168\n"         \
+  "    .endif\n"                                                                                                   \
+  "  .endif\n"                                                                                                     \
+  ".endm\n"                                                                                                        \
+  /* S/dP MFMA m, the read of position m+6, copy load m (m < 8), dS half-steps (dP wave, with ds), and */        \
+  /* the middle barrier after position bp */                                                                      \
+  ".macro KS_SM m, nsx, kv, ds, lr, bs, bp\n"                                                                      \
   "  .if (\\m) < (\\nsx)\n"                                                                                        \
-  "    KS_WT (\\m), (\\nsx), (\\kv), (\\lr)\n"                                                                     \
+  "    KS_WT (\\m), (\\nsx), (\\kv), (\\lr), (\\bs)\n"                                                             \
   "    .if (\\m) == 0\n"                                                                                           \
   "      v_mfma_f32_32x32x16_bf16 v[152:167], v[232 + ((\\m) %% 6) * 4 : 235 + ((\\m) %% 6) * 4], "                \
   "a[(\\m) * 4 : (\\m) * 4 + 3], 0\n"                                                                             \
@@ -266,73 +300,90 @@ struct KvCopy {
   "    .endif\n"                                                                                                   \
   "    KS_RD ((\\m) + 6), (\\nsx), (\\kv)\n"                                                                       \
   "    .if (\\m) < 8\n      KC_LD (\\m)\n    .endif\n"                                                           \
-  "    .if (\\ds)\n      KS_DSR (((\\m) * 16) / (\\nsx)), ((((\\m) + 1) * 16) / (\\nsx))\n    .endif\n"            \
+  "    .if (\\ds) && (%[dh] == 1)\n"                                                                               \
+  "      KS_DSR (((\\m) * 16) / ((\\nsx) - 1)), ((((\\m) + 1) * 16) / ((\\nsx) - 1))\n"                            \
+  "    .endif\n"                                                                                                   \
+  "    .if (\\m) == (\\bp)\n      KS_MB (\\kv)\n    .endif\n"                                                      \
   "  .endif\n"                                                                                                     \
   ".endm\n"                                                                                                        \
-  /* dV/dK MFMA of fragment f (position nsx + f), the read 6 ahead, and with ex its exponential slots */         \
-  /* one dV/dK MFMA: acc += fragment buffer (p mod 6) x B (4 registers from vb) */                               \
-  ".macro KS_MF acc, p, vb\n"                                                                                       \
-  "  v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], v[\\vb : (\\vb) + 3], \\acc\n" \
+  /* one dV (dv) or dK MFMA of query chunk cc, local block i, fragment buffer p mod 6 */                           \
+  ".macro KS_MF acc, p, vb\n"                                                                                      \
+  "  v_mfma_f32_32x32x16_bf16 \\acc, v[232 + ((\\p) %% 6) * 4 : 235 + ((\\p) %% 6) * 4], v[\\vb : (\\vb) + 3], "  \
+  "\\acc\n"                                                                                                        \
   ".endm\n"                                                                                                        \
-  ".macro KS_KM2 cc, i, dv, p\n"                                                                                   \
-  "  .if (\\dv) && ((\\i) == 0)\n    KS_MF %[dv0], (\\p), (184 + 4 * (\\cc))\n"                                       \
-  "  .elseif (\\dv) && ((\\i) == 1)\n    KS_MF %[dv1], (\\p), (184 + 4 * (\\cc))\n"                                   \
-  "  .elseif (\\dv) && ((\\i) == 2)\n    KS_MF %[dv2], (\\p), (184 + 4 * (\\cc))\n"                                   \
-  "  .elseif (\\dv)\n    KS_MF %[dv3], (\\p), (184 + 4 * (\\cc))\n"                                                    \
-  "  .elseif (\\i) == 0\n    KS_MF %[dk0], (\\p), (224 + 4 * (\\cc))\n"                                                 \
-  "  .elseif (\\i) == 1\n    KS_MF %[dk1], (\\p), (224 + 4 * (\\cc))\n"                                                 \
-  "  .elseif (\\i) == 2\n    KS_MF %[dk2], (\\p), (224 + 4 * (\\cc))\n"                                                 \
-  "  .else\n    KS_MF %[dk3], (\\p), (224 + 4 * (\\cc))\n  .endif\n"                                                   \
+  ".macro KS_KV cc, i, dv, p\n"                                                                                    \
+  "  .if (\\dv) && ((\\i) == 0)\n    KS_MF %[dv0], (\\p), (184 + 4 * (\\cc))\n"                                     \
+  "  .elseif (\\dv) && ((\\i) == 1)\n    KS_MF %[dv1], (\\p), (184 + 4 * (\\cc))\n"                                 \
+  "  .elseif (\\dv) && ((\\i) == 2)\n    KS_MF %[dv2], (\\p), (184 + 4 * (\\cc))\n"                                 \
+  "  .elseif (\\dv)\n    KS_MF %[dv3], (\\p), (184 + 4 * (\\cc))\n"                                                  \
+  "  .elseif (\\i) == 0\n    KS_MF %[dk0], (\\p), (224 + 4 * (\\cc))\n"                                               \
+  "  .elseif (\\i) == 1\n    KS_MF %[dk1], (\\p), (224 + 4 * (\\cc))\n"                                               \
+  "  .elseif (\\i) == 2\n    KS_MF %[dk2], (\\p), (224 + 4 * (\\cc))\n"                                               \
+  "  .else\n    KS_MF %[dk3], (\\p), (224 + 4 * (\\cc))\n  .endif\n"                                                 \
   ".endm\n"                                                                                                        \
-  ".macro KS_KM f, nsx, ex\n"                                                                                      \
+  /* dV/dK MFMA f (position nsx + f; dV for f < 2 nb), the read 6 ahead, the exponential slots (S wave, */       \
+  /* with ex), and the middle barrier after position bp */                                                        \
+  ".macro KS_KM f, nsx, ex, bs, bp\n"                                                                              \
   "  .if (\\f) < 4 * %[nb]\n"                                                                                      \
-  "    KS_WT ((\\nsx) + (\\f)), (\\nsx), 1, 0\n"                                                                   \
-  "    KS_KM2 ((\\f) / (2 * %[nb])), (((\\f) %% (2 * %[nb])) >> 1), (1 - ((\\f) & 1)), ((\\nsx) + (\\f))\n"       \
+  "    KS_WT ((\\nsx) + (\\f)), (\\nsx), 1, 0, (\\bs)\n"                                                           \
+  "    .if (\\f) < 2 * %[nb]\n"                                                                                    \
+  "      KS_KV ((\\f) / %[nb]), ((\\f) %% %[nb]), 1, ((\\nsx) + (\\f))\n"                                          \
+  "    .else\n"                                                                                                    \
+  "      KS_KV (((\\f) - 2 * %[nb]) / %[nb]), (((\\f) - 2 * %[nb]) %% %[nb]), 0, ((\\nsx) + (\\f))\n"              \
+  "    .endif\n"                                                                                                   \
   "    KS_RD ((\\nsx) + (\\f) + 6), (\\nsx), 1\n"                                                                  \
   "    .if (\\ex) && (%[dh] == 0)\n"                                                                               \
   "      .if (\\f) == 0\n        s_nop 7\n        s_nop 7\n        s_nop 7\n      .endif\n"                        \
   "      KS_EXR (((\\f) * 18) / (4 * %[nb])), ((((\\f) + 1) * 18) / (4 * %[nb]))\n"                                \
   "    .endif\n"                                                                                                   \
+  "    .if ((\\nsx) + (\\f)) == (\\bp)\n      KS_MB 1\n    .endif\n"                                             \
   "  .endif\n"                                                                                                     \
   ".endm\n"                                                                                                        \
-  ".macro KS_SMS nsx, kv, ds, lr\n"                                                                                \
+  ".macro KS_SMS nsx, kv, ds, lr, bs, bp\n"                                                                        \
   KS_SMC(0) KS_SMC(1) KS_SMC(2) KS_SMC(3) KS_SMC(4) KS_SMC(5) KS_SMC(6) KS_SMC(7)                                  \
   KS_SMC(8) KS_SMC(9) KS_SMC(10) KS_SMC(11) KS_SMC(12) KS_SMC(13) KS_SMC(14) KS_SMC(15)                            \
   ".endm\n"                                                                                                        \
-  ".macro KS_KMS nsx, ex\n"                                                                                        \
+  ".macro KS_KMS nsx, ex, bs, bp\n"                                                                                \
   KS_KMC(0) KS_KMC(1) KS_KMC(2) KS_KMC(3) KS_KMC(4) KS_KMC(5) KS_KMC(6) KS_KMC(7)                                  \
   KS_KMC(8) KS_KMC(9) KS_KMC(10) KS_KMC(11) KS_KMC(12) KS_KMC(13) KS_KMC(14) KS_KMC(15)                            \
   ".endm\n"                                                                                                        \
+  /* the middle barrier's position with both chains: after the S wave's first 2 nb - 6 dV MFMAs (so that */     \
+  /* every dK fragment is read after dS), after the dP chain for the dP wave */                                   \
+  ".set ks_bp, (%[ns] - 1 + (1 - %[dh]) * (2 * %[nb] - 6))\n"                                                      \
+  ".set ks_bs, (ks_bp - 1000 * %[dh])\n"                                                                           \
   "s_cmp_eq_u32 %[mode], 7\ns_cbranch_scc1 L_full_%=\n"                                                            \
   "s_cmp_eq_u32 %[mode], 3\ns_cbranch_scc1 L_p12_%=\n"                                                             \
   "s_cmp_eq_u32 %[mode], 5\ns_cbranch_scc1 L_p1e_%=\n"                                                             \
   "s_cmp_eq_u32 %[mode], 1\ns_cbranch_scc1 L_p1_%=\n"                                                              \
   "s_cmp_eq_u32 %[mode], 2\ns_cbranch_scc1 L_p2_%=\n"                                                              \
+  "s_barrier\n"                                                                                                    \
   "s_branch L_end_%=\n"                                                                                            \
   "L_full_%=:\n"                                                                                                   \
-  "KS_XR\nKS_RD6 %[ns], 1\nKS_LR\nKS_SMS %[ns], 1, 1, (4 - 4 * %[dh])\nKS_KMS %[ns], 1\nKS_ST\n"                  \
+  "KS_XR\nKS_RD6 %[ns], 1\nKS_LR\nKS_SMS %[ns], 1, 1, (4 - 4 * %[dh]), ks_bs, ks_bp\n"                             \
+  "KS_KMS %[ns], 1, ks_bs, ks_bp\nKS_ST\n"                                                                         \
   "s_branch L_end_%=\n"                                                                                            \
   "L_p12_%=:\n"                                                                                                    \
-  "KS_XR\nKS_RD6 %[ns], 1\nKS_SMS %[ns], 1, 1, 0\nKS_KMS %[ns], 0\n"                                               \
+  "KS_XR\nKS_RD6 %[ns], 1\nKS_SMS %[ns], 1, 1, 0, ks_bs, ks_bp\nKS_KMS %[ns], 0, ks_bs, ks_bp\n"                   \
   "s_branch L_end_%=\n"                                                                                            \
   "L_p1e_%=:\n"                                                                                                    \
-  "KS_RD6 %[ns], 0\nKS_LR\nKS_SMS %[ns], 0, 0, (4 - 4 * %[dh])\n"                                                  \
+  "KS_RD6 %[ns], 0\nKS_LR\nKS_SMS %[ns], 0, 0, (4 - 4 * %[dh]), -1000, (%[ns] - 1)\n"                              \
   "s_nop 7\ns_nop 7\ns_nop 7\n"                                                                                    \
   "KS_EXR 0, 18\nKS_ST\n"                                                                                          \
   "s_branch L_end_%=\n"                                                                                            \
   "L_p1_%=:\n"                                                                                                     \
-  "KS_RD6 %[ns], 0\nKS_SMS %[ns], 0, 0, 0\n"                                                                       \
+  "KS_RD6 %[ns], 0\nKS_SMS %[ns], 0, 0, 0, -1000, (%[ns] - 1)\n"                                                   \
   "s_branch L_end_%=\n"                                                                                            \
   "L_p2_%=:\n"                                                                                                     \
-  "KS_XR\nKS_RD6 0, 1\nKS_WT2 0, 6, 0, 0\nKS_DSR 0, 16\nKS_KMS 0, 0\n"                                             \
+  "KS_XR\n"                                                                                                        \
+  ".if %[dh] == 1\n  s_waitcnt lgkmcnt(0)\n  KS_DSR 0, 16\n.endif\n"                                               \
+  "KS_MB 1\nKS_RD6 0, 1\nKS_KMS 0, 0, -1000, -1000\n"                                                              \
   "L_end_%=:\n"                                                                                                    \
   "s_waitcnt lgkmcnt(0)\n"                                                                                         \
   "s_nop 7\ns_nop 7\ns_nop 7\n" /* MFMA results may be read by vector instructions next */                         \
   ".purgem KS_WAIT\n.purgem KC_LD\n.purgem KS_XR\n.purgem KS_LR\n.purgem KS_RX\n.purgem KS_TR2\n"                  \
   ".purgem KS_TX\n.purgem KS_RD\n.purgem KS_RD6\n.purgem KS_WT2\n.purgem KS_WT3\n.purgem KS_WT\n"                  \
-  ".purgem KS_DS1\n.purgem KS_DSR\n.purgem KS_EX1\n.purgem KS_EXR\n.purgem KS_ST\n.purgem KS_SM\n"                 \
-  ".purgem KS_MF\n.purgem KS_KM2\n.purgem KS_KM\n.purgem KS_SMS\n.purgem KS_KMS\n"
-
+  ".purgem KS_DS1\n.purgem KS_DSR\n.purgem KS_EX1\n.purgem KS_EXR\n.purgem KS_ST\n.purgem KS_MB\n"                 \
+  ".purgem KS_SM\n.purgem KS_MF\n.purgem KS_KV\n.purgem KS_KM\n.purgem KS_SMS\n.purgem KS_KMS\n"
 #define KV_STEP_IN                                                                                                 \
   [ns] "i"(NS), [nb] "i"(NB), [dh] "i"(DH), [mode] "s"(mode), [r0] "v"(r[0]), [r1] "v"(r[1]), \
                  [r2] "v"(r[2]), [r3] "v"(r[3]), [r4] "v"(r[4]), [r5] "v"(r[5]), [r6] "v"(r[6]), [r7] "v"(r[7]), \
@@ -422,11 +473,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const int n_qtiles = (N + C::kQTile - 1) / C::kQTile;
   const int t_begin = CAUSAL ? k0 / C::kQTile : 0;  // earlier query tiles see none of these keys
   // exchange of tile t in buffer t % 2: [key group][P (bf16x8 [cc][lane]),
-  // dP (fp32x4 [r/4][lane]: each lane's 16 values as four 16-byte runs)];
-  // the lane's entry of buffer xb
+  // dP (fp32x4 [r/4][lane]: each lane's 16 values as four 16-byte runs),
+  // dS (as P)]; the lane's entry of buffer xb
   auto xp = [&](int xb) {
     return (bf16x8 __attribute__((address_space(3)))*)(smem + 3 * C::kSlotBytes + xb * C::kXBytes +
-                                                         kgrp * (C::kXpBytes + C::kXdBytes)) + lane;
+                                                         kgrp * C::kXGroupBytes) + lane;
   };
   auto xlane = [&](int xb) { return lds_addr((const lds_char*)xp(xb)); };
 

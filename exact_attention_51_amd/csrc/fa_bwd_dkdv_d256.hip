@@ -26,7 +26,7 @@
 // formed once, by the dP wave from the P the S wave published the step
 // before, and reaches the S wave through the exchange across a barrier in
 // the middle of the step.  Query tiles live two steps (a 3-slot ring) and
-// the exchange is double-buffered.
+// the exchange is triple-buffered (by tile, as the ring).
 //
 // Layouts are those of the general kernel (fa_bwd.hip): S = Q K^T and
 // dP = dO V^T put a key in every lane column and 16 queries in its
@@ -57,20 +57,19 @@ struct KvDsplitCfg {
   static constexpr int kSlotBytes = 2 * kTileBytes + 2 * kStatBytes;  // Q, dO, L, delta of one tile
   static constexpr int kXGroupBytes = kXpBytes + kXdBytes + kXsBytes;  // one key group
   static constexpr int kXBytes = 2 * kXGroupBytes;                     // both key groups
-  static constexpr int kLdsBytes = 3 * kSlotBytes + 2 * kXBytes;
+  static constexpr int kLdsBytes = 3 * kSlotBytes + 3 * kXBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 };
 
 // The next query tile's copy, issued from inside the step (one load after
-// each of its first 8 MFMAs): 4 loads of Q rows, then 4 of dO rows, from the
-// tiles' global bases qg, og to LDS lq, lo + 1024 i at the copier's lane
-// offsets; exec = 0 leaves them out.  Issued in one burst after the step's
-// barrier, the 8 loads of 1 KB stalled the wave for about 500 cycles while
-// the vector memory path drained them.
+// each of its first 8 MFMAs): 4 loads of Q rows, then 4 of dO rows, from
+// global bases qg, og plus the lane's byte offsets off[i] to LDS lq, lo +
+// 1024 i.  Issued in one burst after the step's barrier, the 8 loads of 1 KB
+// stalled the wave for about 500 cycles while the vector memory path
+// drained them.
 struct KvCopy {
   uint64_t qg, og;
   uint32_t lq, lo;
-  uint64_t exec;
   uint32_t off[4];
 };
 
@@ -122,11 +121,13 @@ struct KvCopy {
   KS_LGK(12) KS_LGK(13) KS_LGK(14)                                                                                 \
   "  .endif\n"                                                                                                     \
   ".endm\n"                                                                                                        \
-  /* copy load n: Q rows (n < 4) or dO rows, load n mod 4 of the wave's share */                                  \
-  ".macro KC_LD n\n"                                                                                               \
+  /* copy load n: Q rows (n < 4) or dO rows, load n mod 4 of the wave's share; M0 is set one */                \
+  /* instruction ahead (a DMA load may not read M0 right after its write) */                                      \
+  ".macro KC_M0 n\n"                                                                                               \
   "  .if ((\\n) >> 2) == 0\n    s_add_u32 m0, %[lq], ((\\n) & 3) * 1024\n"                                        \
   "  .else\n    s_add_u32 m0, %[lo], ((\\n) & 3) * 1024\n  .endif\n"                                              \
-  "  s_mov_b64 exec, %[cx]\n"                                                                                      \
+  ".endm\n"                                                                                                        \
+  ".macro KC_LD n\n"                                                                                               \
   "  .if (\\n) == 0\n    global_load_lds_dwordx4 %[o0], %[qg]\n"                                                   \
   "  .elseif (\\n) == 1\n    global_load_lds_dwordx4 %[o1], %[qg]\n"                                               \
   "  .elseif (\\n) == 2\n    global_load_lds_dwordx4 %[o2], %[qg]\n"                                               \
@@ -135,7 +136,6 @@ struct KvCopy {
   "  .elseif (\\n) == 5\n    global_load_lds_dwordx4 %[o1], %[og]\n"                                               \
   "  .elseif (\\n) == 6\n    global_load_lds_dwordx4 %[o2], %[og]\n"                                               \
   "  .else\n    global_load_lds_dwordx4 %[o3], %[og]\n  .endif\n"                                                 \
-  "  s_mov_b64 exec, -1\n"                                                                                         \
   ".endm\n"                                                                                                        \
   /* tile t-1's P; for the dP wave also its dP and delta */                                                       \
   ".macro KS_XR\n"                                                                                                 \
@@ -298,6 +298,7 @@ struct KvCopy {
   "      v_mfma_f32_32x32x16_bf16 v[152:167], v[232 + ((\\m) %% 6) * 4 : 235 + ((\\m) %% 6) * 4], "                \
   "a[(\\m) * 4 : (\\m) * 4 + 3], v[152:167]\n"                                                                     \
   "    .endif\n"                                                                                                   \
+  "    .if (\\m) < 8\n      KC_M0 (\\m)\n    .endif\n"                                                           \
   "    KS_RD ((\\m) + 6), (\\nsx), (\\kv)\n"                                                                       \
   "    .if (\\m) < 8\n      KC_LD (\\m)\n    .endif\n"                                                           \
   "    .if (\\ds) && (%[dh] == 1)\n"                                                                               \
@@ -372,15 +373,14 @@ struct KvCopy {
   "s_branch L_end_%=\n"                                                                                            \
   "L_p1_%=:\n"                                                                                                     \
   "KS_RD6 %[ns], 0\nKS_SMS %[ns], 0, 0, 0, -1000, (%[ns] - 1)\n"                                                   \
+  "s_nop 7\ns_nop 7\ns_nop 7\n" /* S may be read by vector instructions next */                                  \
   "s_branch L_end_%=\n"                                                                                            \
   "L_p2_%=:\n"                                                                                                     \
   "KS_XR\n"                                                                                                        \
   ".if %[dh] == 1\n  s_waitcnt lgkmcnt(0)\n  KS_DSR 0, 16\n.endif\n"                                               \
   "KS_MB 1\nKS_RD6 0, 1\nKS_KMS 0, 0, -1000, -1000\n"                                                              \
   "L_end_%=:\n"                                                                                                    \
-  "s_waitcnt lgkmcnt(0)\n"                                                                                         \
-  "s_nop 7\ns_nop 7\ns_nop 7\n" /* MFMA results may be read by vector instructions next */                         \
-  ".purgem KS_WAIT\n.purgem KC_LD\n.purgem KS_XR\n.purgem KS_LR\n.purgem KS_RX\n.purgem KS_TR2\n"                  \
+  ".purgem KS_WAIT\n.purgem KC_M0\n.purgem KC_LD\n.purgem KS_XR\n.purgem KS_LR\n.purgem KS_RX\n.purgem KS_TR2\n"                  \
   ".purgem KS_TX\n.purgem KS_RD\n.purgem KS_RD6\n.purgem KS_WT2\n.purgem KS_WT3\n.purgem KS_WT\n"                  \
   ".purgem KS_DS1\n.purgem KS_DSR\n.purgem KS_EX1\n.purgem KS_EXR\n.purgem KS_ST\n.purgem KS_MB\n"                 \
   ".purgem KS_SM\n.purgem KS_MF\n.purgem KS_KV\n.purgem KS_KM\n.purgem KS_SMS\n.purgem KS_KMS\n"
@@ -390,11 +390,11 @@ struct KvCopy {
                  [ta0] "v"(ta[0]), [ta1] "v"(ta[1]), [ta2] "v"(ta[2]), [ta3] "v"(ta[3]), [tb0] "v"(tb[0]), \
                  [tb1] "v"(tb[1]), [tb2] "v"(tb[2]), [tb3] "v"(tb[3]), [xpr] "v"(xpr), [xpw] "v"(xpw), [dlr] "v"(dlr), \
                  [llr] "v"(llr), [c] "v"(c), [qg] "s"(cp.qg), [og] "s"(cp.og), [lq] "s"(cp.lq), [lo] "s"(cp.lo), \
-                 [cx] "s"(cp.exec), [o0] "v"(cp.off[0]), [o1] "v"(cp.off[1]), [o2] "v"(cp.off[2]), \
+                 [o0] "v"(cp.off[0]), [o1] "v"(cp.off[1]), [o2] "v"(cp.off[2]), \
                  [o3] "v"(cp.off[3]), "{a[0:15]}"(kvg[0]), "{a[16:31]}"(kvg[1]), "{a[32:47]}"(kvg[2]), \
                  "{a[48:63]}"(kvg[3])
 #define KV_STEP_CLOB                                                                                               \
-  "memory", "scc", "m0", "exec", "v148", "v149", "v168", "v169", "v170", "v171", "v172", "v173", "v174", \
+  "memory", "scc", "m0", "v148", "v149", "v168", "v169", "v170", "v171", "v172", "v173", "v174", \
                  "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", \
                  "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", \
                  "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", \
@@ -472,7 +472,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const bool group_active = wk0 < N;
   const int n_qtiles = (N + C::kQTile - 1) / C::kQTile;
   const int t_begin = CAUSAL ? k0 / C::kQTile : 0;  // earlier query tiles see none of these keys
-  // exchange of tile t in buffer t % 2: [key group][P (bf16x8 [cc][lane]),
+  // exchange of tile t in buffer t % 3: [key group][P (bf16x8 [cc][lane]),
   // dP (fp32x4 [r/4][lane]: each lane's 16 values as four 16-byte runs),
   // dS (as P)]; the lane's entry of buffer xb
   auto xp = [&](int xb) {
@@ -512,8 +512,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   int roff[8];
 #pragma unroll
   for (int ds = 0; ds < 8; ++ds) roff[ds] = lds_off_bytes<DP>(l32, ds * 2 + half);
-  // does key group kgrp see any query of tile t?
-  auto tile_work = [&](int t) { return group_active && !(CAUSAL && t * C::kQTile + C::kQTile - 1 < wk0); };
 
   // The two output halves run separate instances of the loop, each with one
   // step site, so that the accumulators stay in their registers throughout.
@@ -555,6 +553,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       const int dcol0 = HB * 32 + (g & 1) * 16 + (j16 & 3) * 4;
       trd2 = lds_off_bytes<DP>(r1 + 8, dcol0 >> 3) - lds_off_bytes<DP>(r1, dcol0 >> 3);
     }
+    // the LDS addresses of a step, fixed per ring slot (the loop runs the
+    // slots as three step sites): the row fragments of tile t in slot sl, the
+    // transposed reads, delta and exchange entry of tile t-1 in slot (sl+2)%3
+    int ra[3][8], ta[3][4], tb[3][4], xa[3], dla[3], lla[3];
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl) {
+      const int rbase = lds_addr(DH == 0 ? qbuf(sl) : obuf(sl)), tbase = lds_addr(qbuf(sl));
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) ra[sl][ds] = rbase + roff[ds];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ta[sl][i] = tbase + troff[i];
+        tb[sl][i] = ta[sl][i] + trd2;
+      }
+      xa[sl] = xlane(sl);
+      dla[sl] = lds_addr(dbuf(sl)) + 16 * half;
+      lla[sl] = lds_addr(lbuf(sl)) + 16 * half;
+    }
+    // (through an empty asm, so that they are kept rather than rebuilt from
+    // the offsets on every step)
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl) {
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) asm volatile("" : "+v"(ra[sl][ds]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(ta[sl][i]), "+v"(tb[sl][i]));
+      asm volatile("" : "+v"(xa[sl]), "+v"(dla[sl]), "+v"(lla[sl]));
+    }
+    // the step's work as thresholds on t: tile t is this key group's from
+    // tile tw0 on (its first key's row under causal masking); P needs the mask
+    // on the causal tile tw0 and from the ragged tile nfull on
+    const int tw0 = !group_active ? n_qtiles + 1 : CAUSAL ? wk0 / C::kQTile : 0;
+    const int nfull = N / C::kQTile;
     // this wave's half of dV^T (acc[0..NB-1]) and dK^T (acc[4..4+NB-1])
     f32x16 acc[8];
 #pragma unroll
@@ -562,59 +593,52 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    for (int t = t_begin; t <= n_qtiles; ++t) {
-      // publishes tile t (loaded last step) and the exchange of tile t-1
-      wait_vmcnt<0>();
-      __syncthreads();
-      // (t through an empty asm: a first step told apart from the rest by the
-      // compiler was peeled off the loop, and with two step sites the
-      // accumulators were moved out of their registers and back every step)
-      int tt = t;
-      asm volatile("" : "+s"(tt));
-      const bool part1 = t < n_qtiles && tile_work(t);
-      const bool part2 = tt > t_begin && tile_work(tt - 1);
+    // step t (tile t in slot SL = t % 3): S or dP of tile t, dS/dV/dK of tile
+    // t-1; steps outside t_begin .. n_qtiles only pass the barriers
+    auto step = [&](int t, auto slc) {
+      constexpr int SL = decltype(slc)::value, SP = (SL + 2) % 3, SN = (SL + 1) % 3;
+      // publishes tile t (loaded last step) and the exchange of tile t-1; the
+      // step's own LDS stores may still be in flight here
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const bool part1 = t >= tw0 && t < n_qtiles;
+      const bool part2 = t > tw0 && t <= n_qtiles;
       // tile t+1 into the slot of tile t-2, finished last step: its Q and dO
-      // rows from inside the step's first chain (a whole tile and a chain to
-      // run), else here
-      KvCopy kc = {0, 0, 0, 0, 0, {cp.off[0], cp.off[1], cp.off[2], cp.off[3]}};
-      if (t + 1 < n_qtiles) {
-        const int sl1 = (t + 1) % 3, row1 = (t + 1) * C::kQTile;
-        if (part1 && row1 + C::kQTile <= N) {
-          kc.qg = (uint64_t)(uintptr_t)(Q + (size_t)row1 * D);
-          kc.og = (uint64_t)(uintptr_t)(dO + (size_t)row1 * D);
-          kc.lq = (uint32_t)(uintptr_t)qbuf(sl1) + cp.lds_wave;
-          kc.lo = (uint32_t)(uintptr_t)obuf(sl1) + cp.lds_wave;
-          kc.exec = ~0ull;
-        } else {
-          load_rows(t + 1);
+      // rows from inside the step's first chain (when it has one), else here.
+      // From inside the chain a tile reaching past row N-1 takes rows clamped
+      // onto it, and a step with no next tile copies such rows into the free
+      // slot.
+      const int row1 = (t + 1) * C::kQTile;
+      KvCopy kc = {(uint64_t)(uintptr_t)(Q + (size_t)row1 * D), (uint64_t)(uintptr_t)(dO + (size_t)row1 * D),
+                   (uint32_t)(uintptr_t)qbuf(SN) + cp.lds_wave, (uint32_t)(uintptr_t)obuf(SN) + cp.lds_wave,
+                   {cp.off[0], cp.off[1], cp.off[2], cp.off[3]}};
+      if (part1) {
+        if (row1 + C::kQTile > N) {
+          kc.qg = (uint64_t)(uintptr_t)Q;
+          kc.og = (uint64_t)(uintptr_t)dO;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rc = min(row1 + cp.rowi[i], N - 1);
+            kc.off[i] = cp.off[i] + (uint32_t)((rc - cp.rowi[i]) * (D * 2));
+          }
         }
-        load_stats(t + 1);
+      } else if (t >= t_begin && t + 1 < n_qtiles) {
+        load_rows(t + 1);
       }
-      const int sl = t % 3, slp = (t + 2) % 3, tq0 = t * C::kQTile;
+      if (t >= t_begin && t + 1 < n_qtiles) load_stats(t + 1);
+      const int tq0 = t * C::kQTile;
       // P of a tile that crosses the diagonal or the end of the sequence
       // needs the mask: computed after the step from the returned S
-      const bool masked = DH == 0 && ((CAUSAL && tq0 < wk0 + 31) || (tq0 + C::kQTile > N));
+      const bool masked = DH == 0 && ((CAUSAL && t == tw0) || t >= nfull);
       const int mode =
           __builtin_amdgcn_readfirstlane((part1 ? 1 : 0) | (part2 ? 2 : 0) | (part1 && !masked ? 4 : 0));
-      int r[8], ta[4], tb[4];
-      const int rbase = lds_addr(DH == 0 ? qbuf(sl) : obuf(sl)), tbase = lds_addr(qbuf(slp));
-#pragma unroll
-      for (int ds = 0; ds < 8; ++ds) r[ds] = rbase + roff[ds];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ta[i] = tbase + troff[i];
-        tb[i] = ta[i] + trd2;
-      }
-      const int xpw = xlane(t & 1), xpr = xlane((t + 1) & 1);
-      const int dlr = lds_addr(dbuf(slp)) + 16 * half, llr = lds_addr(lbuf(sl)) + 16 * half;
       f32x16 mine;
-      kv_step<kDSteps, NB, DH>(mode, r, ta, tb, xpr, xpw, dlr, llr, c, kc, kvg, mine, acc);
+      kv_step<kDSteps, NB, DH>(mode, ra[SL], ta[SP], tb[SP], xa[SP], xa[SL], dla[SP], lla[SL], c, kc, kvg, mine, acc);
       if (DH == 0 && part1 && masked) {
         // P = exp(S - L) with the mask; queries of register r: (r/4)*8 + half*4 + r%4
         float lq[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *(const f32x4 __attribute__((address_space(3)))*)(lbuf(sl) + 4 * (g * 8 + half * 4));
+          const f32x4 l4 = *(const f32x4 __attribute__((address_space(3)))*)(lbuf(SL) + 4 * (g * 8 + half * 4));
 #pragma unroll
           for (int i = 0; i < 4; ++i) lq[g * 4 + i] = l4[i];
         }
@@ -632,11 +656,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
           bf16x2 pp[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) pp[i] = pack_bf16(mine[cc * 8 + 2 * i], mine[cc * 8 + 2 * i + 1]);
-          xp(t & 1)[cc * 64] = join8(pp[0], pp[1], pp[2], pp[3]);
+          xp(SL)[cc * 64] = join8(pp[0], pp[1], pp[2], pp[3]);
         }
       }
+    };
+    // (t0 through an empty asm: a first step told apart from the rest by the
+    // compiler was peeled off the loop, and with more step sites the
+    // accumulators were moved out of their registers and back every step)
+    for (int t0 = t_begin - t_begin % 3; t0 <= n_qtiles; t0 += 3) {
+      int tt = t0;
+      asm volatile("" : "+s"(tt));
+      step(tt, std::integral_constant<int, 0>());
+      step(tt + 1, std::integral_constant<int, 1>());
+      step(tt + 2, std::integral_constant<int, 2>());
     }
 
+    // the last MFMAs' results are read next
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     wait_vmcnt<0>();  // no direct-to-LDS copy may outlive the workgroup
     if (!group_active || key >= N) return;
     __bf16* __restrict__ dK = (__bf16*)a.dk + head_off;

@@ -22,9 +22,13 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace fwd
 
+int launch_fwd_d256(const FwdArgs& a, hipStream_t stream);  // fa_fwd_d256.hip
+
 // D = 256, and D = 160 with the same workgroup shape and LDS layout (96
-// columns of each LDS row unused).
+// columns of each LDS row unused).  Without causal masking and from N = 64
+// on, D = 256 runs the kernel with the assembly key loop (fa_fwd_d256.hip).
 int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream) {
+  if (a.D == 256 && !a.causal && a.N >= 64) return launch_fwd_d256(a, stream);
   if (a.D == 160) return a.causal ? fwd::launch<160, true, 1, 4>(a, stream) : fwd::launch<160, false, 1, 4>(a, stream);
   return a.causal ? fwd::launch<256, true, 1, 4>(a, stream) : fwd::launch<256, false, 1, 4>(a, stream);
 }

@@ -169,9 +169,10 @@ typedef __attribute__((ext_vector_type(16))) int i32x16;
     .endr
   .endm
   // score MFMA m of the tile in K slot ks into score set sd (B: Q^T from
-  // AGPRs), the read six positions ahead, K copy m of the tile two ahead
-  // (into K slot ks^1), and the softmax slots of the tile in set se
-  .macro FD_SM m, sd, se, ks, vs
+  // AGPRs), the read six positions ahead, copy m of the tile two ahead (K
+  // into K slot ks^1 for m < 8, then V into V slot vd: the step after waits
+  // for the K copies only), and the softmax slots of the tile in set se
+  .macro FD_SM m, sd, se, ks, vs, vd
     FD_WT (\m), 16
     .if (\m) == 0
       v_mfma_f32_32x32x16_bf16 v[16*(\sd):16*(\sd)+15], v[40+((\m)%%6)*4:43+((\m)%%6)*4], a[128+4*(\m):131+4*(\m)], 0
@@ -180,10 +181,14 @@ typedef __attribute__((ext_vector_type(16))) int i32x16;
     .endif
     .if (\m) < 8
       s_add_u32 m0, s77, ((\ks)^1)*32768+(\m)*1024
+    .else
+      s_add_u32 m0, s78, (\vd)*32768+((\m)-8)*1024
     .endif
     FD_RD ((\m)+6), 16, (\ks), (\vs)
     .if (\m) < 8
       global_load_lds_dwordx4 v[112+(\m)], s[86:87]
+    .else
+      global_load_lds_dwordx4 v[112+(\m)-8], s[88:89]
     .endif
     FD_EXR (((\m)*19)/16), ((((\m)+1)*19)/16), (\se)
   .endm
@@ -236,12 +241,12 @@ typedef __attribute__((ext_vector_type(16))) int i32x16;
     s_addc_u32 s89, s73, 0
     FD_RD6 16, ((\j)^1), \u
     .irp m, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15
-      FD_SM \m, ((\j)^1), \j, ((\j)^1), \u
+      FD_SM \m, ((\j)^1), \j, ((\j)^1), \u, (((\u)+2)%%3)
     .endr
     FD_CHECK \j, r\j\u, \uid
     v_add_f32 v82, v82, v83
     .irp f, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15
-      FD_PM \f, 16, \u, (((\u)+2)%%3), 1
+      FD_PM \f, 16, \u, 0, 0
     .endr
     // tile p+1 is the ragged last tile: its scores take the mask
     s_add_u32 s82, s74, 1

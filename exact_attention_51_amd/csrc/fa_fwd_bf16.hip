@@ -22,6 +22,7 @@ int launch(const FwdArgs& a, hipStream_t stream) {
 }  // namespace fwd
 
 int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
+int launch_fwd_d64(const FwdArgs& a, hipStream_t stream);  // fa_fwd_d64.hip
 
 // Query blocks of 32 rows per wave, and waves per workgroup by head
 // dimension: at D = 128 one 8-wave workgroup per CU (two waves per SIMD;
@@ -36,16 +37,20 @@ int launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t stream);
 // non-causal grids of 256..511 blocks lose (B=1 H=8 N=8192: 263 -> 310 us).
 int launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   constexpr int QB = 1, W64 = 4, W128 = 8;
-  if (a.D == 128 || a.D == 96) {
+  if (a.D == 128 || a.D == 96 || a.D == 64) {
     const long blocks = (long)((a.N + 255) / 256) * a.B * a.H;
     const int cus = device_cus();
-    if (blocks < cus || (a.causal && blocks < 2 * cus)) {
+    const bool small = blocks < cus || (a.causal && blocks < 2 * cus);
+    if (a.D == 64) {
+      if (!small && a.N >= 64) return launch_fwd_d64(a, stream);  // 64 rows per wave, assembly key loop
+      return a.causal ? fwd::launch<64, true, QB, W64>(a, stream) : fwd::launch<64, false, QB, W64>(a, stream);
+    }
+    if (small) {
       if (a.D == 128)
         return a.causal ? fwd::launch<128, true, QB, 4>(a, stream) : fwd::launch<128, false, QB, 4>(a, stream);
       return a.causal ? fwd::launch<96, true, QB, 4>(a, stream) : fwd::launch<96, false, QB, 4>(a, stream);
     }
   }
-  if (a.D == 64) return a.causal ? fwd::launch<64, true, QB, W64>(a, stream) : fwd::launch<64, false, QB, W64>(a, stream);
   if (a.D == 32)  // the D = 64 workgroup shape and LDS layout, 32 columns unused
     return a.causal ? fwd::launch<32, true, QB, W64>(a, stream) : fwd::launch<32, false, QB, W64>(a, stream);
   if (a.D == 128) {

@@ -130,15 +130,30 @@ def test_forward_bf16_many_heads(D, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", [(3, 37, 1000), (2, 20, 3000)])
-def test_forward_d128_persistent_rounds(B, H, N, causal):
-    """D = 128 grids larger than the GPU run one persistent workgroup per
-    compute unit, which carries its K/V ring from one 256-row block into the
-    next.  Both shapes take a full round of blocks and a partial one, with a
-    ragged last key tile: 111 heads of N = 1000 (444 blocks; heads not a
-    multiple of the eight XCDs, so no per-XCD head groups) and 40 heads of
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_persistent_rounds(D, B, H, N, causal):
+    """D = 64 and 128 grids larger than the GPU run one persistent workgroup
+    per compute unit, which carries its K/V ring from one 256-row block into
+    the next.  Both shapes take a full round of blocks and a partial one,
+    with a ragged last key tile: 111 heads of N = 1000 (444 blocks; heads not
+    a multiple of the eight XCDs, so no per-XCD head groups) and 40 heads of
     N = 3000 (480 blocks, 5 heads per XCD, blocks of 4 to 47 key tiles)."""
-    w = WORKLOADS["c3"].with_(name="rounds", B=B, H=H, N=N, D=128, causal=causal, seed=N + H)
-    log(f"test_forward_d128_persistent_rounds B={B} H={H} N={N} causal={causal}")
+    w = WORKLOADS["c3"].with_(name="rounds", B=B, H=H, N=N, D=D, causal=causal, seed=N + H + D)
+    log(f"test_forward_persistent_rounds D={D} B={B} H={H} N={N} causal={causal}")
+    x = make_inputs(w, with_do=False)
+    o, lse = _run(w, x)
+    _check_full(w, x, o, lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [64, 130, 200])
+def test_forward_d64_short_many_heads(N, causal):
+    """520 heads of N < 256: one 256-row block per head, enough blocks for
+    the D = 64 assembly kernel (also under the causal mask), too short for
+    its persistent walk: one block per workgroup, 1 to 4 key tiles, a ragged
+    last tile at 130 and 200."""
+    w = WORKLOADS["c2"].with_(name="short", B=2, H=260, N=N, D=64, causal=causal, seed=N + 7)
+    log(f"test_forward_d64_short_many_heads N={N} causal={causal}")
     x = make_inputs(w, with_do=False)
     o, lse = _run(w, x)
     _check_full(w, x, o, lse)
@@ -194,19 +209,20 @@ def test_forward_growing_scores(D, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_d128_persistent_growing_scores(causal):
-    """The growing-score inputs above on a D = 128 grid large enough to run
-    persistently (260 heads of N = 512: 520 blocks), so the out-of-line
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_persistent_growing_scores(D, causal):
+    """The growing-score inputs above on a D = 64 or 128 grid large enough to
+    run persistently (260 heads of N = 512: 520 blocks), so the out-of-line
     rescale path runs in blocks that took their first K/V tiles from the
     ring of the block before."""
     from fa_inputs import Inputs, bf16_round
 
-    n, h, D = 512, 260, 128
-    rng = np.random.default_rng(97)
+    n, h = 512, 260
+    rng = np.random.default_rng(97 + D)
     scale = 1.0 / np.sqrt(D)
     for growth in (30.0, 200.0):
         for rising in (True, False):
-            log(f"test_forward_d128_persistent_growing_scores causal={causal} growth={growth} rising={rising}")
+            log(f"test_forward_persistent_growing_scores D={D} causal={causal} growth={growth} rising={rising}")
             q = 0.1 * rng.standard_normal((1, h, n, D)).astype(np.float32)
             q[..., 0] = 1.0
             k = 0.1 * rng.standard_normal((1, h, n, D)).astype(np.float32)

@@ -32,8 +32,6 @@
 //   v[0:63], v[64:127]   score sets: tile q in set q mod 2, block (kb, qb)
 //                        at set*64 + (kb*2 + qb)*16; exponentials in place
 //   v[128:159]           P (bf16 pairs), (qb, kb, cc) at 128 + ((qb*2 + kb)*2 + cc)*4
-//   v[160:175]           4 K-fragment buffers
-//   v[176:191]           4 V-fragment buffers
 //   v192, v193; v194, v195  running max m; row sum l (per 32-row block)
 //   v196, v197           this tile's row sums;  v198, v199  -m*c per block
 //   v[200:203]           per-lane K fragment LDS addresses (one per k-step)
@@ -45,6 +43,10 @@
 //   a[0:63]              O^T accumulators, block (qb, db) at (qb*2 + db)*16
 //   a[64:95]             Q^T fragments, (qb, ds) at 64 + (qb*4 + ds)*4
 //   a[96:103]            row-sum accumulators, block qb at 96 + qb*4
+//   a[104:135]           the eight K fragments of a tile (read during the P V
+//                        half, used by the next score half)
+//   a[136:167]           the eight V fragments of a tile (read at the end of
+//                        the score half, used by the next step's P V half)
 //   s[70:71]             K of the head;  s74 position p;  s75 tiles;
 //   s76 masked tiles R;  s77 first masked tile;  s78 last tile byte offset;
 //   s79 scale*log2(e);  s80 LDS ring base + this wave's copy offset;  s81 wave;
@@ -116,15 +118,15 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
   // query block qb = k mod 2) into set n
   .macro FA_SMFMA k, n
     .if (((\k)>>2) == 0)
-      v_mfma_f32_32x32x16_bf16 v[(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16:(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16+15], v[160+(((\k)>>1)&3)*4:163+(((\k)>>1)&3)*4], a[64+(((\k)&1)*4+((\k)>>2))*4:67+(((\k)&1)*4+((\k)>>2))*4], 0
+      v_mfma_f32_32x32x16_bf16 v[(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16:(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16+15], a[104+((\k)>>1)*4:107+((\k)>>1)*4], a[64+(((\k)&1)*4+((\k)>>2))*4:67+(((\k)&1)*4+((\k)>>2))*4], 0
     .else
-      v_mfma_f32_32x32x16_bf16 v[(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16:(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16+15], v[160+(((\k)>>1)&3)*4:163+(((\k)>>1)&3)*4], a[64+(((\k)&1)*4+((\k)>>2))*4:67+(((\k)&1)*4+((\k)>>2))*4], v[(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16:(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16+15]
+      v_mfma_f32_32x32x16_bf16 v[(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16:(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16+15], a[104+((\k)>>1)*4:107+((\k)>>1)*4], a[64+(((\k)&1)*4+((\k)>>2))*4:67+(((\k)&1)*4+((\k)>>2))*4], v[(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16:(\n)*64+((((\k)>>1)&1)*2+((\k)&1))*16+15]
     .endif
   .endm
   // P V MFMA of V fragment j (16-key chunk kc = j/2, d block db = j mod 2)
   // for query block qb: O(qb, db) += V^T P^T
   .macro FA_PMFMA j, qb
-    v_mfma_f32_32x32x16_bf16 a[(\qb)*32+((\j)&1)*16:(\qb)*32+((\j)&1)*16+15], v[176+((\j)&3)*4:179+((\j)&3)*4], v[128+(\qb)*16+((\j)>>1)*4:131+(\qb)*16+((\j)>>1)*4], a[(\qb)*32+((\j)&1)*16:(\qb)*32+((\j)&1)*16+15]
+    v_mfma_f32_32x32x16_bf16 a[(\qb)*32+((\j)&1)*16:(\qb)*32+((\j)&1)*16+15], a[136+(\j)*4:139+(\j)*4], v[128+(\qb)*16+((\j)>>1)*4:131+(\qb)*16+((\j)>>1)*4], a[(\qb)*32+((\j)&1)*16:(\qb)*32+((\j)&1)*16+15]
   .endm
   // row-sum MFMA of P block b = 2 kb + cc of query block qb (16 keys), on
   // the 16x16x32 shape: B = the P block as it stands (lane group g = lane/16
@@ -139,14 +141,16 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
       v_mfma_f32_16x16x32_bf16 a[96+(\qb)*4:99+(\qb)*4], v[224:227], v[128+(\qb)*16+(\b)*4:131+(\qb)*16+(\b)*4], a[96+(\qb)*4:99+(\qb)*4]
     .endif
   .endm
-  // K fragment i (k-step i/2, key block i mod 2) of ring slot b
+  // K fragment i (k-step i/2, key block i mod 2) of ring slot b, into
+  // buffer i (a whole tile of fragments fits the eight buffers)
   .macro FA_KREAD i, b
-    ds_read_b128 v[160+((\i)&3)*4:163+((\i)&3)*4], v[200+((\i)>>1)] offset:(\b)*8192+((\i)&1)*4096
+    ds_read_b128 a[104+(\i)*4:107+(\i)*4], v[200+((\i)>>1)] offset:(\b)*8192+((\i)&1)*4096
   .endm
-  // V fragment j (keys 16*(j/2) .., d block j mod 2) of ring slot b
+  // V fragment j (keys 16*(j/2) .., d block j mod 2) of ring slot b, into
+  // buffer j
   .macro FA_VREAD j, b
-    ds_read_b64_tr_b16 v[176+((\j)&3)*4:177+((\j)&3)*4], v[208+((\j)&1)*2] offset:(\b)*8192+((\j)>>1)*2048
-    ds_read_b64_tr_b16 v[178+((\j)&3)*4:179+((\j)&3)*4], v[209+((\j)&1)*2] offset:(\b)*8192+((\j)>>1)*2048
+    ds_read_b64_tr_b16 a[136+(\j)*4:137+(\j)*4], v[208+((\j)&1)*2] offset:(\b)*8192+((\j)>>1)*2048
+    ds_read_b64_tr_b16 a[138+(\j)*4:139+(\j)*4], v[209+((\j)&1)*2] offset:(\b)*8192+((\j)>>1)*2048
   .endm
   // byte offset of the tile at sequence position s82 -> s82: masked tiles
   // (positions < R) are tiles first_masked.., the rest tiles 0..; a ragged
@@ -210,21 +214,13 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
     s_addc_u32 s99, s91, 0
     s_branch L_kr_\j\()_\uid
   .endm
-  // score MFMA k of the step: K fragments waited for before each even k and
-  // read three ahead (the first three were read in the P V half; the next
-  // tile's first V reads follow k = 13 and 14, hence the counts at the end)
+  // score MFMA k of the step; the tile's eight K fragments were read
+  // during the P V half and are waited for once, before the first
   .macro FA_SK k, j
-    .if ((\k)&1) == 0
-      .if ((\k)>>1) == 6
-        s_waitcnt lgkmcnt(1)
-      .else
-        s_waitcnt lgkmcnt(2)
-      .endif
+    .if (\k) == 0
+      s_waitcnt lgkmcnt(0)
     .endif
     FA_SMFMA \k, ((\j)&1)
-    .if (((\k)&1) == 1) && (((\k)>>1) <= 4)
-      FA_KREAD (((\k)>>1)+3), (((\j)+2)&3)
-    .endif
   .endm
   // the score-half MFMA at step position t (16..39): row-sum MFMAs at 17, 20,
   // 23, 26, 29, 32, 34, 36 (each two or more positions after the last pack
@@ -300,33 +296,24 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
   // ---- step p (s74), unrolled over the ring: j = p mod 4.  Scores of tile
   // p+1 are in set (j+1) mod 2 (masked), P of tile p in v[128:159].
   .macro FA_STEP j, uid
-    s_waitcnt vmcnt(4)
+    // this tile's V fragments (read at the end of the last step) and this
+    // wave's copies of K(p+2) and V(p+1) have landed
+    s_waitcnt vmcnt(4) lgkmcnt(0)
     s_barrier
-    // P V half: positions 0..15 (each V fragment waited for before its
-    // first MFMA and read three ahead; the first K fragments of tile p+2
-    // after the last three reads)
+    s_add_u32 s86, s74, 2
+    // P V half: positions 0..15; the eight K fragments of tile p+2 are read
+    // at positions 0..7, each right after its MFMA: an LDS or scalar
+    // instruction issued behind a position's vector work stalls the wave
+    // until that work drains
     .irp t, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15
-      .if ((\t)&1) == 0
-        .if ((\t)>>1) <= 5
-          s_waitcnt lgkmcnt(4)
-        .elseif ((\t)>>1) == 6
-          s_waitcnt lgkmcnt(3)
-        .else
-          s_waitcnt lgkmcnt(2)
-        .endif
-      .endif
       FA_PMFMA ((\t)>>1), ((\t)&1)
-      .if (((\t)&1) == 1) && (((\t)>>1) <= 4)
-        FA_VREAD (((\t)>>1)+3), (\j)
+      .if (\t) < 8
+        FA_KREAD \t, (((\j)+2)&3)
       .endif
       FA_VPOS \t, (((\j)+1)&1)
-      .if ((\t) == 11) || ((\t) == 13) || ((\t) == 15)
-        FA_KREAD (((\t)-11)>>1), (((\j)+2)&3)
-      .endif
     .endr
     // score half: positions 16..39 (16 score MFMAs of tile p+2, 8 row sums);
     // past the block's last tile (p+2 >= nt) the variant without scores
-    s_add_u32 s86, s74, 2
     s_cmp_ge_u32 s86, s75
     s_cbranch_scc1 L_ns_\j\()_\uid
     s_cmp_lt_u32 s86, s76
@@ -334,12 +321,12 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
   L_sfull_\j\()_\uid:
     .irp t, 16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31,32,33,34,35,36,37,38,39
       FA_SPOS \t, \j
+      .if (\t) >= 32
+        FA_VREAD ((\t)-32), (((\j)+1)&3)
+      .endif
       FA_VPOS \t, (((\j)+1)&1)
       .if (\t) >= 34
         FA_REFILL ((\t)-34), \j, \uid
-      .endif
-      .if (\t) >= 37
-        FA_VREAD ((\t)-37), (((\j)+1)&3)
       .endif
     .endr
   L_nsret_\j\()_\uid:
@@ -370,7 +357,7 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
   // from K slot (j+1) mod 4 and masked, the running max raised to their row
   // max where it grew by more than 2^8 (exp2 domain) with O and l rescaled,
   // exponentials, P and row sums redone.  The K fragment buffers are idle
-  // at the end of a step.
+  // at the end of a step (the V buffers hold tile p+1's fragments).
   .macro FA_RARE j, uid
   L_rare_\j\()_\uid:
     .irp k, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15
@@ -478,12 +465,12 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
         s_nop 4
         FA_SPOS \t, \j
       .endif
+      .if (\t) >= 32
+        FA_VREAD ((\t)-32), (((\j)+1)&3)
+      .endif
       FA_VPOS \t, (((\j)+1)&1)
       .if (\t) >= 34
         FA_REFILL ((\t)-34), \j, \uid\()n
-      .endif
-      .if (\t) >= 37
-        FA_VREAD ((\t)-37), (((\j)+1)&3)
       .endif
     .endr
     s_nop 7
@@ -520,23 +507,43 @@ static_assert(RowTileCopier<D, D, kBlockN, kWaves>::kLoads == 2, "two copies per
   FA_VREAD 0, 0
   FA_VREAD 1, 0
   FA_VREAD 2, 0
+  FA_VREAD 3, 0
+  FA_VREAD 4, 0
+  FA_VREAD 5, 0
+  FA_VREAD 6, 0
+  FA_VREAD 7, 0
   s_branch L_s0_%=
 L_e1_%=:
   FA_SWAPSETS
   FA_VREAD 0, 1
   FA_VREAD 1, 1
   FA_VREAD 2, 1
+  FA_VREAD 3, 1
+  FA_VREAD 4, 1
+  FA_VREAD 5, 1
+  FA_VREAD 6, 1
+  FA_VREAD 7, 1
   s_branch L_s1_%=
 L_e2_%=:
   FA_VREAD 0, 2
   FA_VREAD 1, 2
   FA_VREAD 2, 2
+  FA_VREAD 3, 2
+  FA_VREAD 4, 2
+  FA_VREAD 5, 2
+  FA_VREAD 6, 2
+  FA_VREAD 7, 2
   s_branch L_s2_%=
 L_e3_%=:
   FA_SWAPSETS
   FA_VREAD 0, 3
   FA_VREAD 1, 3
   FA_VREAD 2, 3
+  FA_VREAD 3, 3
+  FA_VREAD 4, 3
+  FA_VREAD 5, 3
+  FA_VREAD 6, 3
+  FA_VREAD 7, 3
   s_branch L_s3_%=
 L_s0_%=:
   FA_STEP 0, %=
@@ -798,8 +805,7 @@ fwd_d64_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
     scores((r0 + 1) & 3, 1, s1);
 
     f32x32 o0, o1;          // O^T: a[0:31] (qb 0, db 0-1), a[32:63] (qb 1)
-    f32x32 junk0, junk1;    // registers the loop uses internally
-    f32x16 junk2, junk3;
+    f32x32 junk0, junk1, junk2, junk3;  // registers the loop uses internally
     f32x4 junk4;
     f32x8 junk5;
     // scalar operands of the loop, pinned to SGPRs (all are wave-uniform)
@@ -834,8 +840,7 @@ fwd_d64_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
                    "+{v[140:143]}"(p0[0][1][1]), "+{v[144:147]}"(p0[1][0][0]), "+{v[148:151]}"(p0[1][0][1]),
                    "+{v[152:155]}"(p0[1][1][0]), "+{v[156:159]}"(p0[1][1][1]), "+{v192}"(m[0]), "+{v193}"(m[1]),
                    "+{v194}"(l[0]), "+{v195}"(l[1]), "+{s74}"(p), "+{s[98:99]}"(k_addr), "=&{v[32:63]}"(junk1),
-                   "=&{v[160:175]}"(junk2),
-                   "=&{v[176:191]}"(junk3), "=&{v[196:199]}"(junk4), "=&{a[96:103]}"(junk5)
+                   "=&{a[104:135]}"(junk2), "=&{a[136:167]}"(junk3), "=&{v[196:199]}"(junk4), "=&{a[96:103]}"(junk5)
                  : "{a[64:67]}"(qf[0][0]), "{a[68:71]}"(qf[0][1]), "{a[72:75]}"(qf[0][2]), "{a[76:79]}"(qf[0][3]),
                    "{a[80:83]}"(qf[1][0]), "{a[84:87]}"(qf[1][1]), "{a[88:91]}"(qf[1][2]), "{a[92:95]}"(qf[1][3]),
                    "{v[200:203]}"(koff), "{v[208:211]}"(voff), "{v[216:217]}"(cpoff), "{v220}"(bound0),

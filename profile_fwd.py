@@ -78,8 +78,8 @@ def _flop(name):
 
 # (the kernel regex is a plain name: each workload runs one instance of it)
 KERNEL_SETS = [
-    ("c2 forward, D=64 (B=4 H=16 N=2048)", "c2_fwd", "fwd_bf16_kernel", "fa_fwd_bf16.hip",
-     "fwd_bf16_kernelILi64ELb0ELi1ELi4ELb0ELb0ELb0E", lambda: _flop("c2").fwd_flop()),
+    ("c2 forward, D=64 (B=4 H=16 N=2048)", "c2_fwd", "fwd_d64_kernel", "fa_fwd_d64.hip",
+     "fwd_d64_kernelILb0E", lambda: _flop("c2").fwd_flop()),
     ("c5 forward, D=256 (B=1 H=4 N=4096)", "c5_fwd", "fwd_d256_kernel", "fa_fwd_d256.hip",
      "fwd_d256_kernel", lambda: _flop("c5").fwd_flop()),
     ("c5 backward dQ, D=256", "c5_bwd", "bwd_dq_kernel", "fa_bwd.hip", "bwd_dq_kernelILi256ELb0E",
@@ -389,7 +389,7 @@ def summarize_all_workloads(out: str, dest: str) -> None:
                 label, seen_c3_bwd = "c3 bwd", True
         elif any(f"fwd_bf16_kernel<{d}," in family for d in (32, 96, 160)):
             label = next(f"d{d} fwd" for d in (32, 96, 160) if f"fwd_bf16_kernel<{d}," in family)
-        elif "fwd_bf16_kernel<64" in family:
+        elif "fwd_bf16_kernel<64" in family or "fwd_d64_kernel" in family:
             label, seen_c2 = "c2 fwd", True
         elif "fwd_bf16_kernel<256" in family or "fwd_d256_kernel" in family:
             label, seen_c5 = "c5 fwd", True

@@ -103,16 +103,18 @@ def test_forward_kv_peaked_rows(splits):
     _run_and_check(1, 2, 64, 4096, 128, True, splits, seed=4, q_mult=3.0)
 
 
-@pytest.mark.parametrize("D,causal", [(64, False), (128, True), (256, True)])
-def test_forward_kv_unsplit_equals_square_forward(D, causal):
+@pytest.mark.parametrize("D,causal,H", [(64, False, 60), (128, True, 256), (256, True, 256)])
+def test_forward_kv_unsplit_equals_square_forward(D, causal, H):
     """With Nq = Nk and one key range the kernel does the square forward's
-    arithmetic in the same order: the results are bitwise equal.  (Enough
-    heads that the square forward keeps its full-size workgroups: small
-    D = 128 grids take 128-row workgroups, which visit the causal diagonal
-    tiles in another order.)"""
+    arithmetic in the same order: the results are bitwise equal.  (At D =
+    128, enough heads that the square forward keeps its full-size
+    workgroups: small D = 128 grids take 128-row workgroups, which visit the
+    causal diagonal tiles in another order.  At D = 64, a grid smaller than
+    the device: larger ones run the square forward's own D = 64 kernel,
+    whose row sums add the rounded P in another order.)"""
     import torch
 
-    scale, _, qb, _, kb, _, vb = _inputs(2, 256, 300, 300, D, 31)
+    scale, _, qb, _, kb, _, vb = _inputs(2, H, 300, 300, D, 31)
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     o1, l1 = _fa().fwd(q, k, v, scale, causal=causal)
     o2, l2 = _fa().fwd_kv(q, k, v, scale, causal=causal, num_splits=1)

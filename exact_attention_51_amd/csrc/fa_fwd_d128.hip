@@ -32,8 +32,9 @@
 // MFMAs too, on the half-cost 16x16x32 shape (a 0/1 selector times P):
 // plain VALU adds of the rounded values would need an unpack per value, and
 // v_dot2 executes in the matrix pipe.  Ring refills go into MFMA positions
-// with light vector work; the copies of positions past the block's last tile
-// run with no lane active.  After the MFMAs the tile's row sums are checked:
+// with light vector work; a V refill reads the tile its K refill read one
+// step before, so its address is that address moved to the V tensor.  After
+// the MFMAs the tile's row sums are checked:
 // a share above 2^16 (or not finite) takes an out-of-line path that
 // recomputes the tile's scores, raises the running max, rescales
 // O and l and redoes the exponentials.  The prologue (Q rows, scores of
@@ -57,10 +58,13 @@
 //   a[0:127]             O^T accumulators, block (qb, db) at (qb*4 + db)*16
 //   a[128:191]           Q^T fragments, (qb, ds) at 128 + (qb*8 + ds)*4
 //   a[192:199]           row-sum accumulators, block qb at 192 + qb*4
-//   s[70:71], s[72:73]   K and V of the head;  s74 position p;  s75 tiles;
+//   s[70:71]             K of the head;  s74 position p;  s75 tiles;
 //   s76 masked tiles R;  s77 first masked tile;  s78 last tile byte offset;
 //   s79 scale*log2(e);  s80 LDS ring base + this wave's copy offset;  s81 wave;
-//   s82..s89 scalar temporaries
+//   s82..s89 scalar temporaries (s[88:89] this step's V refill address);
+//   s[90:91], s94, s95 the next block's K, R and first masked tile;
+//   s[92:93] the distance from the K tensor to the V tensor;  s97 the ring
+//   slot the block starts in;  s[98:99] the address of the last K refill
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_sched.h"
@@ -161,51 +165,46 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_lshl_b32 s82, s82, 14
     s_min_u32 s82, s82, s78
   .endm
-  // ring refill piece r of step p (slot j = p mod 4): 0 = address of K(p+4),
-  // 1..4 = its four copies into slot j, 5 = address of V(p+3), 6..9 = its
-  // copies into V slot (j+3) mod 4.  A position past the block's last tile
-  // is the next block's tile (position minus nt) when the workgroup has one,
-  // computed out of line; else its copies run with no lane active.
+  // ring refill piece r of step p (slot j = p mod 4): 0 = address of V(p+3),
+  // which is the address K(p+3) was copied from one step before moved by
+  // the distance between the K and V tensors (s[92:93]: heads sit at the
+  // same offset in both), and M0 of its first copy; 1..4 = its four copies
+  // into V slot (j+3) mod 4; 5 = address of K(p+4) into s[98:99]; 6..9 =
+  // its copies into slot j.  M0 is written one piece before the copy that
+  // reads it.  A position past the block's last tile is the next block's
+  // tile (position minus nt), computed out of line; the last block's "next
+  // block" is itself, so every copy reads a valid tile (those past the end
+  // land in ring slots no step reads again).
   .macro FA_REFILL r, j, uid
     .if (\r) == 0
+      s_add_u32 s88, s98, s92
+      s_addc_u32 s89, s99, s93
+      s_add_u32 m0, s80, 65536+((((\j)+3)&3)*16384)
+    .elseif (\r) <= 3
+      global_load_lds_dwordx4 v[216+(\r)-1], s[88:89]
+      s_add_u32 m0, s80, 65536+((((\j)+3)&3)*16384)+(\r)*1024
+    .elseif (\r) == 4
+      global_load_lds_dwordx4 v219, s[88:89]
+      s_add_u32 m0, s80, (\j)*16384
+    .elseif (\r) == 5
       s_add_u32 s82, s74, 4
       s_cmp_lt_u32 s82, s75
       s_cbranch_scc0 L_kn_\j\()_\uid
       FA_TILE_BYTES
-      s_add_u32 s86, s70, s82
-      s_addc_u32 s87, s71, 0
-      s_mov_b64 s[88:89], -1
+      s_add_u32 s98, s70, s82
+      s_addc_u32 s99, s71, 0
     L_kr_\j\()_\uid:
-    .elseif (\r) <= 4
-      s_add_u32 m0, s80, (\j)*16384+((\r)-1)*1024
-      s_mov_b64 exec, s[88:89]
-      global_load_lds_dwordx4 v[216+(\r)-1], s[86:87]
-      s_mov_b64 exec, -1
-    .elseif (\r) == 5
-      s_add_u32 s82, s74, 3
-      s_cmp_lt_u32 s82, s75
-      s_cbranch_scc0 L_vn_\j\()_\uid
-      FA_TILE_BYTES
-      s_add_u32 s86, s72, s82
-      s_addc_u32 s87, s73, 0
-      s_mov_b64 s[88:89], -1
-    L_vr_\j\()_\uid:
+    .elseif (\r) <= 8
+      global_load_lds_dwordx4 v[216+(\r)-6], s[98:99]
+      s_add_u32 m0, s80, (\j)*16384+((\r)-5)*1024
     .else
-      s_add_u32 m0, s80, 65536+((((\j)+3)&3)*16384)+((\r)-6)*1024
-      s_mov_b64 exec, s[88:89]
-      global_load_lds_dwordx4 v[216+(\r)-6], s[86:87]
-      s_mov_b64 exec, -1
+      global_load_lds_dwordx4 v219, s[98:99]
     .endif
   .endm
-  // out of line: the byte offset of the next block's tile at position
-  // s82 - nt (its masked tiles first, as for every block), on the next
-  // block's K (kv = 0) or V (kv = 1); no lane active without a next block
-  .macro FA_RNEXT kv, j, uid
-    .if (\kv) == 0
-    L_kn_\j\()_\uid:
-    .else
-    L_vn_\j\()_\uid:
-    .endif
+  // out of line: the K address of the next block's tile at position
+  // s82 - nt (its masked tiles first, as for every block)
+  .macro FA_RNEXT j, uid
+  L_kn_\j\()_\uid:
     s_sub_u32 s82, s82, s75
     s_add_u32 s83, s82, s95
     s_sub_u32 s84, s82, s94
@@ -213,20 +212,9 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_cselect_b32 s82, s83, s84
     s_lshl_b32 s82, s82, 14
     s_min_u32 s82, s82, s78
-    .if (\kv) == 0
-      s_add_u32 s86, s90, s82
-      s_addc_u32 s87, s91, 0
-    .else
-      s_add_u32 s86, s92, s82
-      s_addc_u32 s87, s93, 0
-    .endif
-    s_cmp_lg_u32 s96, 0
-    s_cselect_b64 s[88:89], -1, 0
-    .if (\kv) == 0
-      s_branch L_kr_\j\()_\uid
-    .else
-      s_branch L_vr_\j\()_\uid
-    .endif
+    s_add_u32 s98, s90, s82
+    s_addc_u32 s99, s91, 0
+    s_branch L_kr_\j\()_\uid
   .endm
   // the score-half MFMA at step position t (32..71): row-sum MFMAs at 32..35,
   // 42, 50, 58, 66 (after the packs they read), score MFMAs k = 0..31 at the
@@ -304,11 +292,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   // ---- step p (s74), unrolled over the ring: j = p mod 4.  Scores of tile
   // p+1 are in set (j+1) mod 2 (masked), P of tile p in v[128:159].
   .macro FA_STEP j, uid
-    s_add_u32 s82, s74, 2
-    s_cmp_ge_u32 s82, s75
-    s_cbranch_scc1 L_wall_\j\()_\uid
     s_waitcnt vmcnt(8)
-  L_wret_\j\()_\uid:
     s_barrier
     v_mul_f32_e64 v198, -v192, s79
     v_mul_f32_e64 v199, -v193, s79
@@ -503,18 +487,6 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_branch L_nsret_\j\()_\uid
   .endm
 
-  // ---- out of line: the last two steps of the workgroup's last block wait
-  // for every copy in flight (copies with no lane active may not count)
-  .macro FA_WALL j, uid
-  L_wall_\j\()_\uid:
-    s_cmp_lg_u32 s96, 0
-    s_cbranch_scc1 L_wnext_\j\()_\uid
-    s_waitcnt vmcnt(0)
-    s_branch L_wret_\j\()_\uid
-  L_wnext_\j\()_\uid:
-    s_waitcnt vmcnt(8)
-    s_branch L_wret_\j\()_\uid
-  .endm
   // score sets swapped on entry at an odd ring slot: tile 1's scores belong
   // in set 0
   .macro FA_SWAPSETS
@@ -575,16 +547,10 @@ L_s3_%=:
   FA_MASK 1, %=
   FA_MASK 2, %=
   FA_MASK 3, %=
-  FA_WALL 0, %=
-  FA_WALL 1, %=
-  FA_WALL 2, %=
-  FA_WALL 3, %=
   .irp jj, 0, 1, 2, 3
     FA_NS \jj, %=
-    FA_RNEXT 0, \jj, %=
-    FA_RNEXT 1, \jj, %=
-    FA_RNEXT 0, \jj, %=n
-    FA_RNEXT 1, \jj, %=n
+    FA_RNEXT \jj, %=
+    FA_RNEXT \jj, %=n
   .endr
 L_done_%=:
   s_waitcnt lgkmcnt(0)
@@ -607,7 +573,6 @@ L_done_%=:
   .purgem FA_STEP
   .purgem FA_RARE
   .purgem FA_MASK
-  .purgem FA_WALL
   .purgem FA_SWAPSETS
   .purgem FA_RNEXT
   .purgem FA_NS
@@ -840,22 +805,27 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
     const int ring_wave = sgpr((int)ring + (int)cp.lds_wave);
     const float cs = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, c)));
     const __bf16* Ks = sgpr_ptr(head((const __bf16*)a.k, cur.bh));
-    const __bf16* Vs = sgpr_ptr(head((const __bf16*)a.v, cur.bh));
     const __bf16* Kn = sgpr_ptr(head((const __bf16*)a.k, nxt.bh));
-    const __bf16* Vn = sgpr_ptr(head((const __bf16*)a.v, nxt.bh));
+    // the address K(3) was copied from (the first V refill reads the same
+    // tile of V), and the distance from the K tensor to the V tensor
+    const __bf16* k_addr =
+        sgpr_ptr((const __bf16*)((const char*)head((const __bf16*)a.k, cur.bh) + tile_bytes(cur, 3)));
+    const int64_t kv_dist = (int64_t)((const char*)a.v - (const char*)a.k);
+    const int64_t kv_s = ((int64_t)sgpr((int)(uint32_t)((uint64_t)kv_dist >> 32)) << 32) |
+                         (int64_t)(uint32_t)sgpr((int)(uint32_t)(uint64_t)kv_dist);
     const int nt_s = sgpr(cur.nt), R_s = sgpr(cur.R), fm_s = sgpr(cur.fm);
     // the diagonal tile at position i (i < R under causal masking) is fully
     // masked for the rows of waves below i
     const int wave_s = sgpr(CAUSAL ? wave : 1 << 30);
     const int ltb_s = sgpr((int)last_tile_bytes);
-    const int Rn_s = sgpr(nxt.R), fmn_s = sgpr(nxt.fm), next_s = sgpr(has_next ? 1 : 0), r0_s = sgpr(r0);
+    const int Rn_s = sgpr(nxt.R), fmn_s = sgpr(nxt.fm), r0_s = sgpr(r0);
     asm volatile(FA_D128_LOOP_ASM
                  : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
                    "=&{v[0:31]}"(junk0), "+{v[64:79]}"(s1[0][0]), "+{v[80:95]}"(s1[0][1]), "+{v[96:111]}"(s1[1][0]),
                    "+{v[112:127]}"(s1[1][1]), "+{v[128:131]}"(p0[0][0][0]), "+{v[132:135]}"(p0[0][0][1]),
                    "+{v[136:139]}"(p0[0][1][0]), "+{v[140:143]}"(p0[0][1][1]), "+{v[144:147]}"(p0[1][0][0]),
                    "+{v[148:151]}"(p0[1][0][1]), "+{v[152:155]}"(p0[1][1][0]), "+{v[156:159]}"(p0[1][1][1]),
-                   "+{v192}"(m[0]), "+{v193}"(m[1]), "+{v194}"(l[0]), "+{v195}"(l[1]), "+{s74}"(p),
+                   "+{v192}"(m[0]), "+{v193}"(m[1]), "+{v194}"(l[0]), "+{v195}"(l[1]), "+{s74}"(p), "+{s[98:99]}"(k_addr),
                    "=&{v[32:63]}"(junk1), "=&{v[160:175]}"(junk2), "=&{v[176:191]}"(junk3), "=&{v[196:199]}"(junk4),
                    "=&{a[192:199]}"(junk5)
                  : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]), "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
@@ -863,9 +833,9 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
                    "{a[160:163]}"(qf[1][0]), "{a[164:167]}"(qf[1][1]), "{a[168:171]}"(qf[1][2]), "{a[172:175]}"(qf[1][3]),
                    "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]), "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
                    "{v[200:207]}"(koff), "{v[208:215]}"(voff), "{v[216:219]}"(cpoff), "{v220}"(bound0), "{v221}"(bound1),
-                   "{v222}"(half4), "{v[224:227]}"(rsel), "{s[70:71]}"(Ks), "{s[72:73]}"(Vs), "{s75}"(nt_s), "{s76}"(R_s),
+                   "{v222}"(half4), "{v[224:227]}"(rsel), "{s[70:71]}"(Ks), "{s75}"(nt_s), "{s76}"(R_s),
                    "{s77}"(fm_s), "{s78}"(ltb_s), "{s79}"(cs), "{s80}"(ring_wave), "{s81}"(wave_s), "{s[90:91]}"(Kn),
-                   "{s[92:93]}"(Vn), "{s94}"(Rn_s), "{s95}"(fmn_s), "{s96}"(next_s), "{s97}"(r0_s)
+                   "{s[92:93]}"(kv_s), "{s94}"(Rn_s), "{s95}"(fmn_s), "{s97}"(r0_s)
                  : "v223", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "s82", "s83", "s84",
                    "s85", "s86", "s87", "s88", "s89", "m0", "vcc", "exec", "scc", "memory");
     // The next block's tiles 0 and 1 have landed (its ring copies were issued

@@ -61,7 +61,8 @@
 //   s[70:71]             K of the head;  s74 position p;  s75 tiles;
 //   s76 masked tiles R;  s77 first masked tile;  s78 last tile byte offset;
 //   s79 scale*log2(e);  s80 LDS ring base + this wave's copy offset;  s81 wave;
-//   s82..s89 scalar temporaries (s[88:89] this step's V refill address);
+//   s82..s85 scalar temporaries;  s86 p+2;  s87 2^16 (the bound on a
+//   tile's exponentials);  s[88:89] this step's V refill address;
 //   s[90:91], s94, s95 the next block's K, R and first masked tile;
 //   s[92:93] the distance from the K tensor to the V tensor;  s97 the ring
 //   slot the block starts in;  s[98:99] the address of the last K refill
@@ -294,8 +295,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   .macro FA_STEP j, uid
     s_waitcnt vmcnt(8)
     s_barrier
-    v_mul_f32_e64 v198, -v192, s79
-    v_mul_f32_e64 v199, -v193, s79
+    s_add_u32 s86, s74, 2
     // P V half: positions 0..31 (each position's LDS reads go out before its
     // vector work, which then covers part of their latency)
     .irp t, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
@@ -312,17 +312,16 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
       .if (((\t)&1) == 1) && (((\t)>>1) <= 12)
         FA_VREAD (((\t)>>1)+3), (\j)
       .endif
-      FA_VPOS \t, (((\j)+1)&1)
       .if ((\t) == 27) || ((\t) == 29) || ((\t) == 31)
         FA_KREAD (((\t)-27)>>1), (((\j)+2)&3)
       .endif
+      FA_VPOS \t, (((\j)+1)&1)
     .endr
     // score half: positions 32..71 (32 score MFMAs of tile p+2, 8 row sums);
     // past the block's last tile (p+2 >= nt) the variant without scores
-    s_add_u32 s82, s74, 2
-    s_cmp_ge_u32 s82, s75
+    s_cmp_ge_u32 s86, s75
     s_cbranch_scc1 L_ns_\j\()_\uid
-    s_cmp_lt_u32 s82, s76
+    s_cmp_lt_u32 s86, s76
     s_cbranch_scc1 L_diag_\j\()_\uid
   L_sfull_\j\()_\uid:
     .irp t, 32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63,64,65,66,67,68,69,70,71
@@ -338,13 +337,12 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   L_nsret_\j\()_\uid:
     v_accvgpr_read_b32 v196, a192
     v_accvgpr_read_b32 v197, a196
-    // tile p+1 exists: check its exponentials, add its row sums
-    s_add_u32 s82, s74, 1
-    s_cmp_lt_u32 s82, s75
+    // tile p+1 exists (p+2 <= nt): check its exponentials against 2^16
+    // (s87), add its row sums
+    s_cmp_le_u32 s86, s75
     s_cbranch_scc0 L_nochk_\j\()_\uid
-    s_mov_b32 s82, 0x47800000
-    v_cmp_nle_f32_e64 s[84:85], v196, s82
-    v_cmp_nle_f32_e64 vcc, v197, s82
+    v_cmp_nle_f32_e64 s[84:85], v196, s87
+    v_cmp_nle_f32_e64 vcc, v197, s87
     s_or_b64 vcc, vcc, s[84:85]
     s_cbranch_vccnz L_rare_\j\()_\uid
   L_rret_\j\()_\uid:
@@ -352,8 +350,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     v_add_f32 v195, v195, v197
   L_nochk_\j\()_\uid:
     // tile p+2 needs the elementwise mask if p+2 < R
-    s_add_u32 s82, s74, 2
-    s_cmp_lt_u32 s82, s76
+    s_cmp_lt_u32 s86, s76
     s_cbranch_scc1 L_mask_\j\()_\uid
   L_mret_\j\()_\uid:
     s_add_u32 s74, s74, 1
@@ -465,7 +462,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     // this wave's rows (position > wave), whose scores the mask turns
     // into -inf whatever they hold
   L_diag_\j\()_\uid:
-    s_cmp_gt_u32 s82, s81
+    s_cmp_gt_u32 s86, s81
     s_cbranch_scc0 L_sfull_\j\()_\uid
   L_ns_\j\()_\uid:
     .irp t, 32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63,64,65,66,67,68,69,70,71
@@ -500,6 +497,9 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     v_accvgpr_write_b32 a[\r], 0
     v_accvgpr_write_b32 a[64+(\r)], 0
   .endr
+  v_mul_f32_e64 v198, -v192, s79
+  v_mul_f32_e64 v199, -v193, s79
+  s_mov_b32 s87, 0x47800000
   s_waitcnt vmcnt(16)
   s_barrier
   // enter the unrolled ring at the block's first slot (s97)

@@ -296,6 +296,11 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_waitcnt vmcnt(8)
     s_barrier
     s_add_u32 s86, s74, 2
+    // a causal diagonal tile past this wave's rows (p < R, p > wave): its P
+    // is zero, the variant without P V products
+    s_cmp_lt_u32 s74, s76
+    s_cbranch_scc1 L_pvd_\j\()_\uid
+  L_pvfull_\j\()_\uid:
     // P V half: positions 0..31 (each position's LDS reads go out before its
     // vector work, which then covers part of their latency)
     .irp t, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
@@ -317,6 +322,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
       .endif
       FA_VPOS \t, (((\j)+1)&1)
     .endr
+  L_pvret_\j\()_\uid:
     // score half: positions 32..71 (32 score MFMAs of tile p+2, 8 row sums);
     // past the block's last tile (p+2 >= nt) the variant without scores
     s_cmp_ge_u32 s86, s75
@@ -447,6 +453,24 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_branch L_rret_\j\()_\uid
   .endm
 
+  // ---- out of line: the P V half of a step whose tile p is a causal
+  // diagonal tile past this wave's rows: its P is zero, so no P V products
+  // and no V reads (V fragments 0..2, read at the end of the last step, are
+  // waited for with the K fragments in the score half); the softmax of tile
+  // p+1 and the first K reads of tile p+2 as in the full half
+  .macro FA_PVD j, uid
+  L_pvd_\j\()_\uid:
+    s_cmp_gt_u32 s74, s81
+    s_cbranch_scc0 L_pvfull_\j\()_\uid
+    .irp t, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
+      .if ((\t) == 27) || ((\t) == 29) || ((\t) == 31)
+        FA_KREAD (((\t)-27)>>1), (((\j)+2)&3)
+      .endif
+      FA_VPOS \t, (((\j)+1)&1)
+    .endr
+    s_branch L_pvret_\j\()_\uid
+  .endm
+
   .macro FA_MASK j, uid
   L_mask_\j\()_\uid:
     FA_MASKSET ((\j)&1), 2
@@ -547,6 +571,10 @@ L_s3_%=:
   FA_MASK 1, %=
   FA_MASK 2, %=
   FA_MASK 3, %=
+  FA_PVD 0, %=
+  FA_PVD 1, %=
+  FA_PVD 2, %=
+  FA_PVD 3, %=
   .irp jj, 0, 1, 2, 3
     FA_NS \jj, %=
     FA_RNEXT \jj, %=
@@ -573,6 +601,7 @@ L_done_%=:
   .purgem FA_STEP
   .purgem FA_RARE
   .purgem FA_MASK
+  .purgem FA_PVD
   .purgem FA_SWAPSETS
   .purgem FA_RNEXT
   .purgem FA_NS

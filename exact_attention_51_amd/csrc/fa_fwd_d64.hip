@@ -22,11 +22,15 @@
 // row-sum products over P), 40 MFMA positions instead of 72.  So each of
 // the first 32 positions carries two exponentials (an FMA to the exp2 domain
 // against the running max and a v_exp_f32, in place) and one pack of a pair
-// into P, about 22 issue cycles under a 32-cycle MFMA; the last positions
-// carry the ring refills and the next tile's first V reads.  A pack into P
-// waits until the P V products of tile p have read the old P block it
-// overwrites (all of them by position 16), and a row-sum product until the
-// four packs of its P block are done.
+// into P, which one wave issues in about 37 cycles beside a 32-cycle MFMA:
+// the step is bound by the wave's instruction issue, so every other
+// instruction is placed where it costs least -- LDS reads right after an
+// MFMA, scalar work before the vector work, the next tile's V reads and the
+// ring refills in the last positions, which carry no exponentials.  The K
+// and V fragment buffers (AGPRs) hold a whole tile each, so a step waits for
+// LDS twice.  A pack into P waits until the P V products of tile p have read
+// the old P block it overwrites (all of them by position 16), and a row-sum
+// product until the four packs of its P block are done.
 //
 // Register map inside the loop (v = VGPR, a = AGPR):
 //   v[0:63], v[64:127]   score sets: tile q in set q mod 2, block (kb, qb)

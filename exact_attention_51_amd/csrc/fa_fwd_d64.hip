@@ -779,7 +779,7 @@ fwd_d64_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
     scores(r0, 0, s0);
     float m[2], l[2];
     bf16x8 p0[2][2][2];  // [qb][kb][cc]
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const bf16x8 rsel_bf = __builtin_bit_cast(bf16x8, rsel);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float t = -kMaxFloor;
@@ -789,21 +789,21 @@ fwd_d64_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
         for (int r = 0; r < 16; ++r) t = __builtin_fmaxf(t, s0[kb][qb][r]);
       m[qb] = max_halves(t);
       const float nmc = -m[qb] * c;
-      float lt = 0.f;
+      // row sums over the rounded P on the loop's row-sum MFMAs (selector x P)
+      f32x4 rs = {};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           bf16x2 pr[4];
 #pragma unroll
-          for (int w4 = 0; w4 < 4; ++w4) {
+          for (int w4 = 0; w4 < 4; ++w4)
             pr[w4] = pack_bf16(fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w4], c, nmc)),
                                fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w4 + 1], c, nmc)));
-            lt = __builtin_amdgcn_fdot2_f32_bf16(pr[w4], ones, lt, false);
-          }
           p0[qb][kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
+          rs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel_bf, p0[qb][kb][cc], rs, 0, 0, 0);
         }
-      l[qb] = sum_halves(lt);  // every lane holds its row's whole sum, as the row-sum MFMAs give it
+      l[qb] = rs[0];  // every lane holds its row's whole sum
     }
     // the scores of tile 1
     scores((r0 + 1) & 3, 1, s1);

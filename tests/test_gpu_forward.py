@@ -129,15 +129,18 @@ def test_forward_bf16_many_heads(D, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("B,H,N", [(3, 37, 1000), (2, 20, 3000)])
+@pytest.mark.parametrize("B,H,N", [(3, 37, 1000), (2, 20, 3000), (2, 64, 1000)])
 @pytest.mark.parametrize("D", [64, 128])
 def test_forward_persistent_rounds(D, B, H, N, causal):
     """D = 64 and 128 grids larger than the GPU run one persistent workgroup
     per compute unit, which carries its K/V ring from one 256-row block into
-    the next.  Both shapes take a full round of blocks and a partial one,
+    the next.  The shapes take a full round of blocks and a partial one,
     with a ragged last key tile: 111 heads of N = 1000 (444 blocks; heads not
     a multiple of the eight XCDs, so no per-XCD head groups) and 40 heads of
-    N = 3000 (480 blocks, 5 heads per XCD, blocks of 4 to 47 key tiles)."""
+    N = 3000 (480 blocks, 5 heads per XCD, blocks of 4 to 47 key tiles).
+    Under the causal mask those grids take the 128-row workgroups of smaller
+    grids; 128 heads of N = 1000 (512 blocks) run the persistent kernels
+    with the mask too."""
     w = WORKLOADS["c3"].with_(name="rounds", B=B, H=H, N=N, D=D, causal=causal, seed=N + H + D)
     log(f"test_forward_persistent_rounds D={D} B={B} H={H} N={N} causal={causal}")
     x = make_inputs(w, with_do=False)

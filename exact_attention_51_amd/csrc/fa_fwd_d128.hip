@@ -332,13 +332,13 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   L_sfull_\j\()_\uid:
     .irp t, 32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63,64,65,66,67,68,69,70,71
       FA_SPOS \t, \j
-      FA_VPOS \t, (((\j)+1)&1)
       .if (\t) >= 62
         FA_REFILL ((\t)-62), \j, \uid
       .endif
       .if (\t) >= 69
         FA_VREAD ((\t)-69), (((\j)+1)&3)
       .endif
+      FA_VPOS \t, (((\j)+1)&1)
     .endr
   L_nsret_\j\()_\uid:
     v_accvgpr_read_b32 v196, a192
@@ -494,13 +494,13 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
         s_nop 4
         FA_SPOS \t, \j
       .endif
-      FA_VPOS \t, (((\j)+1)&1)
       .if (\t) >= 62
         FA_REFILL ((\t)-62), \j, \uid\()n
       .endif
       .if (\t) >= 69
         FA_VREAD ((\t)-69), (((\j)+1)&3)
       .endif
+      FA_VPOS \t, (((\j)+1)&1)
     .endr
     s_nop 7
     s_nop 7

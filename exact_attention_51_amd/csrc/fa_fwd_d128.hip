@@ -81,7 +81,7 @@ constexpr int kTileBytes = kBlockN * D * 2;
 constexpr int kNB = 4;                   // ring slots per tensor
 constexpr int kRingBytes = 2 * kNB * kTileBytes;
 constexpr int kStageBytes = kWaves * 32 * D * 2;  // epilogue staging, 32 rows per wave
-constexpr float kMaxFloor = 1.0e30f;     // the running max starts at -kMaxFloor (0xf149f2ca in the entry code)
+constexpr float kMaxFloor = 1.0e30f;     // the running max starts at -kMaxFloor
 
 typedef __attribute__((ext_vector_type(32))) float f32x32;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
@@ -508,101 +508,21 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
     s_branch L_nsret_\j\()_\uid
   .endm
 
-  // ---- block entry (ring slot b of tile 0): the scores of tiles 0 and 1
-  // (K slots b and b+1) into sets b mod 2 and (b+1) mod 2, where step 0
-  // expects them; their masks; tile 0's running max (its row max, floored)
-  // and its P and row sums
-  .macro FA_PSC k, b, n
-    .if ((\k)&1) == 0
-      .if ((\k)>>1) <= 13
-        s_waitcnt lgkmcnt(2)
-      .elseif ((\k)>>1) == 14
-        s_waitcnt lgkmcnt(1)
-      .else
-        s_waitcnt lgkmcnt(0)
-      .endif
-    .endif
-    FA_SMFMA \k, \n
-    .if (((\k)&1) == 1) && (((\k)>>1) <= 12)
-      FA_KREAD (((\k)>>1)+3), \b
-    .endif
+  // score sets swapped on entry at an odd ring slot: tile 1's scores belong
+  // in set 0
+  .macro FA_SWAPSETS
+    .irp r, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31,32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63
+      v_mov_b32 v[\r], v[64+(\r)]
+    .endr
   .endm
-  .macro FA_PRO b, uid
-    FA_KREAD 0, \b
-    FA_KREAD 1, \b
-    FA_KREAD 2, \b
-    .irp k, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
-      FA_PSC \k, \b, ((\b)&1)
-    .endr
-    // tile 1 is a causal diagonal tile past wave 0's rows when R > 1
-    s_cmp_eq_u32 s81, 0
-    s_cbranch_scc0 L_p1_\b\()_\uid
-    s_cmp_gt_u32 s76, 1
-    s_cbranch_scc1 L_p1s_\b\()_\uid
-  L_p1_\b\()_\uid:
-    FA_KREAD 0, (((\b)+1)&3)
-    FA_KREAD 1, (((\b)+1)&3)
-    FA_KREAD 2, (((\b)+1)&3)
-    .irp k, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
-      FA_PSC \k, (((\b)+1)&3), (((\b)+1)&1)
-    .endr
-  L_p1s_\b\()_\uid:
-    s_nop 7
-    s_nop 7
-    s_cmp_gt_u32 s76, 0
-    s_cbranch_scc0 L_pm0_\b\()_\uid
-    FA_MASKSET ((\b)&1), 0
-  L_pm0_\b\()_\uid:
-    s_cmp_gt_u32 s76, 1
-    s_cbranch_scc0 L_pm1_\b\()_\uid
-    FA_MASKSET (((\b)+1)&1), 1
-  L_pm1_\b\()_\uid:
-    s_nop 7
-    s_nop 7
-    .irp qb, 0, 1
-      v_max3_f32 v228, v[((\b)&1)*64+(\qb)*16], v[((\b)&1)*64+(\qb)*16+1], v[((\b)&1)*64+(\qb)*16+2]
-      .irp r, 3, 5, 7, 9, 11, 13
-        v_max3_f32 v228, v228, v[((\b)&1)*64+(\qb)*16+(\r)], v[((\b)&1)*64+(\qb)*16+(\r)+1]
-      .endr
-      v_max_f32 v228, v228, v[((\b)&1)*64+(\qb)*16+15]
-      .irp r, 0, 2, 4, 6, 8, 10, 12, 14
-        v_max3_f32 v228, v228, v[((\b)&1)*64+32+(\qb)*16+(\r)], v[((\b)&1)*64+32+(\qb)*16+(\r)+1]
-      .endr
-      v_mov_b32 v229, v228
-      s_nop 1
-      v_permlane32_swap_b32 v228, v229
-      s_nop 1
-      v_max_f32 v230, 0xf149f2ca, v228
-      v_max_f32 v[192+(\qb)], v230, v229
-    .endr
-    v_mul_f32_e64 v198, -v192, s79
-    v_mul_f32_e64 v199, -v193, s79
-    .irp n, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
-      FA_E \n, 0, ((\b)&1)
-      FA_E \n, 1, ((\b)&1)
-    .endr
-    s_nop 2
-    .irp n, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31
-      FA_C \n, ((\b)&1)
-    .endr
-    s_nop 4
-    .irp bb, 0, 1, 2, 3
-      FA_RSMFMA \bb, 0
-      FA_RSMFMA \bb, 1
-    .endr
-    s_nop 7
-    s_nop 7
-    s_nop 7
-    v_accvgpr_read_b32 v194, a192
-    v_accvgpr_read_b32 v195, a196
-  .endm
-
 
   s_waitcnt lgkmcnt(0)
   .irp r, 0,1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17,18,19,20,21,22,23,24,25,26,27,28,29,30,31,32,33,34,35,36,37,38,39,40,41,42,43,44,45,46,47,48,49,50,51,52,53,54,55,56,57,58,59,60,61,62,63
     v_accvgpr_write_b32 a[\r], 0
     v_accvgpr_write_b32 a[64+(\r)], 0
   .endr
+  v_mul_f32_e64 v198, -v192, s79
+  v_mul_f32_e64 v199, -v193, s79
   s_mov_b32 s87, 0x47800000
   s_waitcnt vmcnt(16)
   s_barrier
@@ -613,25 +533,23 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
   s_cbranch_scc1 L_e2_%=
   s_cmp_eq_u32 s97, 3
   s_cbranch_scc1 L_e3_%=
-  FA_PRO 0, %=
   FA_VREAD 0, 0
   FA_VREAD 1, 0
   FA_VREAD 2, 0
   s_branch L_s0_%=
 L_e1_%=:
-  FA_PRO 1, %=
+  FA_SWAPSETS
   FA_VREAD 0, 1
   FA_VREAD 1, 1
   FA_VREAD 2, 1
   s_branch L_s1_%=
 L_e2_%=:
-  FA_PRO 2, %=
   FA_VREAD 0, 2
   FA_VREAD 1, 2
   FA_VREAD 2, 2
   s_branch L_s2_%=
 L_e3_%=:
-  FA_PRO 3, %=
+  FA_SWAPSETS
   FA_VREAD 0, 3
   FA_VREAD 1, 3
   FA_VREAD 2, 3
@@ -684,8 +602,7 @@ L_done_%=:
   .purgem FA_RARE
   .purgem FA_MASK
   .purgem FA_PVD
-  .purgem FA_PSC
-  .purgem FA_PRO
+  .purgem FA_SWAPSETS
   .purgem FA_RNEXT
   .purgem FA_NS
 )ASM"
@@ -821,13 +738,88 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
       bound1 = min(N, wq0 + 32 + l32 + 1);
     }
 
-    // Every wave's copies of tiles 0 and 1 have landed (waited for above, or
-    // at the start of the previous block's last step); the loop's entry code
-    // computes their scores, tile 0's running max, P and row sums.
+    // scores of the tile at position p from K ring slot b, masked when p < R
+    auto scores = [&](int b, int p, f32x16 (&s)[2][2]) {
+      if (CAUSAL && p < cur.R && p > wave) {  // a diagonal tile past this wave's rows
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][qb][r] = -__builtin_inff();
+        return;
+      }
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf =
+              *(const bf16x8 __attribute__((address_space(3)))*)(smem + b * kTileBytes + koff[ds] - ring + kb * 32 * D * 2);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(kf, qf[qb][ds], ds == 0 ? f32x16{} : s[kb][qb]);
+        }
+      if (p < cur.R) {
+        // -inf where a key is invisible (the loop's mask rule)
+        const int t = cur.fm + p;
+        const int row0 = min(t * kBlockN, N - kBlockN);
+        int base = row0 + half4;
+        // (kept opaque: hoisted out of the block loop, the 64 comparisons
+        // would each hold an SGPR pair for the kernel's whole life)
+        asm volatile("" : "+v"(base));
+        const int lo = t * kBlockN - base;
+        const int hi[2] = {bound0 - base, bound1 - base};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+              s[kb][qb][r] = (off >= lo && off < hi[qb]) ? s[kb][qb][r] : -__builtin_inff();
+            }
+      }
+    };
+
+    // tile 0: scores, the running max (its row max; a finite floor where a
+    // row sees none of its keys), P and the row sums over the rounded P.
+    // Every wave's copies of tiles 0 and 1 have landed (waited for above,
+    // or at the start of the previous block's last step).
     __syncthreads();
+    f32x16 s0[2][2], s1[2][2];
+    scores(r0, 0, s0);
     float m[2], l[2];
+    bf16x8 p0[2][2][2];  // [qb][kb][cc]
+    const bf16x8 rsel_bf = __builtin_bit_cast(bf16x8, rsel);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float t = -kMaxFloor;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t = __builtin_fmaxf(t, s0[kb][qb][r]);
+      m[qb] = max_halves(t);
+      const float nmc = -m[qb] * c;
+      // row sums over the rounded P on the loop's row-sum MFMAs (selector x P)
+      f32x4 rs = {};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x2 pr[4];
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4)
+            pr[w4] = pack_bf16(fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w4], c, nmc)),
+                               fast_exp2(__builtin_fmaf(s0[kb][qb][cc * 8 + 2 * w4 + 1], c, nmc)));
+          p0[qb][kb][cc] = join8(pr[0], pr[1], pr[2], pr[3]);
+          rs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel_bf, p0[qb][kb][cc], rs, 0, 0, 0);
+        }
+      l[qb] = rs[0];  // every lane holds its row's whole sum
+    }
+    // the scores of tile 1
+    scores((r0 + 1) & 3, 1, s1);
+
     f32x32 o0, o1, o2, o3;  // O^T: a[0:31] (qb 0, db 0-1) .. a[96:127] (qb 1, db 2-3)
-    f32x32 junk0, junk1, junk6, junk7, junk8;  // registers the loop uses internally
+    f32x32 junk0, junk1;    // registers the loop uses internally
     f32x16 junk2, junk3;
     f32x4 junk4;
     f32x8 junk5;
@@ -858,8 +850,11 @@ fwd_d128_kernel(FwdArgs a, TileSched sched, int n_blocks, int cont) {
     const int Rn_s = sgpr(nxt.R), fmn_s = sgpr(nxt.fm), r0_s = sgpr(r0);
     asm volatile(FA_D128_LOOP_ASM
                  : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
-                   "=&{v[0:31]}"(junk0), "=&{v[64:95]}"(junk6), "=&{v[96:127]}"(junk7), "=&{v[128:159]}"(junk8),
-                   "={v192}"(m[0]), "={v193}"(m[1]), "={v194}"(l[0]), "={v195}"(l[1]), "+{s74}"(p), "+{s[98:99]}"(k_addr),
+                   "=&{v[0:31]}"(junk0), "+{v[64:79]}"(s1[0][0]), "+{v[80:95]}"(s1[0][1]), "+{v[96:111]}"(s1[1][0]),
+                   "+{v[112:127]}"(s1[1][1]), "+{v[128:131]}"(p0[0][0][0]), "+{v[132:135]}"(p0[0][0][1]),
+                   "+{v[136:139]}"(p0[0][1][0]), "+{v[140:143]}"(p0[0][1][1]), "+{v[144:147]}"(p0[1][0][0]),
+                   "+{v[148:151]}"(p0[1][0][1]), "+{v[152:155]}"(p0[1][1][0]), "+{v[156:159]}"(p0[1][1][1]),
+                   "+{v192}"(m[0]), "+{v193}"(m[1]), "+{v194}"(l[0]), "+{v195}"(l[1]), "+{s74}"(p), "+{s[98:99]}"(k_addr),
                    "=&{v[32:63]}"(junk1), "=&{v[160:175]}"(junk2), "=&{v[176:191]}"(junk3), "=&{v[196:199]}"(junk4),
                    "=&{a[192:199]}"(junk5)
                  : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]), "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
